@@ -1,0 +1,170 @@
+"""CPU oracle for the dense GEMM C = A*B -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never calls it and it
+never calls the GPU library: the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, bit-level decoders); this
+module only marshals numpy arrays into it.  What it follows:
+
+* "[CUDA 优化实战] hgemm - 超越 cuBLAS", sections 0-1: C = A*B, A (M x K) and
+  B (K x N) both row-major, fp16/bf16 inputs, fp32 accumulation;
+* "CUDA GEMM 优化实践笔记", register-tiling section: the fp32 SGEMM with the
+  same row-major indexing;
+* "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3 and
+  section 5.2 (third pitfall): E4M3 operands with one 32-bit scale per 64x64
+  sub-block.
+
+``gemm`` returns the exact sum (fp64, k ascending, never rounded to the
+output type).  ``within_tolerance`` is the element-wise acceptance test
+|gpu - ref| <= rtol*|ref| + atol, with any NaN/Inf in the candidate failing.
+
+Parity pins: every function here is pinned by ``tests/test_oracle.py`` against
+library decoders (exhaustively), closed forms and exact rational brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16, F32, FP8 = 0, 1, 2, 3
+DTYPES = {"f16": F16, "bf16": BF16, "f32": F32, "fp8": FP8}
+SCALE_BLOCK = 64
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    _lib = bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def bind(lib):
+    """Declare the C signatures on a loaded oracle library handle."""
+    vp, i64, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
+    lib.orc_gemm.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, dp, i64,
+                             ctypes.c_int]
+    lib.orc_gemm.restype = ctypes.c_int
+    lib.orc_gemm_entries.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     vp, vp, i64, dp]
+    lib.orc_gemm_entries.restype = ctypes.c_int
+    for name in ("orc_decode_f16", "orc_decode_bf16", "orc_decode_e4m3", "orc_decode_f32"):
+        getattr(lib, name).argtypes = [vp, dp, i64]
+        getattr(lib, name).restype = None
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _raw(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Row-major raw bit array of an operand (uint16 / float32 / uint8)."""
+    want = {"f16": np.uint16, "bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}[dtype]
+    if x.dtype != want:
+        if dtype == "f16" and x.dtype == np.float16:
+            x = x.view(np.uint16)
+        elif dtype == "f32" and x.dtype == np.uint32:
+            x = x.view(np.float32)
+        else:
+            raise TypeError(f"{dtype} operand must be {want}, got {x.dtype}")
+    if x.ndim != 2 or x.strides[1] != x.itemsize:
+        raise ValueError("operand must be 2-D with unit column stride")
+    return x
+
+
+def _ld(x: np.ndarray) -> int:
+    return x.strides[0] // x.itemsize
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 values of raw fp16/bf16 (uint16), e4m3 (uint8) or fp32 bits."""
+    lib = _load()
+    src = np.ascontiguousarray(bits)
+    out = np.empty(src.shape, dtype=np.float64)
+    fn = {"f16": lib.orc_decode_f16, "bf16": lib.orc_decode_bf16,
+          "fp8": lib.orc_decode_e4m3, "f32": lib.orc_decode_f32}[dtype]
+    if dtype == "f32":
+        src = src.view(np.uint32)
+    fn(src.ctypes.data, out.ctypes.data, src.size)
+    return out
+
+
+def gemm(dtype: str, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+         scale_a: np.ndarray | None = None, scale_b: np.ndarray | None = None,
+         nthreads: int | None = None) -> np.ndarray:
+    """Exact (fp64) C = A[:M,:K] * B[:K,:N] of raw operands; returns M x N float64."""
+    lib = _load()
+    A = _raw(A, dtype)
+    B = _raw(B, dtype)
+    if A.shape[0] < M or A.shape[1] < K or B.shape[0] < K or B.shape[1] < N:
+        raise ValueError("operand smaller than (M, N, K)")
+    sa = sb = None
+    if dtype == "fp8":
+        sa = np.ascontiguousarray(scale_a, dtype=np.float32)
+        sb = np.ascontiguousarray(scale_b, dtype=np.float32)
+        if sa.shape != (-(-M // SCALE_BLOCK), -(-K // SCALE_BLOCK)) or \
+           sb.shape != (-(-K // SCALE_BLOCK), -(-N // SCALE_BLOCK)):
+            raise ValueError("scale grid shape does not match the 64x64 blocks")
+    out = np.empty((M, N), dtype=np.float64)
+    nt = nthreads or os.cpu_count() or 1
+    rc = lib.orc_gemm(DTYPES[dtype], _ptr(A), _ptr(B), _ptr(sa), _ptr(sb), M, N, K,
+                      _ld(A), _ld(B), out.ctypes.data, N, int(nt))
+    if rc != 0:
+        raise RuntimeError(f"orc_gemm failed ({rc})")
+    return out
+
+
+def gemm_entries(dtype: str, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+                 rows: np.ndarray, cols: np.ndarray, scale_a: np.ndarray | None = None,
+                 scale_b: np.ndarray | None = None) -> np.ndarray:
+    """Exact (fp64) entries C[rows[t], cols[t]] only."""
+    lib = _load()
+    A = _raw(A, dtype)
+    B = _raw(B, dtype)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    sa = sb = None
+    if dtype == "fp8":
+        sa = np.ascontiguousarray(scale_a, dtype=np.float32)
+        sb = np.ascontiguousarray(scale_b, dtype=np.float32)
+    out = np.empty(rows.shape[0], dtype=np.float64)
+    rc = lib.orc_gemm_entries(DTYPES[dtype], _ptr(A), _ptr(B), _ptr(sa), _ptr(sb), M, N, K,
+                              _ld(A), _ld(B), rows.ctypes.data, cols.ctypes.data,
+                              rows.shape[0], out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"orc_gemm_entries failed ({rc})")
+    return out
+
+
+def within_tolerance(gpu: np.ndarray, ref: np.ndarray, rtol: float, atol: float):
+    """Element-wise |gpu - ref| <= rtol*|ref| + atol; NaN/Inf in gpu fail.
+
+    Returns (ok, n_fail, worst_ratio, worst_index) where worst_ratio is
+    max |gpu-ref| / (rtol*|ref| + atol) over the finite entries.
+    """
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if gpu.shape != ref.shape:
+        raise ValueError(f"shape mismatch {gpu.shape} vs {ref.shape}")
+    if gpu.size == 0:
+        return True, 0, 0.0, None
+    tol = rtol * np.abs(ref) + atol
+    finite = np.isfinite(gpu)
+    err = np.where(finite, np.abs(gpu - ref), np.inf)
+    ratio = err / tol
+    bad = ~(err <= tol)
+    worst = int(np.argmax(ratio))
+    idx = np.unravel_index(worst, ratio.shape)
+    return (not bad.any()), int(bad.sum()), float(ratio.flat[worst]), tuple(int(i) for i in idx)

@@ -1,0 +1,242 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the dense GEMM
+ * C = A * B (row-major A of M x K, row-major B of K x N).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header or table with the GPU library.
+ *
+ * What it computes (the plain definition, no blocking, no reordering):
+ *   - "[CUDA 优化实战] hgemm - 超越 cuBLAS", sections 0-1: C = A*B with A and B
+ *     both row-major ("A/B 都行优先"), half-precision (fp16 or bf16) inputs and
+ *     an fp32 accumulator; the reference here accumulates in fp64 and never
+ *     rounds the result, so the tests compare the GPU output against the exact
+ *     sum up to fp64 rounding.
+ *   - "CUDA GEMM 优化实践笔记", register-tiling section: the fp32 SGEMM with the
+ *     same row-major indexing A[row*K + col], B[row*N + col].
+ *   - "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3: FP8
+ *     (E4M3) operands, each 64x64 sub-block multiplied by its own scale factor;
+ *     section 5.2 (third pitfall): the scales are 32-bit floats.
+ *
+ * Every input is decoded bit by bit to an exact double by the decoders below
+ * (they do not use compiler half/bfloat/fp8 types).  The sum for each entry runs
+ * over k = 0 .. K-1 in ascending order.  Build with -ffp-contract=off and no
+ * fast-math so that each step is one IEEE multiply and one IEEE add in fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- decoders */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double orc_f16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^(1-15-10) */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(0x400 | f), e - 25);    /* (1.f) * 2^(e-15), as an integer * 2^(e-15-10) */
+    return s ? -v : v;
+}
+
+/* bfloat16: the upper half of an IEEE binary32: 1 sign, 8 exponent (bias 127), 7 fraction. */
+double orc_bf16_to_f64(uint16_t b)
+{
+    int s = (b >> 15) & 1, e = (b >> 7) & 0xff, f = b & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);                /* subnormal: f * 2^(1-127-7) */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(0x80 | f), e - 134);    /* (128+f) * 2^(e-127-7) */
+    return s ? -v : v;
+}
+
+/* OCP FP8 E4M3 ("E4M3FN"): 1 sign, 4 exponent (bias 7), 3 mantissa; no infinities;
+ * S.1111.111 is NaN; largest finite magnitude 448; subnormals down to 2^-9. */
+double orc_e4m3_to_f64(uint8_t q)
+{
+    int s = (q >> 7) & 1, e = (q >> 3) & 0xf, m = q & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                  /* subnormal: m * 2^(1-7-3) */
+    else
+        v = ldexp((double)(8 | m), e - 10);        /* (8+m) * 2^(e-7-3) */
+    return s ? -v : v;
+}
+
+/* IEEE binary32 from its bit pattern, built from the fields as well. */
+double orc_f32_to_f64(uint32_t u)
+{
+    int s = (u >> 31) & 1, e = (u >> 23) & 0xff;
+    uint32_t f = u & 0x7fffff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -149);                /* subnormal: f * 2^(1-127-23) */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(0x800000u | f), e - 150);
+    return s ? -v : v;
+}
+
+void orc_decode_f16(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_f16_to_f64(in[i]);
+}
+void orc_decode_bf16(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_bf16_to_f64(in[i]);
+}
+void orc_decode_e4m3(const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_e4m3_to_f64(in[i]);
+}
+void orc_decode_f32(const uint32_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_f32_to_f64(in[i]);
+}
+
+/* ------------------------------------------------------ operand decoding */
+
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_F32 = 2, ORC_FP8 = 3 };
+
+/* Block edge of the FP8 scale grid (64x64 sub-blocks). */
+#define ORC_SCALE_BLOCK 64
+
+/* Value of element (r, c) of a row-major operand with leading dimension ld.
+ * For FP8, scale is the row-major grid of per-block fp32 scales with
+ * scale_cols columns, and the element is e4m3(q) * scale[r/64][c/64]. */
+static double operand_at(int dtype, const void *p, int64_t ld, int64_t r, int64_t c,
+                         const float *scale, int64_t scale_cols)
+{
+    int64_t idx = r * ld + c;
+    switch (dtype) {
+    case ORC_F16:  return orc_f16_to_f64(((const uint16_t *)p)[idx]);
+    case ORC_BF16: return orc_bf16_to_f64(((const uint16_t *)p)[idx]);
+    case ORC_F32:  return orc_f32_to_f64(((const uint32_t *)p)[idx]);
+    default: {
+        uint32_t sbits;
+        float s = scale[(r / ORC_SCALE_BLOCK) * scale_cols + (c / ORC_SCALE_BLOCK)];
+        memcpy(&sbits, &s, 4);
+        return orc_e4m3_to_f64(((const uint8_t *)p)[idx]) * orc_f32_to_f64(sbits);
+    }
+    }
+}
+
+/* Decode a rows x cols operand into a dense fp64 array (leading dimension cols). */
+static void decode_operand(int dtype, const void *p, int64_t ld, int64_t rows, int64_t cols,
+                           const float *scale, double *out)
+{
+    int64_t scale_cols = (cols + ORC_SCALE_BLOCK - 1) / ORC_SCALE_BLOCK;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            out[r * cols + c] = operand_at(dtype, p, ld, r, c, scale, scale_cols);
+}
+
+/* ------------------------------------------------------------ the product */
+
+typedef struct {
+    const double *a, *b;   /* M x K and K x N, dense */
+    double *c;             /* M x N, leading dimension ldc */
+    int64_t n, k, ldc, row0, row1;
+} rows_job;
+
+/* C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j] for rows row0 <= i < row1.
+ * The i-k-j loop order adds the terms of every entry in ascending k, exactly
+ * like the textbook i-j-k triple loop; it only visits memory in rows. */
+static void *rows_worker(void *arg)
+{
+    const rows_job *job = (const rows_job *)arg;
+    for (int64_t i = job->row0; i < job->row1; i++) {
+        double *ci = job->c + i * job->ldc;
+        for (int64_t j = 0; j < job->n; j++) ci[j] = 0.0;
+        for (int64_t kk = 0; kk < job->k; kk++) {
+            double aik = job->a[i * job->k + kk];
+            const double *bk = job->b + kk * job->n;
+            for (int64_t j = 0; j < job->n; j++) ci[j] = ci[j] + aik * bk[j];
+        }
+    }
+    return NULL;
+}
+
+static int run_rows(const double *a, const double *b, double *c, int64_t m, int64_t n, int64_t k,
+                    int64_t ldc, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (m < nthreads) nthreads = m > 0 ? (int)m : 1;
+    pthread_t tid[256];
+    int running[256];
+    rows_job jobs[256];
+    int64_t per = (m + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; t++) {
+        jobs[t].a = a; jobs[t].b = b; jobs[t].c = c;
+        jobs[t].n = n; jobs[t].k = k; jobs[t].ldc = ldc;
+        jobs[t].row0 = t * per < m ? t * per : m;
+        jobs[t].row1 = (t + 1) * per < m ? (t + 1) * per : m;
+        running[t] = nthreads > 1 && pthread_create(&tid[t], NULL, rows_worker, &jobs[t]) == 0;
+        if (!running[t]) rows_worker(&jobs[t]);   /* single thread, or no thread: do the rows here */
+    }
+    for (int t = 0; t < nthreads; t++)
+        if (running[t]) pthread_join(tid[t], NULL);
+    return 0;
+}
+
+/*
+ * Full reference product.  A: M x K (leading dimension lda), B: K x N (ldb),
+ * raw bits of the given dtype; for FP8 scale_a is the ceil(M/64) x ceil(K/64)
+ * grid and scale_b the ceil(K/64) x ceil(N/64) grid, both row-major fp32.
+ * out: M x N fp64 with leading dimension ldo (the exact sum, not rounded).
+ * Returns 0, or -1 on a bad argument / allocation failure.
+ */
+int orc_gemm(int dtype, const void *A, const void *B, const float *scale_a, const float *scale_b,
+             int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, double *out, int64_t ldo,
+             int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N || ldo < N) return -1;
+    if (dtype == ORC_FP8 && K > 0 && (!scale_a || !scale_b)) return -1;
+    if (M == 0 || N == 0) return 0;
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * (K > 0 ? K : 1)));
+    double *b = (double *)malloc(sizeof(double) * (size_t)((K > 0 ? K : 1) * N));
+    if (!a || !b) { free(a); free(b); return -1; }
+    decode_operand(dtype, A, lda, M, K, scale_a, a);
+    decode_operand(dtype, B, ldb, K, N, scale_b, b);
+    run_rows(a, b, out, M, N, K, ldo, nthreads);
+    free(a);
+    free(b);
+    return 0;
+}
+
+/*
+ * The same sum for a list of entries (rows[t], cols[t]) only, decoding the
+ * operands on the fly: used to check products too large to form in full.
+ */
+int orc_gemm_entries(int dtype, const void *A, const void *B, const float *scale_a,
+                     const float *scale_b, int64_t M, int64_t N, int64_t K, int64_t lda,
+                     int64_t ldb, const int64_t *rows, const int64_t *cols, int64_t count,
+                     double *out)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < N) return -1;
+    int64_t sa_cols = (K + ORC_SCALE_BLOCK - 1) / ORC_SCALE_BLOCK;
+    int64_t sb_cols = (N + ORC_SCALE_BLOCK - 1) / ORC_SCALE_BLOCK;
+    for (int64_t t = 0; t < count; t++) {
+        int64_t i = rows[t], j = cols[t];
+        if (i < 0 || i >= M || j < 0 || j >= N) return -1;
+        double acc = 0.0;
+        for (int64_t kk = 0; kk < K; kk++)
+            acc = acc + operand_at(dtype, A, lda, i, kk, scale_a, sa_cols) *
+                            operand_at(dtype, B, ldb, kk, j, scale_b, sb_cols);
+        out[t] = acc;
+    }
+    return 0;
+}

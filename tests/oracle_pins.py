@@ -1,0 +1,279 @@
+"""Pins for the CPU oracle: facts fixed by the number formats and by mathematics,
+not by the oracle itself.
+
+Each ``pin_*`` function returns a list of failure descriptions (empty = pass),
+so the same checks serve the ordinary tests and the mutation tests, which plant
+a mistake in a copy of oracle.c and require at least one pin to fail.
+
+Independent sources used here:
+* library decoders: numpy float16, torch bfloat16 / float8_e4m3fn, numpy float32;
+* closed forms: A*I = A, I*B = B, P*B = row-permuted B, all-ones -> K,
+  rank-1 (u 1^T)(1 z^T) = K u z^T, K = 1 outer product, K = 0 -> 0;
+* exact rational brute force (fractions.Fraction) on tiny inputs.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import gemm_inputs as gi
+
+DTYPES = ("f16", "bf16", "f32", "fp8")
+
+
+# ------------------------------------------------------------ independent decoding
+
+def lib_decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Decode raw bits with numpy/torch casts (not the oracle's decoders)."""
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+        return t.to(torch.float64).numpy()
+    if dtype == "fp8":
+        t = torch.from_numpy(np.ascontiguousarray(bits)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
+    if dtype == "f32":
+        return np.ascontiguousarray(bits).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Float values (exactly representable) -> raw operand bits of dtype."""
+    x = np.asarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return gi.to_f16_bits(x)
+    if dtype == "bf16":
+        return gi.to_bf16_bits(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x)
+    if dtype == "fp8":
+        return gi.to_e4m3_bits(x)
+    raise ValueError(dtype)
+
+
+def unit_scales(rows: int, cols: int) -> np.ndarray:
+    return np.ones((-(-rows // 64), -(-cols // 64)), dtype=np.float32)
+
+
+def random_operand(rows: int, cols: int, dtype: str, seed: int):
+    """(bits, scales-or-None) with the workloads' value distributions."""
+    if dtype in ("f16", "bf16"):
+        return gi.uniform_h16(rows, cols, seed, dtype), None
+    if dtype == "f32":
+        return gi.normal_f32(rows, cols, seed), None
+    return gi.normal_fp8_blockscaled(rows, cols, seed)
+
+
+def exact_values(bits: np.ndarray, dtype: str, scales) -> list:
+    """Exact rational value of every element (Fraction), from library decoding."""
+    vals = lib_decode(bits, dtype)
+    rows, cols = vals.shape
+    out = [[Fraction(float(vals[r, c])) for c in range(cols)] for r in range(rows)]
+    if dtype == "fp8":
+        for r in range(rows):
+            for c in range(cols):
+                out[r][c] *= Fraction(float(scales[r // 64, c // 64]))
+    return out
+
+
+# ------------------------------------------------------------------ the pins
+
+def pin_decoders(orc) -> list:
+    fails = []
+    all16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    all8 = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    for dtype, bits in (("f16", all16), ("bf16", all16), ("fp8", all8)):
+        got, want = orc.decode(bits, dtype), lib_decode(bits, dtype)
+        same = (got == want) | (np.isnan(got) & np.isnan(want))
+        if not same.all():
+            i = int(np.argmin(same))
+            fails.append(f"decode {dtype}: pattern {int(bits[i]):#x} -> {got[i]!r}, library {want[i]!r}")
+    rng = np.random.default_rng(5)
+    f32 = np.concatenate([rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32),
+                          np.array([0, 1, 0x7fffff, 0x800000, 0x7f7fffff, 0x7f800000,
+                                    0xff800000, 0x80000001, 0x3f800000], dtype=np.uint32)])
+    got = orc.decode(f32.view(np.float32), "f32")
+    want = lib_decode(f32.view(np.float32), "f32")
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    if not same.all():
+        fails.append("decode f32 mismatch")
+    return fails
+
+
+def _exact(orc, name, dtype, A, B, M, N, K, want, sa=None, sb=None) -> list:
+    got = orc.gemm(dtype, A, B, M, N, K, sa, sb, nthreads=2)
+    if got.shape != want.shape or not np.array_equal(got, want):
+        bad = np.argwhere(~(got == want)) if got.shape == want.shape else [None]
+        return [f"{name} {dtype} (M,N,K)=({M},{N},{K}): first mismatch at {bad[0]}"]
+    return []
+
+
+def pin_closed_forms(orc) -> list:
+    fails = []
+    for dtype in DTYPES:
+        M, N, K = 37, 29, 70
+        A, sa = random_operand(M, K, dtype, 11)
+        B, sb = random_operand(K, N, dtype, 12)
+        a, b = lib_decode(A, dtype), lib_decode(B, dtype)
+        if dtype == "fp8":
+            # unit scales: the operand values are the decoded E4M3 codes themselves
+            sa, sb = unit_scales(M, K), unit_scales(K, N)
+        eye = encode(np.eye(K), dtype)
+        unit_kk = unit_scales(K, K) if dtype == "fp8" else None
+        # A * I = A (I is K x K)
+        fails += _exact(orc, "A*I", dtype, A, eye, M, K, K, a, sa, unit_kk)
+        # I * B = B
+        fails += _exact(orc, "I*B", dtype, eye, B, K, N, K, b, unit_kk, sb)
+        # P * B = row-permuted B (P is K x K)
+        perm = np.random.default_rng(3).permutation(K)
+        P = np.zeros((K, K), dtype=np.float32)
+        P[np.arange(K), perm] = 1.0
+        fails += _exact(orc, "P*B", dtype, encode(P, dtype), B, K, N, K, b[perm],
+                        unit_scales(K, K) if dtype == "fp8" else None, sb)
+        # all ones -> every entry equals K
+        ones_a, ones_b = encode(np.ones((M, K)), dtype), encode(np.ones((K, N)), dtype)
+        fails += _exact(orc, "ones", dtype, ones_a, ones_b, M, N, K, np.full((M, N), float(K)),
+                        unit_scales(M, K) if dtype == "fp8" else None,
+                        unit_scales(K, N) if dtype == "fp8" else None)
+        # rank-1: A[i][k] = u_i, B[k][j] = z_j -> C = K u_i z_j (dyadic, exact)
+        u = np.array([((i % 9) - 4) / 8.0 for i in range(M)])
+        z = np.array([((j % 7) - 3) / 4.0 for j in range(N)])
+        fails += _exact(orc, "rank1", dtype, encode(np.repeat(u[:, None], K, 1), dtype),
+                        encode(np.repeat(z[None, :], K, 0), dtype), M, N, K, K * np.outer(u, z),
+                        unit_scales(M, K) if dtype == "fp8" else None,
+                        unit_scales(K, N) if dtype == "fp8" else None)
+        # K = 1: outer product of a column and a row (each product exact in fp64)
+        A1, sa1 = random_operand(M, 1, dtype, 21)
+        B1, sb1 = random_operand(1, N, dtype, 22)
+        a1 = lib_decode(A1, dtype) * (sa1[0, 0] if dtype == "fp8" else 1.0)
+        b1 = lib_decode(B1, dtype)
+        if dtype == "fp8":
+            b1 = b1 * np.repeat(sb1, 64, axis=1)[:, :N].astype(np.float64)
+            a1 = lib_decode(A1, dtype) * np.repeat(sa1, 64, axis=0)[:M].astype(np.float64)
+        fails += _exact(orc, "K=1", dtype, A1, B1, M, N, 1, a1 * b1, sa1, sb1)
+        # K = 0: the empty sum
+        fails += _exact(orc, "K=0", dtype, A[:, :0], B[:0], M, N, 0, np.zeros((M, N)),
+                        np.zeros((-(-M // 64), 0), np.float32), np.zeros((0, -(-N // 64)), np.float32))
+        # leading dimensions larger than the row: padding (NaN) is never read
+        padA = np.full((M, K + 5), encode(np.array([np.nan]), dtype)[0], dtype=A.dtype)
+        padA[:, :K] = A
+        padB = np.full((K, N + 3), encode(np.array([np.nan]), dtype)[0], dtype=B.dtype)
+        padB[:, :N] = B
+        ref = orc.gemm(dtype, A, B, M, N, K, sa, sb, nthreads=1)
+        got = orc.gemm(dtype, padA[:, :K], padB[:, :N], M, N, K, sa, sb, nthreads=3)
+        if not np.array_equal(ref, got):
+            fails.append(f"leading-dimension padding changed the result ({dtype})")
+    return fails
+
+
+def _bruteforce(A, B, M, N, K, dtype, sa=None, sb=None):
+    a = exact_values(A, dtype, sa)
+    b = exact_values(B, dtype, sb)
+    return [[sum((a[i][k] * b[k][j] for k in range(K)), Fraction(0)) for j in range(N)]
+            for i in range(M)], a, b
+
+
+def _check_bound(name, got, exact, a, b, K) -> list:
+    """|oracle - exact| <= 2 K eps64 sum|a b| (recursive-summation bound)."""
+    fails = []
+    eps = 2.0 ** -53
+    for i in range(len(exact)):
+        for j in range(len(exact[0])):
+            mag = sum(abs(float(a[i][k] * b[k][j])) for k in range(K))
+            err = abs(Fraction(float(got[i][j])) - exact[i][j])
+            if err > Fraction(2 * K * eps * mag + 1e-300):
+                fails.append(f"{name}: entry ({i},{j}) off by {float(err)!r}")
+                return fails
+    return fails
+
+
+def pin_bruteforce(orc) -> list:
+    fails = []
+    shapes = [(1, 1, 1), (2, 3, 4), (5, 7, 3), (8, 8, 8), (3, 1, 6), (7, 4, 1)]
+    for dtype in DTYPES:
+        for t, (M, N, K) in enumerate(shapes):
+            A, sa = random_operand(M, K, dtype, 100 + t)
+            B, sb = random_operand(K, N, dtype, 200 + t)
+            exact, a, b = _bruteforce(A, B, M, N, K, dtype, sa, sb)
+            got = orc.gemm(dtype, A, B, M, N, K, sa, sb, nthreads=2)
+            fails += _check_bound(f"brute {dtype} {M}x{N}x{K}", got, exact, a, b, K)
+    return fails
+
+
+def pin_scale_blocks(orc) -> list:
+    """Several 64x64 scale blocks in every direction, distinct scales: sampled
+    entries against exact rationals (which block scales which element)."""
+    fails = []
+    M, N, K = 150, 140, 200
+    A, sa = random_operand(M, K, "fp8", 31)
+    B, sb = random_operand(K, N, "fp8", 32)
+    rng = np.random.default_rng(4)
+    rows = rng.integers(0, M, 12)
+    cols = rng.integers(0, N, 12)
+    rows[:3], cols[:3] = [0, M - 1, 64], [N - 1, 0, 128]
+    a = exact_values(A, "fp8", sa)
+    b = exact_values(B, "fp8", sb)
+    full = orc.gemm("fp8", A, B, M, N, K, sa, sb, nthreads=4)
+    ent = orc.gemm_entries("fp8", A, B, M, N, K, rows, cols, sa, sb)
+    for t, (i, j) in enumerate(zip(rows, cols)):
+        exact = sum((a[i][k] * b[k][j] for k in range(K)), Fraction(0))
+        mag = sum(abs(float(a[i][k] * b[k][j])) for k in range(K))
+        tol = Fraction(2 * K * 2.0 ** -53 * mag)
+        for name, val in (("gemm", full[i, j]), ("entries", ent[t])):
+            if abs(Fraction(float(val)) - exact) > tol:
+                fails.append(f"fp8 scale blocks {name}: entry ({i},{j})")
+    return fails
+
+
+def pin_entries(orc) -> list:
+    """The per-entry path against exact rationals, every dtype, with ld > row."""
+    fails = []
+    for t, dtype in enumerate(("f16", "bf16", "f32")):
+        M, N, K = 9, 11, 13
+        A, _ = random_operand(M, K + 3, dtype, 300 + t)
+        B, _ = random_operand(K, N + 2, dtype, 400 + t)
+        A, B = A[:, :K], B[:, :N]
+        a = exact_values(np.ascontiguousarray(A), dtype, None)
+        b = exact_values(np.ascontiguousarray(B), dtype, None)
+        rows = np.array([0, 8, 3, 5]); cols = np.array([10, 0, 7, 2])
+        got = orc.gemm_entries(dtype, A, B, M, N, K, rows, cols)
+        for s, (i, j) in enumerate(zip(rows, cols)):
+            exact = sum((a[i][k] * b[k][j] for k in range(K)), Fraction(0))
+            mag = sum(abs(float(a[i][k] * b[k][j])) for k in range(K))
+            if abs(Fraction(float(got[s])) - exact) > Fraction(2 * K * 2.0 ** -53 * mag):
+                fails.append(f"entries {dtype} ({i},{j})")
+    return fails
+
+
+def pin_tolerance_checker(orc) -> list:
+    fails = []
+    ref = np.array([0.0, 1.0, -2.0, 100.0])
+    inside = 0.999 * np.array([1e-3, 1e-3 + 1e-3, -(2e-3 + 1e-3), 0.1 + 1e-3])
+    ok, n, _, _ = orc.within_tolerance(ref + inside, ref, 1e-3, 1e-3)
+    if not ok or n:
+        fails.append("tolerance: boundary values rejected")
+    ok, n, _, _ = orc.within_tolerance(ref + np.array([0, 0, 0, 0.1 + 2e-3]), ref, 1e-3, 1e-3)
+    if ok or n != 1:
+        fails.append("tolerance: out-of-bound value accepted")
+    for bad in (np.nan, np.inf, -np.inf):
+        ok, n, _, _ = orc.within_tolerance(np.array([0.0, bad, 1.0, 100.0]), ref, 1.0, 1.0)
+        if ok:
+            fails.append(f"tolerance: {bad} accepted")
+    return fails
+
+
+ALL_PINS = (pin_decoders, pin_closed_forms, pin_bruteforce, pin_scale_blocks, pin_entries,
+            pin_tolerance_checker)
+
+
+def run_all(orc) -> list:
+    fails = []
+    for pin in ALL_PINS:
+        try:
+            fails += pin(orc)
+        except Exception as e:  # a planted mistake may also make the oracle refuse
+            fails.append(f"{pin.__name__} raised {type(e).__name__}: {e}")
+    return fails

@@ -1,0 +1,111 @@
+"""CPU oracle against its pins (decoders, closed forms, exact brute force), plus
+mutation tests: a mistake planted in a copy of oracle.c must make a pin fail."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def test_decoders_exhaustive(orc):
+    assert pins.pin_decoders(orc) == []
+
+
+def test_closed_forms(orc):
+    assert pins.pin_closed_forms(orc) == []
+
+
+def test_bruteforce_exact_rationals(orc):
+    assert pins.pin_bruteforce(orc) == []
+
+
+def test_fp8_scale_blocks(orc):
+    assert pins.pin_scale_blocks(orc) == []
+
+
+def test_entries_path(orc):
+    assert pins.pin_entries(orc) == []
+
+
+def test_tolerance_checker(orc):
+    assert pins.pin_tolerance_checker(orc) == []
+
+
+def test_thread_count_does_not_change_result(orc):
+    import gemm_inputs as gi
+    A = gi.uniform_h16(67, 45, 1, "bf16")
+    B = gi.uniform_h16(45, 53, 2, "bf16")
+    r1 = orc.gemm("bf16", A, B, 67, 53, 45, nthreads=1)
+    r7 = orc.gemm("bf16", A, B, 67, 53, 45, nthreads=7)
+    assert np.array_equal(r1, r7)
+
+
+def test_bad_arguments_rejected(orc):
+    A = np.zeros((4, 4), np.uint16)
+    with pytest.raises(RuntimeError):
+        orc.gemm_entries("bf16", A, A, 4, 4, 4, np.array([4]), np.array([0]))
+    with pytest.raises(ValueError):
+        orc.gemm("fp8", A.astype(np.uint8), A.astype(np.uint8), 4, 4, 4,
+                 np.ones((2, 2), np.float32), np.ones((1, 1), np.float32))
+
+
+# (original text, planted mistake): each is a plausible slip in the oracle.
+MUTANTS = {
+    "sign": ("ci[j] = ci[j] + aik * bk[j]", "ci[j] = ci[j] - aik * bk[j]"),
+    "dropped_last_term": ("kk < job->k; kk++", "kk + 1 < job->k; kk++"),
+    "b_row_index": ("job->b + kk * job->n", "job->b + kk"),
+    "a_index": ("job->a[i * job->k + kk]", "job->a[i * job->k]"),
+    "no_zero_init": ("for (int64_t j = 0; j < job->n; j++) ci[j] = 0.0;", ""),
+    "f16_exponent": ("e - 25);", "e - 24);"),
+    "f16_subnormal": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    "bf16_exponent": ("e - 134);", "e - 133);"),
+    "bf16_subnormal": ("ldexp((double)f, -133)", "ldexp((double)f, -126)"),
+    "e4m3_nan_rule": ("if (e == 15 && m == 7)", "if (e == 15)"),
+    "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "f32_exponent": ("e - 150);", "e - 149);"),
+    "scale_not_applied": ("* orc_f32_to_f64(sbits)", ""),
+    "scale_grid_transposed": ("(r / ORC_SCALE_BLOCK) * scale_cols + (c / ORC_SCALE_BLOCK)",
+                              "(c / ORC_SCALE_BLOCK) * scale_cols + (r / ORC_SCALE_BLOCK)"),
+    "scale_block_32": ("#define ORC_SCALE_BLOCK 64", "#define ORC_SCALE_BLOCK 32"),
+    "entries_wrong_scale_cols": ("int64_t sb_cols = (N + ORC_SCALE_BLOCK",
+                                 "int64_t sb_cols = (K + ORC_SCALE_BLOCK"),
+}
+
+_RUNNER = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle, oracle_pins
+oracle._lib = oracle.bind(ctypes.CDLL({lib!r}))
+fails = oracle_pins.run_all(oracle)
+print("PIN_FAILURES", len(fails))
+for f in fails[:3]: print(f)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new)
+    with tempfile.TemporaryDirectory() as d:
+        c_path, so_path = os.path.join(d, "m.c"), os.path.join(d, "libm.so")
+        open(c_path, "w").write(mutated)
+        subprocess.run(["gcc", "-O1", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+                        c_path, "-o", so_path, "-lm"], check=True)
+        r = subprocess.run([sys.executable, "-c",
+                            _RUNNER.format(root=ROOT, tests=HERE, lib=so_path)],
+                           capture_output=True, text=True, timeout=300)
+    out = r.stdout + r.stderr
+    if r.returncode != 0:
+        # the planted mistake crashed the oracle: detected, loudly
+        return
+    n = int(out.split("PIN_FAILURES")[1].split()[0])
+    assert n > 0, f"planted mistake {name} passed every pin:\n{out}"
