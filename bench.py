@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""libgemm benchmark: GEMM TFLOP/s (2MNK / time) on MI355X and the fraction of
+the dense matrix-core peak, on seeded synthetic matrices resident in HBM.
+
+A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
+(row-major A and B, fp32 accumulation, bf16 C).  The other workloads (fp16
+4096^3, the ragged bf16 shapes, fp32 4096^3, fp8 block-scaled 8192^3, fp16
+256^3) are measured in the same run and listed under "workloads".
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
+
+Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s at M=N=K=4096 bf16/fp16 + % of MI355X dense MFMA peak"
+# MI355X dense peaks (TFLOP/s): 256 CUs x 2.4 GHz x (4096 bf16/fp16, 8192 fp8,
+# 256 fp32 matrix) flop per clock per CU.  HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+# Best kernel of "[CUDA 优化实战] hgemm - 超越 cuBLAS" section 5 at M=N=K=4096
+# (half precision, RTX 5060 Laptop GPU): 4.075860 ms = 33.72 TFLOP/s.  Context only.
+PAGES_TFLOPS_4096 = 33.72
+ELEM_BYTES = {"f16": 2, "bf16": 2, "f32": 4, "fp8": 1}
+OUT_BYTES = {"f16": 2, "bf16": 2, "f32": 4, "fp8": 2}
+
+
+def tflops(M: int, N: int, K: int, seconds: float) -> float:
+    """The pages' metric: 2*M*N*K floating-point operations over the time."""
+    return 2.0 * M * N * K / seconds / 1e12
+
+
+def algorithmic_bytes(dtype: str, M: int, N: int, K: int) -> int:
+    """Bytes a GEMM must move at least once: A and B read, C written (+ fp8 scales)."""
+    b = ELEM_BYTES[dtype] * (M * K + K * N) + OUT_BYTES[dtype] * M * N
+    if dtype == "fp8":
+        cd = lambda a: -(-a // 64)
+        b += 4 * (cd(M) * cd(K) + cd(K) * cd(N))
+    return b
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_13_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    def __init__(self, name, dtype, M, N, K, wid):
+        self.name, self.dtype, self.M, self.N, self.K, self.wid = name, dtype, M, N, K, wid
+
+    def setup(self):
+        import numpy as np
+        import torch
+
+        import dense_gemm_13_amd as dg
+        import gemm_inputs as gi
+        ops = gi.operands(self.dtype, self.M, self.N, self.K, self.wid)
+        self.ops = ops
+        dev = torch.device("cuda:0")
+        if self.dtype in ("bf16", "f16"):
+            tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
+            self.A = torch.from_numpy(ops["A"].view(np.int16)).view(tdt).to(dev)
+            self.B = torch.from_numpy(ops["B"].view(np.int16)).view(tdt).to(dev)
+            self.C = torch.empty((self.M, self.N), dtype=tdt, device=dev)
+        elif self.dtype == "f32":
+            self.A = torch.from_numpy(ops["A"]).to(dev)
+            self.B = torch.from_numpy(ops["B"]).to(dev)
+            self.C = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
+        else:
+            self.A = torch.from_numpy(ops["A"]).to(dev)
+            self.B = torch.from_numpy(ops["B"]).to(dev)
+            self.sa = torch.from_numpy(ops["scale_a"]).to(dev)
+            self.sb = torch.from_numpy(ops["scale_b"]).to(dev)
+            self.C = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        M, N, K = self.M, self.N, self.K
+        a, b, c = self.A.data_ptr(), self.B.data_ptr(), self.C.data_ptr()
+        if self.dtype == "fp8":
+            fn, sa, sb = dg.lib.gemm_fp8_blockscaled, self.sa.data_ptr(), self.sb.data_ptr()
+            self.call = lambda: fn(a, b, c, M, N, K, K, N, N, sa, sb, s)
+        else:
+            fn = getattr(dg.lib, "gemm_" + self.dtype)
+            self.call = lambda: fn(a, b, c, M, N, K, K, N, N, s)
+        torch.cuda.synchronize()
+
+    def run(self, steps: int, warmup: int) -> dict:
+        import torch
+        for _ in range(warmup):
+            rc = self.call()
+            if rc != 0:
+                raise RuntimeError(f"{self.name}: libgemm returned {rc}")
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(self.stream)
+            self.call()
+            ends[i].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
+        region = starts[0].elapsed_time(ends[-1]) * 1e-3
+        mean = sum(per) / len(per)
+        median = per[len(per) // 2]
+        M, N, K, dt = self.M, self.N, self.K, self.dtype
+        return {
+            "workload": self.name, "dtype": dt, "M": M, "N": N, "K": K,
+            "region_s": region, "wall_s": wall,
+            "mean_launch_us": mean * 1e6, "median_launch_us": median * 1e6,
+            "tflops": tflops(M, N, K, region / steps),
+            "kernel_tflops": tflops(M, N, K, mean),
+            "pct_peak": 100.0 * tflops(M, N, K, mean) / PEAK_TFLOPS[dt],
+            "alg_gbs": algorithmic_bytes(dt, M, N, K) / mean / 1e9,
+        }
+
+
+WORKLOADS = [
+    Workload("bf16 GEMM M=N=K=4096", "bf16", 4096, 4096, 4096, 2),
+    Workload("fp16 GEMM M=N=K=4096", "f16", 4096, 4096, 4096, 2),
+    Workload("fp16 GEMM M=N=K=256", "f16", 256, 256, 256, 1),
+    Workload("bf16 GEMM 1000x1000x1000", "bf16", 1000, 1000, 1000, 3),
+    Workload("bf16 GEMM 4097x4095x4100", "bf16", 4097, 4095, 4100, 3),
+    Workload("bf16 GEMM 8192x64x4096", "bf16", 8192, 64, 4096, 3),
+    Workload("fp32 SGEMM M=N=K=4096", "f32", 4096, 4096, 4096, 4),
+    Workload("fp8 E4M3 64x64-block-scaled GEMM M=N=K=8192, bf16 C", "fp8", 8192, 8192, 8192, 5),
+]
+
+
+def cpu_baseline(headline: Workload) -> dict:
+    """The CPU oracle, as it stands, on the first rows of the headline product."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    rows = 512
+    A = headline.ops["A"][:rows]
+    t0 = time.perf_counter()
+    oracle.gemm(headline.dtype, A, headline.ops["B"], rows, headline.N, headline.K,
+                nthreads=threads)
+    t = time.perf_counter() - t0
+    return {"value": tflops(rows, headline.N, headline.K, t), "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {headline.M} rows of the {headline.name} product "
+                      f"(fp64, bit-exact decode included), {t:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", choices=("headline", "all"), default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library "
+              "has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    headline = WORKLOADS[0]
+    todo = WORKLOADS if args.workloads == "all" else [headline]
+    results = []
+    for w in todo:
+        print(f"[bench] {w.name}: setup", file=sys.stderr, flush=True)
+        w.setup()
+        steps = args.steps if w is headline else max(10, args.steps // 2)
+        r = w.run(steps, args.warmup)
+        print(f"[bench] {w.name}: {r['kernel_tflops']:.1f} TFLOP/s "
+              f"({r['pct_peak']:.1f}% peak), {r['mean_launch_us']:.1f} us/launch",
+              file=sys.stderr, flush=True)
+        results.append(r)
+        if w is not headline:
+            del w.A, w.B, w.C
+            torch.cuda.empty_cache()
+    h = results[0]
+    steps = args.steps
+    flops = 2 * headline.M * headline.N * headline.K
+    out = {
+        "metric": METRIC,
+        "value": round(h["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["region_s"] / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(h["tflops"] / PAGES_TFLOPS_4096, 2),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": headline.name + " (row-major A and B, fp32 accumulation, bf16 C; "
+                   "uniform[-1,1) inputs, seeds A=1002 B=2002)",
+                   "M": headline.M, "N": headline.N, "K": headline.K,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(flops / (h["mean_launch_us"] * 1e-6) / 1e12, 2),
+            "peak": PEAK_TFLOPS["bf16"],
+            "unit": "TFLOP/s",
+            "frac": round(flops / (h["mean_launch_us"] * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "traffic": measured_traffic("bf16_4096"),
+        },
+        "kernel_source_digest": kernel_source_digest(),
+        "workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+                      for r in results],
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(headline)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+"""Python binding of libgemm (dense GEMM C = A*B on MI355X / gfx950).
+
+Argument marshalling only: every step of the product runs in the HIP kernels of
+libgemm.so.  torch supplies device memory and streams.  There is no fallback:
+importing this package without the built library raises ImportError.
+
+Entry points (same names as the C ABI in include/libgemm.h):
+    gemm_f16(A, B, C=None, stream=None)
+    gemm_bf16(A, B, C=None, stream=None)
+    gemm_f32(A, B, C=None, stream=None)
+    gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None)
+A is M x K and B is K x N (row-major: unit column stride; the row stride is the
+leading dimension).  C, when given, must be M x N with unit column stride; it is
+allocated when omitted.  Work is enqueued on `stream` (default: the current
+torch stream of A's device) and the call returns without synchronising.
+
+``lib`` is the raw ctypes handle for calls with plain pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm.so")
+
+GEMM_OK = 0
+STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM_ERR_LD",
+                -4: "GEMM_ERR_ALIGN", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_DEVICE",
+                -7: "GEMM_ERR_LAUNCH"}
+ENTRY_POINTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled",
+                "gemm_status_string", "gemm_version")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libgemm is not built ({LIB_PATH} missing); run "
+                          "`python dense_gemm_13_amd/build.py` or __graft_entry__.build()")
+    h = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    for name in ("gemm_f16", "gemm_bf16", "gemm_f32"):
+        fn = getattr(h, name)
+        fn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    h.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
+    h.gemm_fp8_blockscaled.restype = ctypes.c_int
+    h.gemm_status_string.argtypes = [ctypes.c_int]
+    h.gemm_status_string.restype = ctypes.c_char_p
+    h.gemm_version.argtypes = []
+    h.gemm_version.restype = ctypes.c_int
+    return h
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.gemm_status_string(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ld(t) -> int:
+    """Leading dimension of a 2-D row-major tensor (row stride in elements)."""
+    if t.dim() != 2:
+        raise ValueError(f"expected a 2-D tensor, got {t.dim()}-D")
+    if t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError("tensor must have unit column stride (row-major)")
+    return max(t.stride(0), t.size(1), 1) if t.size(0) > 1 else max(t.size(1), 1)
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != GEMM_OK:
+        raise GemmError(status, where)
+
+
+def _h16(name, want_dtype, A, B, C, stream):
+    torch = _torch()
+    if A.dtype != want_dtype or B.dtype != want_dtype:
+        raise TypeError(f"{name}: A and B must be {want_dtype}")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"{name}: inner dimensions differ ({K} vs {K2})")
+    if C is None:
+        C = torch.empty((M, N), dtype=want_dtype, device=A.device)
+    if C.dtype != want_dtype or tuple(C.shape) != (M, N):
+        raise ValueError(f"{name}: C must be {want_dtype} of shape ({M}, {N})")
+    _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A), _ld(B),
+                              _ld(C), _stream_handle(stream, A.device)), name)
+    return C
+
+
+def gemm_f16(A, B, C=None, stream=None):
+    """C = A @ B for float16 A (M x K), B (K x N); fp32 accumulation, fp16 C."""
+    return _h16("gemm_f16", _torch().float16, A, B, C, stream)
+
+
+def gemm_bf16(A, B, C=None, stream=None):
+    """C = A @ B for bfloat16 A (M x K), B (K x N); fp32 accumulation, bf16 C."""
+    return _h16("gemm_bf16", _torch().bfloat16, A, B, C, stream)
+
+
+def gemm_f32(A, B, C=None, stream=None):
+    """C = A @ B for float32 A (M x K), B (K x N); fp32 accumulation and C."""
+    return _h16("gemm_f32", _torch().float32, A, B, C, stream)
+
+
+def gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None):
+    """C = (A * scale_a) @ (B * scale_b) with E4M3 codes and one fp32 scale per 64 x 64 block.
+
+    A: M x K and B: K x N, torch.uint8 or torch.float8_e4m3fn (OCP E4M3 codes).
+    scale_a: ceil(M/64) x ceil(K/64) float32, scale_b: ceil(K/64) x ceil(N/64)
+    float32, both contiguous.  C: M x N bfloat16.
+    """
+    torch = _torch()
+    if A.dtype not in (torch.uint8, torch.float8_e4m3fn) or B.dtype != A.dtype:
+        raise TypeError("gemm_fp8_blockscaled: A and B must be uint8 or float8_e4m3fn")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"gemm_fp8_blockscaled: inner dimensions differ ({K} vs {K2})")
+    cdiv = lambda a, b: -(-a // b)
+    for s, shape, nm in ((scale_a, (cdiv(M, 64), cdiv(K, 64)), "scale_a"),
+                         (scale_b, (cdiv(K, 64), cdiv(N, 64)), "scale_b")):
+        if s.dtype != torch.float32 or tuple(s.shape) != shape or not s.is_contiguous():
+            raise ValueError(f"gemm_fp8_blockscaled: {nm} must be contiguous float32 {shape}")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, N):
+        raise ValueError(f"gemm_fp8_blockscaled: C must be bfloat16 of shape ({M}, {N})")
+    _check(lib.gemm_fp8_blockscaled(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A),
+                                    _ld(B), _ld(C), scale_a.data_ptr(), scale_b.data_ptr(),
+                                    _stream_handle(stream, A.device)), "gemm_fp8_blockscaled")
+    return C
+
+
+__all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "status_string",
+           "GemmError", "lib", "LIB_PATH"]

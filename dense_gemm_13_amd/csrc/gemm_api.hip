@@ -1,0 +1,197 @@
+// libgemm C ABI: argument checks, device check, dispatch to the kernel launchers.
+//
+// Every entry point checks its arguments synchronously and launches nothing on
+// an error; the work itself is enqueued on the caller's stream.  The library
+// allocates nothing and keeps no per-call state (it caches, per device, whether
+// the device is a gfx950).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "gemm_launch.hpp"
+#include "libgemm.h"
+
+namespace gemm {
+
+namespace {
+
+// Set the M x N window of C to zero (the K == 0 case: every sum is empty).
+template <typename T>
+__global__ void zero_window_kernel(T *__restrict__ C, int M, int N, int64_t ldc)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)M * N) return;
+    const int64_t m = idx / N, n = idx % N;
+    C[m * ldc + n] = T(0);
+}
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<int> g_device_ok[MAX_DEVICES];   // 0 = unknown, 1 = gfx950, -1 = other
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_DEVICE;
+    if (dev >= MAX_DEVICES) return GEMM_ERR_DEVICE;
+    int state = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_DEVICE;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_device_ok[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1 ? GEMM_OK : GEMM_ERR_DEVICE;
+}
+
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+// Bytes spanned by a rows x cols row-major window with leading dimension ld.
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize)
+{
+    if (rows == 0 || cols == 0) return 0;
+    return ((rows - 1) * ld + cols) * esize;
+}
+
+constexpr int64_t DIM_LIMIT = 0x7fffffff;
+
+// Checks shared by all dtypes.  On success returns GEMM_OK and, when there is
+// work to do, leaves *work = true.
+int check_args(const void *A, const void *B, const void *C, int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldc, int64_t esize_in, int64_t esize_out,
+               bool *work)
+{
+    *work = false;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    if (M > DIM_LIMIT || N > DIM_LIMIT || K > DIM_LIMIT) return GEMM_ERR_DIM;
+    if (lda < K || ldb < N || ldc < N) return GEMM_ERR_LD;
+    if (lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40 || ldc > (int64_t)1 << 40)
+        return GEMM_ERR_LD;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (C == nullptr) return GEMM_ERR_NULL;
+    if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL;
+    if ((uintptr_t)C % esize_out) return GEMM_ERR_ALIGN;
+    if (K > 0 && ((uintptr_t)A % esize_in || (uintptr_t)B % esize_in)) return GEMM_ERR_ALIGN;
+    const int64_t cb = span_bytes(M, N, ldc, esize_out);
+    if (K > 0 && (overlaps(C, cb, A, span_bytes(M, K, lda, esize_in)) ||
+                  overlaps(C, cb, B, span_bytes(K, N, ldb, esize_in))))
+        return GEMM_ERR_ALIAS;
+    *work = true;
+    return GEMM_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
+
+int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, int64_t N,
+              int64_t K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    bool work;
+    int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 2, 2, &work);
+    if (st != GEMM_OK || !work) return st;
+    if ((st = check_device()) != GEMM_OK) return st;
+    if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 2, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
+    p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
+                ldc % 8 == 0;
+    int cfg = h16_pick_config(p.M, p.N, p.K);
+    // Tuning / testing override: LIBGEMM_H16_CONFIG=<H16Config id>.
+    if (const char *e = std::getenv("LIBGEMM_H16_CONFIG")) {
+        const int forced = std::atoi(e);
+        if (forced >= 0 && forced < H16_NUM_CONFIGS) cfg = forced;
+    }
+    return to_status(h16_launch(is_bf16, cfg, p));
+}
+
+}  // namespace
+
+hipError_t zero_launch(void *C, int M, int N, int64_t ldc, int esize, hipStream_t stream)
+{
+    const int64_t total = (int64_t)M * N;
+    const int threads = 256;
+    const int64_t blocks = (total + threads - 1) / threads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (esize == 2)
+        hipLaunchKernelGGL(zero_window_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0,
+                           stream, static_cast<uint16_t *>(C), M, N, ldc);
+    else
+        hipLaunchKernelGGL(zero_window_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0,
+                           stream, static_cast<float *>(C), M, N, ldc);
+    return hipGetLastError();
+}
+
+}  // namespace gemm
+
+using namespace gemm;
+
+extern "C" int gemm_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    return h16_entry(false, A, B, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+extern "C" int gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    return h16_entry(true, A, B, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+extern "C" int gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    bool work;
+    int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 4, 4, &work);
+    if (st != GEMM_OK || !work) return st;
+    if ((st = check_device()) != GEMM_OK) return st;
+    if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 4, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
+    p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
+                ldc % 4 == 0;
+    return to_status(f32_launch(p));
+}
+
+extern "C" int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
+                                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                    const float *scale_a, const float *scale_b, hipStream_t stream)
+{
+    bool work;
+    int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 1, 2, &work);
+    if (st != GEMM_OK || !work) return st;
+    if (K > 0 && (scale_a == nullptr || scale_b == nullptr)) return GEMM_ERR_NULL;
+    if (K > 0 && (((uintptr_t)scale_a & 3) || ((uintptr_t)scale_b & 3))) return GEMM_ERR_ALIGN;
+    if (K > 0) {
+        const int64_t cb = span_bytes(M, N, ldc, 2);
+        const int64_t sab = ((M + 63) / 64) * ((K + 63) / 64) * 4;
+        const int64_t sbb = ((K + 63) / 64) * ((N + 63) / 64) * 4;
+        if (overlaps(C, cb, scale_a, sab) || overlaps(C, cb, scale_b, sbb)) return GEMM_ERR_ALIAS;
+    }
+    if ((st = check_device()) != GEMM_OK) return st;
+    if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 2, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
+    p.aligned = aligned16(A) && ((uintptr_t)B & 3) == 0 && aligned16(C) && lda % 16 == 0 &&
+                ldb % 4 == 0 && ldc % 8 == 0;
+    return to_status(fp8_launch(p, scale_a, scale_b));
+}
+
+extern "C" const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_NULL: return "a required pointer is NULL";
+    case GEMM_ERR_DIM: return "M, N or K is negative or too large";
+    case GEMM_ERR_LD: return "leading dimension smaller than the row (lda < K, ldb < N or ldc < N)";
+    case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case GEMM_ERR_ALIAS: return "C overlaps an input";
+    case GEMM_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int gemm_version(void) { return 100; }

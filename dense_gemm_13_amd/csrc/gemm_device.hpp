@@ -1,0 +1,95 @@
+// Device-side building blocks shared by the libgemm kernels (gfx950 only).
+//
+// Vector types for MFMA operands, LDS helpers, the XOR swizzle of 16-byte LDS
+// chunks, the workgroup -> output-tile remap, and fp32 -> fp16/bf16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// 16-byte chunk index XOR pattern for tiles whose rows are 8 chunks (128 bytes)
+// long.  Rows r..r+7 (r a multiple of 8) map a given logical chunk to 8 distinct
+// physical chunks, and so do rows r, r+8, ..., r+56: both the column-of-rows
+// fragment reads and the strided transposed writes spread over all banks.  It is
+// the half-precision XOR swizzle of "[CUDA 优化实战] hgemm - 超越 cuBLAS" section 2
+// (XOR row bits into the 16-byte chunk index, leave the bytes inside a chunk
+// alone), with the row bits chosen for the access patterns of these kernels.
+__host__ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Same idea for rows of 4 chunks (64 bytes, two rows per 128-byte line).
+__host__ __device__ __forceinline__ int swz4(int row) { return (row >> 1) & 3; }
+
+// ---------------------------------------------------------------- tile remap
+//
+// Workgroups of a 1-D grid are handed to the 8 XCDs of the chip round-robin
+// (workgroup b runs on XCD b % 8), and each XCD has its own L2.  The remap first
+// gives each XCD a contiguous range of logical tile ids, then walks tile ids in
+// strips of `group_m` tile-rows so that the tiles one XCD holds at a time share
+// A row-panels and B column-panels in its L2 (the grid swizzle of
+// "[CUDA 优化实战] hgemm - 超越 cuBLAS" section 1, made XCD-aware and correct for
+// grids that are not multiples of the strip width or of 8).
+__host__ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
+                                            int group_m, int &tm, int &tn)
+{
+    constexpr int XCDS = 8;
+    int q = nwg / XCDS, r = nwg % XCDS;
+    int xcd = bid % XCDS, pos = bid / XCDS;
+    int id = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + pos;
+    int per_group = group_m * tiles_n;
+    int g = id / per_group;
+    int first_m = g * group_m;
+    int rows = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    int in_g = id - g * per_group;
+    tm = first_m + in_g % rows;
+    tn = in_g / rows;
+}
+
+// ------------------------------------------------------------ output rounding
+
+// Round to nearest, ties to even (hardware conversions on gfx950).
+__device__ __forceinline__ uint16_t to_bf16_bits(float f)
+{
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint16_t to_f16_bits(float f)
+{
+    _Float16 h = static_cast<_Float16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <bool IS_BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi)
+{
+    if constexpr (IS_BF16)
+        return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+    else
+        return (uint32_t)to_f16_bits(lo) | ((uint32_t)to_f16_bits(hi) << 16);
+}
+
+// -------------------------------------------------------------- MFMA wrappers
+
+// D(32x32, fp32) += X(32x16) * Y(16x32) with X taken from `x` (row = lane%32,
+// k = 8*(lane/32) + 0..7) and Y from `y` (column = lane%32, same k).
+template <bool IS_BF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 x, u32x4 y, f32x16 acc)
+{
+    if constexpr (IS_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x),
+                                                       __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x),
+                                                      __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
+}
+
+}  // namespace gemm

@@ -1,0 +1,38 @@
+// Host-side interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm {
+
+// One GEMM call after argument checking: every size fits in int, K >= 1,
+// M >= 1, N >= 1.  `aligned` says the 16-byte vector paths are legal for this
+// call (pointer and leading-dimension alignment as required by the dtype).
+struct Problem {
+    const void *A;
+    const void *B;
+    void *C;
+    int M, N, K;
+    int64_t lda, ldb, ldc;
+    bool aligned;
+    hipStream_t stream;
+};
+
+// Half-precision tile configurations (rows x cols of C per workgroup, waves).
+enum H16Config {
+    H16_256x256_W8 = 0,   // 256x256 tile, 8 waves (2 x 4), wave tile 128x64
+    H16_128x128_W4 = 1,   // 128x128 tile, 4 waves (2 x 2), wave tile 64x64
+    H16_64x64_W4 = 2,     // 64x64 tile, 4 waves (2 x 2), wave tile 32x32
+    H16_32x64_W2 = 3,     // 32x64 tile, 2 waves (1 x 2), wave tile 32x32
+    H16_NUM_CONFIGS = 4
+};
+
+int h16_pick_config(int M, int N, int K);
+hipError_t h16_launch(bool is_bf16, int config, const Problem &p);
+hipError_t f32_launch(const Problem &p);
+hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
+// Set the M x N window of C (element size esize bytes, leading dimension ldc) to zero.
+hipError_t zero_launch(void *C, int M, int N, int64_t ldc, int esize, hipStream_t stream);
+
+}  // namespace gemm

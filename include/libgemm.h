@@ -1,0 +1,94 @@
+/*
+ * libgemm -- dense GEMM C = A * B on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (all four entry points):
+ *   C[i*ldc + j] = round_out( sum_{k<K} a(i,k) * b(k,j) )   for 0 <= i < M, 0 <= j < N,
+ * with a(i,k) = A[i*lda + k] and b(k,j) = B[k*ldb + j]: A is M x K and B is K x N,
+ * both row-major, as in "[CUDA 优化实战] hgemm - 超越 cuBLAS" sections 0-1 (both
+ * operands row-major, fp16/bf16 inputs, fp32 accumulator, results rounded to the
+ * output type with round-to-nearest-even) and in the register-tiling section of
+ * "CUDA GEMM 优化实践笔记" (fp32 SGEMM, same indexing).  The sum is accumulated in
+ * fp32 in an order of the library's choosing.  There is no alpha, beta, bias or
+ * transpose: C is overwritten.  Bytes of C outside the M x N window (the padding
+ * between N and ldc) are never written.
+ *
+ * Conventions shared by every entry point:
+ *   - A, B, C (and the fp8 scales) are DEVICE pointers owned by the caller, on the
+ *     current HIP device; the library never allocates, frees or synchronises, keeps
+ *     no state between calls and may be called from several host threads.
+ *   - M, N, K >= 0; lda >= K, ldb >= N, ldc >= N (elements, not bytes).
+ *   - Pointers must be aligned to their element size and non-NULL whenever the
+ *     region they describe is non-empty.  C must not overlap A, B or the scales.
+ *   - M == 0 or N == 0: nothing to do, returns GEMM_OK without a launch.
+ *     K == 0: the sums are empty, so the M x N window of C is set to zero.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call returns
+ *     without waiting.  Argument errors are detected synchronously and nothing is
+ *     launched.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Return value: GEMM_OK (0) or a negative gemm_status; gemm_status_string()
+ *     describes it.
+ */
+#ifndef LIBGEMM_H
+#define LIBGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as in the HIP runtime headers. */
+typedef struct ihipStream_t *hipStream_t;
+
+enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_NULL = -1,    /* a required pointer is NULL */
+    GEMM_ERR_DIM = -2,     /* M, N or K negative, or larger than the library supports */
+    GEMM_ERR_LD = -3,      /* lda < K, ldb < N or ldc < N */
+    GEMM_ERR_ALIGN = -4,   /* a pointer is not aligned to its element size */
+    GEMM_ERR_ALIAS = -5,   /* C overlaps an input */
+    GEMM_ERR_DEVICE = -6,  /* the current device is not a gfx950 GPU, or it cannot be queried */
+    GEMM_ERR_LAUNCH = -7   /* the kernel launch was rejected by the runtime */
+};
+
+/* fp16 (IEEE binary16) A, B and C; fp32 accumulation; C rounded to nearest-even.
+ * "[CUDA 优化实战] hgemm - 超越 cuBLAS", sections 1-4 (the half-precision kernels). */
+int gemm_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+             int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream);
+
+/* bfloat16 A, B and C; fp32 accumulation; C rounded to nearest-even.
+ * Same passage as gemm_f16: one kernel design serves both half formats. */
+int gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+              int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream);
+
+/* fp32 A, B and C (SGEMM); fp32 accumulation.
+ * "CUDA GEMM 优化实践笔记", register-tiling section (BM/BN/BK/TM/TN listing and the
+ * zero fill of out-of-range operand elements). */
+int gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+             int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream);
+
+/* FP8 block-scaled GEMM.  A and B hold OCP E4M3 ("E4M3FN") codes, one byte each.
+ * Every 64 x 64 sub-block of A and of B carries one fp32 scale:
+ *   a(i,k) = e4m3(A[i*lda + k]) * scale_a[(i/64) * ceil(K/64) + k/64]
+ *   b(k,j) = e4m3(B[k*ldb + j]) * scale_b[(k/64) * ceil(N/64) + j/64]
+ * i.e. scale_a is the row-major ceil(M/64) x ceil(K/64) grid and scale_b the
+ * row-major ceil(K/64) x ceil(N/64) grid (blocks at ragged edges are partial).
+ * The products are accumulated in fp32 and C is bfloat16, rounded to nearest-even.
+ * "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3 (E4M3
+ * operands scaled per 32x32 or 64x64 sub-block; 64x64 here) and section 5.2, third
+ * pitfall (the scale factors are kept in 32 bits).  Scales must be finite. */
+int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N,
+                         int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                         const float *scale_a, const float *scale_b, hipStream_t stream);
+
+/* Static, NUL-terminated description of a gemm_status value. */
+const char *gemm_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_H */

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every function include/libgemm.h declares,
+and rejects bad arguments synchronously (no GPU needed: errors are found before
+any device call; pointers here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgemm.h")
+
+import dense_gemm_13_amd as dg  # noqa: E402
+
+lib = dg.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gemm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(dg.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        s = dg.status_string(code)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert dg.status_string(-99) == "unknown status"
+    assert lib.gemm_version() >= 100
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    for name, val in re.findall(r"(GEMM_\w+)\s*=\s*(-?\d+)", text):
+        assert dg.STATUS_NAMES[int(val)] == name
+
+
+# Fake, never-dereferenced device addresses: 4 KiB aligned and far apart.
+A, B, C, SA, SB = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def h16(fn, a=A, b=B, c=C, M=64, N=64, K=64, lda=None, ldb=None, ldc=None):
+    return fn(a, b, c, M, N, K, K if lda is None else lda, N if ldb is None else ldb,
+              N if ldc is None else ldc, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_f16", "gemm_bf16", "gemm_f32"])
+def test_argument_errors(name):
+    fn = getattr(lib, name)
+    assert h16(fn, M=-1) == -2
+    assert h16(fn, K=-5) == -2
+    assert h16(fn, N=1 << 31) == -2
+    assert h16(fn, lda=63) == -3
+    assert h16(fn, ldb=63) == -3
+    assert h16(fn, ldc=10) == -3
+    assert h16(fn, c=0) == -1
+    assert h16(fn, a=0) == -1
+    assert h16(fn, b=0) == -1
+    assert h16(fn, a=A + 1) == -4
+    assert h16(fn, c=C + 1) == -4
+    # C overlapping A or B
+    assert h16(fn, c=A + 64) == -5
+    assert h16(fn, c=B) == -5
+
+
+@pytest.mark.parametrize("name", ["gemm_f16", "gemm_bf16", "gemm_f32"])
+def test_empty_problems_do_nothing(name):
+    fn = getattr(lib, name)
+    # M == 0 or N == 0: success without touching the device, even with NULL pointers
+    assert h16(fn, a=0, b=0, c=0, M=0) == 0
+    assert h16(fn, a=0, b=0, c=0, N=0, ldb=0, ldc=0) == 0
+
+
+def test_fp8_argument_errors():
+    fn = lib.gemm_fp8_blockscaled
+
+    def call(a=A, b=B, c=C, M=64, N=64, K=64, sa=SA, sb=SB, lda=64, ldb=64, ldc=64):
+        return fn(a, b, c, M, N, K, lda, ldb, ldc, sa, sb, None)
+
+    assert call(M=-1) == -2
+    assert call(lda=1) == -3
+    assert call(sa=0) == -1
+    assert call(sb=0) == -1
+    assert call(sa=SA + 2) == -4
+    assert call(c=C + 1) == -4
+    assert call(c=SA) == -5           # C overlapping the scale grid
+    assert call(c=A) == -5
+    assert call(a=0, b=0, c=0, sa=0, sb=0, M=0) == 0
+
+
+def test_no_gpu_is_reported_as_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert h16(lib.gemm_bf16) == -6
+    # K == 0 still needs the device (it zeroes C)
+    assert h16(lib.gemm_bf16, a=0, b=0, K=0, lda=0) == -6
+
+
+def test_tensor_binding_validates_before_calling():
+    import torch
+    a = torch.zeros(4, 3, dtype=torch.bfloat16)
+    b = torch.zeros(5, 2, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dg.gemm_bf16(a, b)
+    with pytest.raises(TypeError):
+        dg.gemm_f16(a, torch.zeros(3, 2, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        dg.gemm_bf16(a.t(), torch.zeros(4, 2, dtype=torch.bfloat16))

@@ -1,0 +1,238 @@
+"""GPU parity: libgemm (through its C ABI via the binding) against the CPU
+oracle, entry by entry, on seeded inputs.
+
+* exact probes: permutation matrices and all-ones inputs give results that are
+  exactly representable, so they must match bit for bit (this pins the MFMA
+  operand/accumulator layouts, LDS swizzles, tile remap and epilogue);
+* the five workloads at full size (fp8 8192^3 on sampled entries), in the
+  launch configuration the benchmark times;
+* every half-precision tile configuration forced on ragged shapes, with
+  aligned and unaligned leading dimensions and offset pointers;
+* random small shapes, K = 0, degenerate sizes, and a guard band around C.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_inputs as gi
+import oracle
+from gpu_helpers import TOL, OUT_DTYPE, compare, reference, run_gemm, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+H16_CONFIGS = (0, 1, 2, 3)
+
+
+@pytest.fixture(autouse=True)
+def _clear_config_override():
+    os.environ.pop("LIBGEMM_H16_CONFIG", None)
+    yield
+    os.environ.pop("LIBGEMM_H16_CONFIG", None)
+
+
+def _encode(x, dtype):
+    x = np.asarray(x, dtype=np.float32)
+    return {"f16": gi.to_f16_bits, "bf16": gi.to_bf16_bits, "fp8": gi.to_e4m3_bits,
+            "f32": lambda v: np.ascontiguousarray(v, dtype=np.float32)}[dtype](x)
+
+
+def _unit_scales(r, c):
+    return np.ones((-(-r // 64), -(-c // 64)), dtype=np.float32)
+
+
+def _perm_case(dtype, M, K, seed):
+    """A random (M x K), P a K x K permutation: A*P permutes the columns of A."""
+    ops = gi.operands(dtype, M, K, K, 90 + seed)
+    perm = np.random.default_rng(seed).permutation(K)
+    P = np.zeros((K, K), np.float32)
+    P[np.arange(K), perm] = 1.0
+    ops["B"] = _encode(P, dtype)
+    if dtype == "fp8":
+        ops["scale_a"], ops["scale_b"] = _unit_scales(M, K), _unit_scales(K, K)
+    return ops, perm
+
+
+@pytest.mark.parametrize("dtype,config", [(d, c) for d in ("bf16", "f16") for c in H16_CONFIGS]
+                         + [("f32", None), ("fp8", None)])
+def test_permutation_probe_exact(dtype, config):
+    if config is not None:
+        os.environ["LIBGEMM_H16_CONFIG"] = str(config)
+    M, K = 320, 384
+    say(f"[probe] A*P {dtype} config={config} M={M} N=K={K}")
+    ops, perm = _perm_case(dtype, M, K, 7)
+    _, got = run_gemm(dtype, ops, M, K, K)
+    vals = oracle.decode(ops["A"], dtype) if dtype != "fp8" else oracle.decode(ops["A"], "fp8")
+    want = np.empty((M, K))
+    want[:, perm] = vals
+    gotv = oracle.decode(got, OUT_DTYPE[dtype])
+    bad = np.argwhere(gotv != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}: gpu {gotv[tuple(bad[0])]}, want {want[tuple(bad[0])]}"
+    # P * B permutes the rows of B
+    say(f"[probe] P*B {dtype} config={config}")
+    opsb = gi.operands(dtype, K, M, K, 95)
+    Pm = np.zeros((K, K), np.float32)
+    Pm[np.arange(K), perm] = 1.0
+    opsb["A"] = _encode(Pm, dtype)
+    if dtype == "fp8":
+        opsb["scale_a"], opsb["scale_b"] = _unit_scales(K, K), _unit_scales(K, M)
+    _, got = run_gemm(dtype, opsb, K, M, K)
+    want = oracle.decode(opsb["B"], dtype)[perm]
+    gotv = oracle.decode(got, OUT_DTYPE[dtype])
+    bad = np.argwhere(gotv != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
+@pytest.mark.parametrize("dtype,K,want", [("bf16", 4100, 4096.0), ("f16", 256, 256.0),
+                                          ("f32", 4100, 4100.0), ("fp8", 4100, 4096.0)])
+def test_all_ones_round_to_nearest_even(dtype, K, want):
+    M, N = 300, 200
+    say(f"[ones] {dtype} K={K}")
+    ops = {"A": _encode(np.ones((M, K)), dtype), "B": _encode(np.ones((K, N)), dtype)}
+    if dtype == "fp8":
+        ops["scale_a"], ops["scale_b"] = _unit_scales(M, K), _unit_scales(K, N)
+    _, got = run_gemm(dtype, ops, M, N, K)
+    vals = oracle.decode(got, OUT_DTYPE[dtype])
+    assert np.all(vals == want), f"values {np.unique(vals)[:5]}"
+
+
+def _full_check(dtype, M, N, K, wid, what):
+    say(f"[{what}] {dtype} M={M} N={N} K={K}: generating")
+    ops = gi.operands(dtype, M, N, K, wid)
+    say(f"[{what}] {dtype} M={M} N={N} K={K}: gpu")
+    _, got = run_gemm(dtype, ops, M, N, K)
+    say(f"[{what}] {dtype}: oracle")
+    ref = reference(dtype, ops, M, N, K)
+    ok, msg, worst = compare(dtype, got, ref, what)
+    say(f"[{what}] {msg}")
+    assert ok, msg
+
+
+def test_workload_f16_256():
+    _full_check("f16", 256, 256, 256, 1, "f16_256")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_workload_h16_4096(dtype):
+    _full_check(dtype, 4096, 4096, 4096, 2, "h16_4096")
+
+
+@pytest.mark.parametrize("shape", [(1000, 1000, 1000), (4097, 4095, 4100), (8192, 64, 4096)])
+def test_workload_bf16_ragged(shape):
+    _full_check("bf16", *shape, 3, "bf16_ragged")
+
+
+def test_workload_f32_4096():
+    _full_check("f32", 4096, 4096, 4096, 4, "f32_4096")
+
+
+def test_workload_fp8_8192_sampled():
+    M = N = K = 8192
+    say("[fp8_8192] generating")
+    ops = gi.operands("fp8", M, N, K, 5)
+    say("[fp8_8192] gpu")
+    _, got = run_gemm("fp8", ops, M, N, K)
+    rng = np.random.default_rng(55)
+    rows = [rng.integers(0, M, 3000)]
+    cols = [rng.integers(0, N, 3000)]
+    for r in (0, 4095, M - 1):                # whole rows
+        rows.append(np.full(N // 8, r)); cols.append(np.arange(0, N, 8) + (r % 8))
+    for c in (0, 4097, N - 1):                # whole columns (strided)
+        rows.append(np.arange(0, M, 8) + (c % 8)); cols.append(np.full(M // 8, c))
+    edges = np.array([0, 31, 32, 63, 64, 127, 128, 255, 256, M - 129, M - 128, M - 1])
+    rr, cc = np.meshgrid(edges, edges)
+    rows.append(rr.ravel()); cols.append(cc.ravel())
+    rows, cols = np.concatenate(rows), np.concatenate(cols)
+    say(f"[fp8_8192] oracle on {rows.size} entries")
+    ref = oracle.gemm_entries("fp8", ops["A"], ops["B"], M, N, K, rows, cols,
+                              ops["scale_a"], ops["scale_b"])
+    ok, msg, _ = compare("fp8", got[rows, cols], ref, "fp8_8192 sampled")
+    say(msg)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("shape", [(1000, 900, 700), (512, 512, 512), (130, 70, 200)])
+def test_fp8_full_ragged(shape):
+    _full_check("fp8", *shape, 5, "fp8_small")
+
+
+@pytest.mark.parametrize("dtype,config,aligned",
+                         [(d, c, a) for d in ("bf16", "f16") for c in H16_CONFIGS
+                          for a in (True, False)])
+def test_forced_config_ragged(dtype, config, aligned):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(config)
+    M, N, K = 300, 520, 200 if aligned else 203
+    kw = {} if aligned else dict(lda=K + 3, ldb=N + 1, ldc=N + 5, offset=1)
+    say(f"[forced] {dtype} config={config} aligned={aligned} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 30 + config)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "forced")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "fp8"])
+def test_fuzz_small_shapes(dtype):
+    rng = np.random.default_rng({"f16": 1, "bf16": 2, "f32": 3, "fp8": 4}[dtype])
+    for case in range(12):
+        M, N, K = (int(x) for x in rng.integers(1, 301, 3))
+        kw = {}
+        if case % 2:
+            kw = dict(lda=K + int(rng.integers(0, 9)), ldb=N + int(rng.integers(0, 9)),
+                      ldc=N + int(rng.integers(0, 9)), offset=int(rng.integers(0, 4)))
+        say(f"[fuzz] {dtype} case {case}: {M}x{N}x{K} {kw}")
+        ops = gi.operands(dtype, M, N, K, 60 + case)
+        _, got = run_gemm(dtype, ops, M, N, K, **kw)
+        ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), f"fuzz {M}x{N}x{K}")
+        assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "fp8"])
+def test_degenerate_sizes(dtype):
+    for (M, N, K) in [(1, 1, 1), (1, 257, 33), (257, 1, 65), (3, 5, 1), (64, 64, 1)]:
+        say(f"[degenerate] {dtype} {M}x{N}x{K}")
+        ops = gi.operands(dtype, M, N, K, 70)
+        _, got = run_gemm(dtype, ops, M, N, K)
+        ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "degenerate")
+        assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "fp8"])
+def test_k_zero_sets_window_to_zero(dtype):
+    M, N = 70, 90
+    say(f"[k0] {dtype}")
+    ops = gi.operands(dtype, M, N, 0, 71)
+    C, got = run_gemm(dtype, ops, M, N, 0, ldc=N + 6)
+    assert np.all(oracle.decode(got, OUT_DTYPE[dtype]) == 0.0)
+    pad = C.as_strided((M, 6), (N + 6, 1), C.storage_offset() + N).float().cpu()
+    assert torch.isnan(pad).all(), "padding between N and ldc was written"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+def test_guard_band_untouched(dtype):
+    M, N, K = 200, 150, 130
+    odt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.bfloat16}[dtype]
+    say(f"[guard] {dtype}")
+    ldc = N + 13
+    buf = torch.full((M + 2, ldc), float("nan"), dtype=odt, device="cuda")
+    C = buf[1:M + 1, :N]
+    ops = gi.operands(dtype, M, N, K, 72)
+    run_gemm(dtype, ops, M, N, K, C=C)
+    host = buf.float().cpu()
+    assert torch.isnan(host[0]).all() and torch.isnan(host[M + 1]).all()
+    assert torch.isnan(host[1:M + 1, N:]).all()
+    assert not torch.isnan(host[1:M + 1, :N]).any()
+
+
+def test_stream_argument_is_used():
+    import dense_gemm_13_amd as dg
+    M = N = K = 512
+    ops = gi.operands("bf16", M, N, K, 73)
+    A, B = to_device(ops["A"], "bf16"), to_device(ops["B"], "bf16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C = dg.gemm_bf16(A, B)
+    s.synchronize()
+    got = C.cpu().view(torch.int16).numpy().view(np.uint16)
+    ok, msg, _ = compare("bf16", got, reference("bf16", ops, M, N, K), "side stream")
+    assert ok, msg
