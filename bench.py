@@ -167,7 +167,7 @@ def cpu_baseline(headline: Workload) -> dict:
     """The CPU oracle, as it stands, on the first rows of the headline product."""
     import oracle
     threads = min(16, os.cpu_count() or 1)
-    rows = 512
+    rows = 2048
     A = headline.ops["A"][:rows]
     t0 = time.perf_counter()
     oracle.gemm(headline.dtype, A, headline.ops["B"], rows, headline.N, headline.K,
@@ -186,6 +186,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", choices=("headline", "all"), default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain elementwise copy (torch.neg) of this many MiB, "
+                         "5 times: the known-size kernel that calibrates HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library "
@@ -213,6 +216,17 @@ def main():
         if w is not headline:
             del w.A, w.B, w.C
             torch.cuda.empty_cache()
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 5 x torch.neg over {args.copy_mib} MiB "
+              f"(reads {args.copy_mib} MiB, writes {args.copy_mib} MiB each)",
+              file=sys.stderr, flush=True)
+        del src, dst
     h = results[0]
     steps = args.steps
     flops = 2 * headline.M * headline.N * headline.K

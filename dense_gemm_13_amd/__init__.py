@@ -42,6 +42,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libgemm is not built ({LIB_PATH} missing); run "
                           "`python dense_gemm_13_amd/build.py` or __graft_entry__.build()")
+    # torch ships its own HIP runtime (soname libamdhip64.so.7, but its libraries
+    # ask for "libamdhip64.so").  Loading torch first makes libgemm bind to that
+    # same runtime; loading libgemm first would put a second HIP runtime in the
+    # process, and device pointers / streams from torch would not belong to it.
+    import torch  # noqa: F401
     h = ctypes.CDLL(LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     for name in ("gemm_f16", "gemm_bf16", "gemm_f32"):
@@ -73,6 +78,8 @@ def _ld(t) -> int:
     """Leading dimension of a 2-D row-major tensor (row stride in elements)."""
     if t.dim() != 2:
         raise ValueError(f"expected a 2-D tensor, got {t.dim()}-D")
+    if t.numel() == 0:          # no elements: strides are meaningless
+        return max(t.size(1), 1)
     if t.size(1) > 1 and t.stride(1) != 1:
         raise ValueError("tensor must have unit column stride (row-major)")
     return max(t.stride(0), t.size(1), 1) if t.size(0) > 1 else max(t.size(1), 1)
