@@ -100,11 +100,14 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
     p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
                 ldc % 8 == 0;
-    int cfg = h16_pick_config(p.M, p.N, p.K);
-    // Tuning / testing override: LIBGEMM_H16_CONFIG=<H16Config id>.
+    int cfg = h16_fast_eligible(p) ? (int)H16_FAST_256x256 : h16_pick_config(p.M, p.N, p.K);
+    // Tuning / testing override: LIBGEMM_H16_CONFIG=<H16Config id> (the large-tile
+    // path only where it is eligible).
     if (const char *e = std::getenv("LIBGEMM_H16_CONFIG")) {
         const int forced = std::atoi(e);
-        if (forced >= 0 && forced < H16_NUM_CONFIGS) cfg = forced;
+        if (forced >= 0 && forced < H16_NUM_CONFIGS &&
+            (forced != H16_FAST_256x256 || h16_fast_eligible(p)))
+            cfg = forced;
     }
     return to_status(h16_launch(is_bf16, cfg, p));
 }

@@ -259,7 +259,7 @@ int h16_pick_config(int M, int N, int K)
 {
     (void)K;
     static const int bm[] = {256, 128, 64, 32}, bn[] = {256, 128, 64, 64};
-    for (int c = 0; c < H16_NUM_CONFIGS; ++c) {
+    for (int c = 0; c < 4; ++c) {
         const int64_t tiles = (int64_t)((M + bm[c] - 1) / bm[c]) * ((N + bn[c] - 1) / bn[c]);
         if (tiles >= 128) return c;
     }
@@ -268,6 +268,7 @@ int h16_pick_config(int M, int N, int K)
 
 hipError_t h16_launch(bool is_bf16, int config, const Problem &p)
 {
+    if (config == H16_FAST_256x256) return h16_fast_launch(is_bf16, p);
     return is_bf16 ? launch_typed<true>(config, p) : launch_typed<false>(config, p);
 }
 

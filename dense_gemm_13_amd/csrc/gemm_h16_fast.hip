@@ -1,0 +1,330 @@
+// fp16 / bf16 GEMM, large-tile path for gfx950 (whole 256 x 256 tiles, K a
+// multiple of BK * STAGES, 16-byte aligned operands).
+//
+// Same product as gemm_h16.hip; what changes is how operands travel:
+//   * global -> LDS with global_load_lds_dwordx4: each lane's 16 bytes land at
+//     LDS base + 16*lane without passing through registers.  The XOR swizzle of
+//     the 16-byte chunks is applied by choosing which global chunk each lane
+//     fetches, so the LDS writes stay contiguous;
+//   * B stays in LDS as rows of k (n contiguous, exactly as in memory) and the
+//     MFMA operand "8 consecutive k of one column" is produced by the LDS
+//     transposing read ds_read_b64_tr_b16: within each 16-lane group, lanes
+//     4r..4r+3 address 16 consecutive n of row r and lane j receives element j of
+//     each of the 4 rows;
+//   * 4 waves (one per SIMD), each owning a 128 x 128 sub-tile as 4 x 4 MFMA
+//     32x32x16 tiles (256 fp32 accumulators per lane), which halves the LDS
+//     bytes read per MFMA compared with 64-column wave tiles;
+//   * a ring of STAGES LDS stages, one separate array per stage and stage
+//     indices known at compile time, so the compiler can tell that loads into
+//     one stage do not alias reads of another and does not serialise them.  The
+//     loads for K step t + STAGES - 1 are issued at step t: a global load has
+//     STAGES - 1 steps to land.  Each wave waits for its own loads of the
+//     current stage and a barrier publishes the stage to all waves.
+// "[CUDA 优化实战] hgemm - 超越 cuBLAS" sections 1-4 describe the same stages
+// (asynchronous 16-byte copies, swizzled shared memory, double buffering,
+// transposing fragment loads) for a different machine.
+#include <utility>
+
+#include "gemm_device.hpp"
+#include "gemm_launch.hpp"
+
+namespace gemm {
+
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+constexpr int FBM = 256, FBN = 256;
+constexpr int FWM = 2, FWN = 2, FNW = FWM * FWN;
+constexpr int FWTM = FBM / FWM, FWTN = FBN / FWN;       // 128 x 128 per wave
+constexpr int FFM = FWTM / 32, FFN = FWTN / 32;         // 4 x 4 MFMA tiles
+constexpr int FAST_BK = 32, FAST_STAGES = 4;
+
+// One LDS array per (stage, operand): distinct objects for alias analysis.
+template <int TAG, int HALVES>
+__shared__ __attribute__((aligned(1024))) uint16_t lds_stage[HALVES];
+
+// A rows of 64 bytes (4 chunks): rows r..r+7 and r..r+15 at one logical chunk
+// land in distinct banks whether the LDS serves 8 or 16 lanes of a 16-byte read
+// per cycle.  Rows of 128 bytes use swz8.
+__host__ __device__ __forceinline__ int swz_a4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+template <int BK>
+__host__ __device__ __forceinline__ int swz_a(int row)
+{
+    if constexpr (BK == 64) return swz8(row);
+    else return swz_a4(row);
+}
+
+// B rows are 512 bytes (32 chunks).  Rows k..k+3 read by one transposing load
+// get their 32-byte pieces XOR-moved by 64 bytes per row, so the 16 lanes of a
+// group (and the two groups sharing rows) cover distinct banks.
+__host__ __device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
+
+__device__ __forceinline__ void dma16(const void *src, uint16_t *lds_block)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_block, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (N < 64), leaving expcnt and lgkmcnt alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads(): those
+// would wait for every outstanding global->LDS load (vmcnt(0)) and collapse the
+// ring to one stage in flight.  Callers wait for exactly the loads they need
+// first; the "memory" clobber keeps the compiler from moving memory accesses
+// across the barrier.  LDS reads issued before it have all been consumed by
+// MFMAs already, so no stage is overwritten while still being read.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F &&f)
+{
+    unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <bool IS_BF16, int BK, int STAGES>
+__global__ void __launch_bounds__(FNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+                uint16_t *__restrict__ C, int K, int64_t lda, int64_t ldb, int64_t ldc,
+                int tiles_m, int tiles_n, int group_m)
+{
+    constexpr int A_STAGE = FBM * BK;                    // halves per stage
+    constexpr int B_STAGE = BK * FBN;
+    constexpr int CPR = BK / 8;                          // 16-byte chunks per A row
+    constexpr int ROWS_PER_KB = 1024 / (BK * 2);         // A rows per 1 KiB load
+    constexpr int A_BLK = A_STAGE * 2 / 1024 / FNW;      // 1 KiB loads per wave per stage
+    constexpr int B_BLK = B_STAGE * 2 / 1024 / FNW;
+    constexpr int SUB = BK / 16;                         // MFMA K sub-steps per stage
+    static_assert(A_BLK >= 1 && B_BLK >= 1 && SUB >= 2, "stage shape");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / FWN) * FWTM;
+    const int wn0 = (wave % FWN) * FWTN;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * FBM, n0 = tn * FBN;
+
+    // ---- per-lane sources of this wave's 1 KiB loads: a wave-uniform base
+    // (this tile's first row of A / first column of B at K step kt) plus a
+    // 32-bit byte offset per lane and load.
+    // A block b: lane -> row ROWS_PER_KB*b + lane/CPR, slot lane%CPR, which
+    // holds logical chunk slot ^ swz_a(row).
+    uint32_t a_off[A_BLK];
+#pragma unroll
+    for (int j = 0; j < A_BLK; ++j) {
+        const int row = ROWS_PER_KB * (wave * A_BLK + j) + lane / CPR;
+        a_off[j] = (uint32_t)(row * lda + 8 * ((lane % CPR) ^ swz_a<BK>(row))) * 2u;
+    }
+    // B block b (2 rows of 512 bytes): lane -> row 2b + lane/32, slot lane%32.
+    uint32_t b_off_g[B_BLK];
+#pragma unroll
+    for (int j = 0; j < B_BLK; ++j) {
+        const int row = 2 * (wave * B_BLK + j) + (lane >> 5);
+        b_off_g[j] = (uint32_t)(row * ldb + 8 * ((lane & 31) ^ swz_b(row))) * 2u;
+    }
+    const char *a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
+    const char *b_base = reinterpret_cast<const char *>(B + n0);
+    const int64_t a_step = (int64_t)BK * 2, b_step = (int64_t)BK * ldb * 2;
+
+    auto issue = [&](uint16_t *as, uint16_t *bs, int kt) {
+        const char *ab = a_base + kt * a_step;
+        const char *bb = b_base + kt * b_step;
+#pragma unroll
+        for (int j = 0; j < A_BLK; ++j) dma16(ab + a_off[j], as + (wave * A_BLK + j) * 512);
+#pragma unroll
+        for (int j = 0; j < B_BLK; ++j) dma16(bb + b_off_g[j], bs + (wave * B_BLK + j) * 512);
+    };
+
+    // ---- fragment addressing (in halves, relative to a stage)
+    // A: lane reads row wm0 + 32i + l32, logical chunk 2s + half.
+    int a_row_off[FFM], a_swz[FFM];
+#pragma unroll
+    for (int i = 0; i < FFM; ++i) {
+        const int row = wm0 + 32 * i + l32;
+        a_row_off[i] = row * BK;
+        a_swz[i] = swz_a<BK>(row);
+    }
+    // B: 16-lane group g, lane w in it: row r = w/4 of the 4 rows read, column
+    // piece 4*(w%4); groups 0/1 take columns 0-15 / 16-31 of the 32-wide tile,
+    // groups 0,1 / 2,3 take k 0-7 / 8-15 of the 16-wide step.
+    const int g = lane >> 4, w16 = lane & 15, r4 = w16 >> 2, c4 = w16 & 3;
+    int b_off[FFN];
+#pragma unroll
+    for (int j = 0; j < FFN; ++j) {
+        const int n = wn0 + 32 * j + 16 * (g & 1) + 4 * c4;
+        b_off[j] = (((n >> 3) ^ swz_b(r4)) << 3) + (n & 7);
+    }
+    const int b_krow = 8 * (g >> 1) + r4;    // + 16 s + 4 q
+
+    f32x16 acc[FFM][FFN];
+#pragma unroll
+    for (int i = 0; i < FFM; ++i)
+#pragma unroll
+        for (int j = 0; j < FFN; ++j) acc[i][j] = f32x16{};
+
+    // Fragments of one 16-wide K sub-step: 4 A tiles (ds_read_b128) and 4 B
+    // tiles (two transposing reads each).
+    struct Frags {
+        u32x4 a[FFM], b[FFN];
+    };
+    auto load_frags = [&](Frags &f, const uint16_t *as, const uint16_t *bs, int s) {
+        const int c = 2 * s + half;
+#pragma unroll
+        for (int i = 0; i < FFM; ++i)
+            f.a[i] = *reinterpret_cast<const u32x4 *>(as + a_row_off[i] + ((c ^ a_swz[i]) << 3));
+#pragma unroll
+        for (int j = 0; j < FFN; ++j) {
+            const uint16_t *p0 = bs + (16 * s + b_krow) * FBN + b_off[j];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p0 + 4 * FBN));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            f.b[j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < FFM; ++i)
+#pragma unroll
+            for (int j = 0; j < FFN; ++j)
+                acc[i][j] = mfma32x32x16<IS_BF16>(f.b[j], f.a[i], acc[i][j]);
+    };
+
+    // K step t runs on stage t % STAGES with the fragments of its first
+    // sub-step already in registers.  Sub-steps 0 .. SUB-2 multiply while the
+    // following sub-step's fragments are read.  Then, before the last sub-step:
+    // wait for this wave's loads of stage t+1, barrier (everyone's loads of stage
+    // t+1 have landed, everyone has finished reading stage t-1), read stage
+    // t+1's first fragments and issue the global->LDS loads of K step
+    // t + STAGES - 1 into stage t-1 while the last sub-step multiplies.  A load
+    // therefore has STAGES - 2 steps to land, and the LDS latency of a step's
+    // first fragments hides behind the previous step's last MFMAs.
+    constexpr int NBLK = A_BLK + B_BLK;
+    constexpr int DS = 2 * FFN + FFM;                   // LDS reads per sub-step (12)
+    static_assert(STAGES >= 3, "ring depth");
+    Frags cur, nxt;
+    auto step = [&](const uint16_t *as, const uint16_t *bs, const uint16_t *nas_read,
+                    const uint16_t *nbs_read, uint16_t *nas_dma, uint16_t *nbs_dma,
+                    int next_kt) {
+#pragma unroll
+        for (int s = 0; s + 1 < SUB; ++s) {
+            load_frags(nxt, as, bs, s + 1);
+            mfmas(cur);
+            cur = nxt;
+#pragma unroll
+            for (int x = 0; x < DS / 2; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(STAGES - 3) * NBLK>();
+        barrier_no_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(nxt, nas_read, nbs_read, 0);
+        issue(nas_dma, nbs_dma, next_kt);
+        mfmas(cur);
+        cur = nxt;
+#pragma unroll
+        for (int x = 0; x < DS / 2; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < NBLK; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2 - NBLK, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: K steps 0 .. STAGES-2 in flight, stage 0 published, its first
+    // fragments read.  Step kt + S issues K step kt + S + STAGES - 1 into the
+    // stage step kt + S - 1 used.  Indices past the end are clamped: the last
+    // steps re-fetch the final K tile into stages nobody reads any more, and the
+    // last step's look-ahead reads a stage whose contents are not used
+    // (identical code in every step).  All loads are drained before the epilogue.
+    const int ktiles = K / BK;                           // a multiple of STAGES
+    unroll<STAGES - 1>([&](auto S) {
+        issue(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>, S);
+    });
+    wait_vmcnt<(STAGES - 2) * NBLK>();
+    barrier_no_fence();
+    load_frags(cur, lds_stage<0, A_STAGE>, lds_stage<STAGES, B_STAGE>, 0);
+    for (int kt = 0; kt < ktiles; kt += STAGES) {
+        unroll<STAGES>([&](auto S) {
+            constexpr int N1 = (S + 1) % STAGES;           // next stage (read ahead)
+            constexpr int NS = (S + STAGES - 1) % STAGES;  // stage to refill
+            const int next = kt + S + STAGES - 1;
+            step(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>,
+                 lds_stage<N1, A_STAGE>, lds_stage<STAGES + N1, B_STAGE>,
+                 lds_stage<NS, A_STAGE>, lds_stage<STAGES + NS, B_STAGE>,
+                 next < ktiles ? next : ktiles - 1);
+        });
+    }
+    wait_vmcnt<0>();
+
+    // ---- epilogue: lane holds C[m][n..n+3] for n = 8q + 4*half (+ tile offsets)
+#pragma unroll
+    for (int i = 0; i < FFM; ++i) {
+        const int m = m0 + wm0 + 32 * i + l32;
+        uint16_t *crow = C + (int64_t)m * ldc + n0 + wn0 + 4 * half;
+#pragma unroll
+        for (int j = 0; j < FFN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u32x2 *>(crow + 32 * j + 8 * q) =
+                    u32x2{pack2<IS_BF16>(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                          pack2<IS_BF16>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+    }
+}
+
+}  // namespace
+
+// Whole tiles and a whole number of stage rings only; the per-lane 32-bit byte
+// offsets (up to 256 rows of A or BK rows of B past the tile's base) must fit.
+bool h16_fast_eligible(const Problem &p)
+{
+    return p.aligned && p.M % FBM == 0 && p.N % FBN == 0 &&
+           p.K % (FAST_BK * FAST_STAGES) == 0 && p.lda < (1 << 22) && p.ldb < (1 << 24);
+}
+
+hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_fast_eligible(p)) return hipErrorInvalidValue;
+    const int tiles_m = p.M / FBM, tiles_n = p.N / FBN;
+    const int64_t nwg = (int64_t)tiles_m * tiles_n;
+    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    const int group_m = tiles_m < 4 ? tiles_m : 4;
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+    uint16_t *C = static_cast<uint16_t *>(p.C);
+    if (is_bf16)
+        hipLaunchKernelGGL((h16_fast_kernel<true, FAST_BK, FAST_STAGES>), dim3((unsigned)nwg),
+                           dim3(FNW * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
+                           tiles_m, tiles_n, group_m);
+    else
+        hipLaunchKernelGGL((h16_fast_kernel<false, FAST_BK, FAST_STAGES>), dim3((unsigned)nwg),
+                           dim3(FNW * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
+                           tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace gemm

@@ -22,7 +22,8 @@ from gpu_helpers import TOL, OUT_DTYPE, compare, reference, run_gemm, say, to_de
 
 pytestmark = pytest.mark.gpu
 
-H16_CONFIGS = (0, 1, 2, 3)
+H16_CONFIGS = (0, 1, 2, 3, 4)
+FAST = 4          # whole 256x256 tiles, K % 128 == 0, aligned
 
 
 @pytest.fixture(autouse=True)
@@ -59,7 +60,7 @@ def _perm_case(dtype, M, K, seed):
 def test_permutation_probe_exact(dtype, config):
     if config is not None:
         os.environ["LIBGEMM_H16_CONFIG"] = str(config)
-    M, K = 320, 384
+    M, K = (512, 512) if config == FAST else (320, 384)
     say(f"[probe] A*P {dtype} config={config} M={M} N=K={K}")
     ops, perm = _perm_case(dtype, M, K, 7)
     _, got = run_gemm(dtype, ops, M, K, K)
@@ -168,6 +169,19 @@ def test_forced_config_ragged(dtype, config, aligned):
     ops = gi.operands(dtype, M, N, K, 30 + config)
     _, got = run_gemm(dtype, ops, M, N, K, **kw)
     ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "forced")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(256, 256, 128), (512, 768, 384), (1024, 512, 2048),
+                                   (768, 256, 1152)])
+def test_fast_path_whole_tiles(dtype, shape):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(FAST)
+    M, N, K = shape
+    say(f"[fast] {dtype} {M}x{N}x{K}")
+    ops = gi.operands(dtype, M, N, K, 40)
+    _, got = run_gemm(dtype, ops, M, N, K)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "fast")
     assert ok, msg
 
 
