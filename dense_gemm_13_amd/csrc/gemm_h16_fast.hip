@@ -281,18 +281,47 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     }
     wait_vmcnt<0>();
 
-    // ---- epilogue: lane holds C[m][n..n+3] for n = 8q + 4*half (+ tile offsets)
+    // ---- epilogue through LDS (the ring is idle now): each wave converts its
+    // 128 x 128 sub-tile to 16-bit and writes it to two 16 KiB ring arrays
+    // (rows 0-63, 64-127; 256-byte rows), then stores whole 256-byte row
+    // segments with 16 bytes per lane.  Lane l holds C[32i + l%32][32j + 8q +
+    // 4*(l/32) .. +3]: 8 bytes in 16-byte chunk 4j + q, half l/32.  Chunks are
+    // XORed with row % 16 and the half with bit 4 of the row, so the 32 rows a
+    // store touches fill all banks.
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): own LDS reads done
+    barrier_no_fence();                                  // every wave is done with the ring
+    static_assert(A_STAGE == 8192 && B_STAGE == 8192 && STAGES == 4, "epilogue staging");
+    uint16_t *st0, *st1;
+    switch (wave) {
+    case 0: st0 = lds_stage<0, A_STAGE>; st1 = lds_stage<1, A_STAGE>; break;
+    case 1: st0 = lds_stage<2, A_STAGE>; st1 = lds_stage<3, A_STAGE>; break;
+    case 2: st0 = lds_stage<4, B_STAGE>; st1 = lds_stage<5, B_STAGE>; break;
+    default: st0 = lds_stage<6, B_STAGE>; st1 = lds_stage<7, B_STAGE>; break;
+    }
 #pragma unroll
     for (int i = 0; i < FFM; ++i) {
-        const int m = m0 + wm0 + 32 * i + l32;
-        uint16_t *crow = C + (int64_t)m * ldc + n0 + wn0 + 4 * half;
+        const int row = 32 * i + l32;
+        uint16_t *buf = (row < 64 ? st0 : st1) + (row & 63) * FWTN;
+        const int hsw = half ^ ((row >> 4) & 1);
 #pragma unroll
         for (int j = 0; j < FFN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<u32x2 *>(crow + 32 * j + 8 * q) =
+            for (int q = 0; q < 4; ++q) {
+                const int chunk = (4 * j + q) ^ (row & 15);
+                *reinterpret_cast<u32x2 *>(buf + chunk * 8 + hsw * 4) =
                     u32x2{pack2<IS_BF16>(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                           pack2<IS_BF16>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            }
+    }
+    uint16_t *const cbase = C + (int64_t)(m0 + wm0) * ldc + n0 + wn0;
+    const int cl = lane & 15;
+#pragma unroll
+    for (int it = 0; it < FWTM / 4; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        const uint16_t *buf = (row < 64 ? st0 : st1) + (row & 63) * FWTN;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(buf + ((cl ^ (row & 15)) << 3));
+        if ((row >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        *reinterpret_cast<u32x4 *>(cbase + (int64_t)row * ldc + 8 * cl) = v;
     }
 }
 
