@@ -37,10 +37,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int FBM = 256, FBN = 256;
-constexpr int FWM = 2, FWN = 2, FNW = FWM * FWN;
-constexpr int FWTM = FBM / FWM, FWTN = FBN / FWN;       // 128 x 128 per wave
-constexpr int FFM = FWTM / 32, FFN = FWTN / 32;         // 4 x 4 MFMA tiles
 constexpr int FAST_BK = 32, FAST_STAGES = 4;
+constexpr int FAST_WM = 2, FAST_WN = 2;                  // waves along M and N
 
 // One LDS array per (stage, operand): distinct objects for alias analysis.
 template <int TAG, int HALVES>
@@ -94,12 +92,31 @@ __device__ __forceinline__ void unroll(F &&f)
     unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <bool IS_BF16, int BK, int STAGES>
-__global__ void __launch_bounds__(FNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// The 16 KiB ring array with index idx (stages of A first, then of B).
+template <int HALVES>
+__device__ __forceinline__ uint16_t *ring_array(int idx)
+{
+    switch (idx) {
+    case 0: return lds_stage<0, HALVES>;
+    case 1: return lds_stage<1, HALVES>;
+    case 2: return lds_stage<2, HALVES>;
+    case 3: return lds_stage<3, HALVES>;
+    case 4: return lds_stage<4, HALVES>;
+    case 5: return lds_stage<5, HALVES>;
+    case 6: return lds_stage<6, HALVES>;
+    default: return lds_stage<7, HALVES>;
+    }
+}
+
+template <bool IS_BF16, int BK, int STAGES, int WM, int WN>
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int K, int64_t lda, int64_t ldb, int64_t ldc,
                 int tiles_m, int tiles_n, int group_m)
 {
+    constexpr int FNW = WM * WN;
+    constexpr int FWTM = FBM / WM, FWTN = FBN / WN;      // wave sub-tile
+    constexpr int FFM = FWTM / 32, FFN = FWTN / 32;      // MFMA tiles per wave
     constexpr int A_STAGE = FBM * BK;                    // halves per stage
     constexpr int B_STAGE = BK * FBN;
     constexpr int CPR = BK / 8;                          // 16-byte chunks per A row
@@ -112,8 +129,8 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave / FWN) * FWTM;
-    const int wn0 = (wave % FWN) * FWTN;
+    const int wm0 = (wave / WN) * FWTM;
+    const int wn0 = (wave % WN) * FWTN;
     const int l32 = lane & 31, half = lane >> 5;
 
     int tm, tn;
@@ -251,6 +268,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
+        static_assert(FFM * FFN >= DS / 2 + NBLK, "MFMAs to interleave with");
         __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2 - NBLK, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -282,45 +300,46 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     wait_vmcnt<0>();
 
     // ---- epilogue through LDS (the ring is idle now): each wave converts its
-    // 128 x 128 sub-tile to 16-bit and writes it to two 16 KiB ring arrays
-    // (rows 0-63, 64-127; 256-byte rows), then stores whole 256-byte row
-    // segments with 16 bytes per lane.  Lane l holds C[32i + l%32][32j + 8q +
-    // 4*(l/32) .. +3]: 8 bytes in 16-byte chunk 4j + q, half l/32.  Chunks are
-    // XORed with row % 16 and the half with bit 4 of the row, so the 32 rows a
-    // store touches fill all banks.
+    // sub-tile to 16-bit and writes it to its own 16 KiB ring arrays, then stores
+    // whole row segments of the sub-tile with 16 bytes per lane.  Lane l holds
+    // C[32i + l%32][32j + 8q + 4*(l/32) .. +3]: 8 bytes in 16-byte chunk 4j + q,
+    // half l/32.  Chunks are XORed with the row modulo the chunks per row and the
+    // half with the next row bit, so the rows one store touches spread over the
+    // banks.
+    static_assert(A_STAGE == 8192 && B_STAGE == 8192 && 2 * STAGES == 8, "epilogue staging");
+    constexpr int ARR = FWTM * FWTN / 8192;              // ring arrays per wave
+    constexpr int ROWS_PER_ARR = 8192 / FWTN;
+    constexpr int CPRC = FWTN / 8;                       // 16-byte chunks per staged row
+    constexpr int RPI = 1024 / (FWTN * 2);               // rows per 1 KiB store
+    static_assert(ARR >= 1 && ARR * FNW <= 8, "staging space");
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): own LDS reads done
     barrier_no_fence();                                  // every wave is done with the ring
-    static_assert(A_STAGE == 8192 && B_STAGE == 8192 && STAGES == 4, "epilogue staging");
-    uint16_t *st0, *st1;
-    switch (wave) {
-    case 0: st0 = lds_stage<0, A_STAGE>; st1 = lds_stage<1, A_STAGE>; break;
-    case 1: st0 = lds_stage<2, A_STAGE>; st1 = lds_stage<3, A_STAGE>; break;
-    case 2: st0 = lds_stage<4, B_STAGE>; st1 = lds_stage<5, B_STAGE>; break;
-    default: st0 = lds_stage<6, B_STAGE>; st1 = lds_stage<7, B_STAGE>; break;
-    }
+    uint16_t *st[ARR];
+#pragma unroll
+    for (int a = 0; a < ARR; ++a) st[a] = ring_array<8192>(wave * ARR + a);
 #pragma unroll
     for (int i = 0; i < FFM; ++i) {
         const int row = 32 * i + l32;
-        uint16_t *buf = (row < 64 ? st0 : st1) + (row & 63) * FWTN;
-        const int hsw = half ^ ((row >> 4) & 1);
+        uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
+        const int hsw = half ^ ((row / CPRC) & 1);
 #pragma unroll
         for (int j = 0; j < FFN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int chunk = (4 * j + q) ^ (row & 15);
+                const int chunk = (4 * j + q) ^ (row % CPRC);
                 *reinterpret_cast<u32x2 *>(buf + chunk * 8 + hsw * 4) =
                     u32x2{pack2<IS_BF16>(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                           pack2<IS_BF16>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
             }
     }
     uint16_t *const cbase = C + (int64_t)(m0 + wm0) * ldc + n0 + wn0;
-    const int cl = lane & 15;
+    const int cl = lane % CPRC;
 #pragma unroll
-    for (int it = 0; it < FWTM / 4; ++it) {
-        const int row = 4 * it + (lane >> 4);
-        const uint16_t *buf = (row < 64 ? st0 : st1) + (row & 63) * FWTN;
-        u32x4 v = *reinterpret_cast<const u32x4 *>(buf + ((cl ^ (row & 15)) << 3));
-        if ((row >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+    for (int it = 0; it < FWTM / RPI; ++it) {
+        const int row = RPI * it + lane / CPRC;
+        const uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
+        u32x4 v = *reinterpret_cast<const u32x4 *>(buf + ((cl ^ (row % CPRC)) << 3));
+        if ((row / CPRC) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
         *reinterpret_cast<u32x4 *>(cbase + (int64_t)row * ldc + 8 * cl) = v;
     }
 }
@@ -346,12 +365,12 @@ hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
     if (is_bf16)
-        hipLaunchKernelGGL((h16_fast_kernel<true, FAST_BK, FAST_STAGES>), dim3((unsigned)nwg),
-                           dim3(FNW * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
+        hipLaunchKernelGGL((h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN>),
+                           dim3((unsigned)nwg), dim3(FAST_WM * FAST_WN * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
                            tiles_m, tiles_n, group_m);
     else
-        hipLaunchKernelGGL((h16_fast_kernel<false, FAST_BK, FAST_STAGES>), dim3((unsigned)nwg),
-                           dim3(FNW * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
+        hipLaunchKernelGGL((h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN>),
+                           dim3((unsigned)nwg), dim3(FAST_WM * FAST_WN * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
                            tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
