@@ -100,16 +100,22 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
     p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
                 ldc % 8 == 0;
-    int cfg = h16_fast_eligible(p) ? (int)H16_FAST_256x256 : h16_pick_config(p.M, p.N, p.K);
     // Tuning / testing override: LIBGEMM_H16_CONFIG=<H16Config id> (the large-tile
-    // path only where it is eligible).
+    // paths only where they are eligible).
     if (const char *e = std::getenv("LIBGEMM_H16_CONFIG")) {
         const int forced = std::atoi(e);
         if (forced >= 0 && forced < H16_NUM_CONFIGS &&
-            (forced != H16_FAST_256x256 || h16_fast_eligible(p)))
-            cfg = forced;
+            (forced != H16_FAST_256x256 || h16_fast_eligible(p)) &&
+            (forced != H16_GEN_256x256 || h16_general_eligible(p)))
+            return to_status(h16_launch(is_bf16, forced, p));
     }
-    return to_status(h16_launch(is_bf16, cfg, p));
+    if (h16_fast_eligible(p)) return to_status(h16_launch(is_bf16, H16_FAST_256x256, p));
+    // Large problems with ragged edges or unaligned rows: the guarded large-tile
+    // kernel.
+    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (p.M >= 256 && p.N >= 256 && big_tiles >= 128 && h16_general_eligible(p))
+        return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
+    return to_status(h16_launch(is_bf16, h16_pick_config(p.M, p.N, p.K), p));
 }
 
 }  // namespace

@@ -269,6 +269,7 @@ int h16_pick_config(int M, int N, int K)
 hipError_t h16_launch(bool is_bf16, int config, const Problem &p)
 {
     if (config == H16_FAST_256x256) return h16_fast_launch(is_bf16, p);
+    if (config == H16_GEN_256x256) return h16_general_launch(is_bf16, p);
     return is_bf16 ? launch_typed<true>(config, p) : launch_typed<false>(config, p);
 }
 

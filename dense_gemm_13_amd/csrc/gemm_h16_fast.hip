@@ -108,11 +108,24 @@ __device__ __forceinline__ uint16_t *ring_array(int idx)
     }
 }
 
-template <bool IS_BF16, int BK, int STAGES, int WM, int WN>
+// GEN = false: whole 256 x 256 tiles, K a multiple of BK * STAGES, 16-byte
+// aligned operands.  GEN = true: any M, N >= 8, K > BK and any leading
+// dimensions (the hardware runs in unaligned-access mode, so 16-byte loads and
+// stores at 2-byte-aligned addresses are legal):
+//   * the last K block (possibly partial) is done first, loaded through
+//     registers with zero fill, so every LDS-direct block is a full one that
+//     never touches B's last row;
+//   * A rows past M are clamped to row M-1 and B column chunks starting past N
+//     to the chunk at N-8 (their products only reach C entries that are not
+//     stored); a chunk straddling N reads a few elements past N inside a row
+//     that is not B's last, i.e. inside the operand;
+//   * steps are guarded when the number of K steps is not a multiple of the
+//     ring depth, and C stores are masked to the M x N window.
+template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
-                uint16_t *__restrict__ C, int K, int64_t lda, int64_t ldb, int64_t ldc,
-                int tiles_m, int tiles_n, int group_m)
+                uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
+                int64_t ldc, int tiles_m, int tiles_n, int group_m)
 {
     constexpr int FNW = WM * WN;
     constexpr int FWTM = FBM / WM, FWTN = FBN / WN;      // wave sub-tile
@@ -146,22 +159,28 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
     for (int j = 0; j < A_BLK; ++j) {
         const int row = ROWS_PER_KB * (wave * A_BLK + j) + lane / CPR;
-        a_off[j] = (uint32_t)(row * lda + 8 * ((lane % CPR) ^ swz_a<BK>(row))) * 2u;
+        const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
+        a_off[j] = (uint32_t)(lrow * lda + 8 * ((lane % CPR) ^ swz_a<BK>(row))) * 2u;
     }
     // B block b (2 rows of 512 bytes): lane -> row 2b + lane/32, slot lane%32.
+    // For GEN the column (including n0) is part of the per-lane offset.
     uint32_t b_off_g[B_BLK];
 #pragma unroll
     for (int j = 0; j < B_BLK; ++j) {
         const int row = 2 * (wave * B_BLK + j) + (lane >> 5);
-        b_off_g[j] = (uint32_t)(row * ldb + 8 * ((lane & 31) ^ swz_b(row))) * 2u;
+        int col = 8 * ((lane & 31) ^ swz_b(row));
+        if (GEN) col = n0 + col >= N ? N - 8 : n0 + col;
+        b_off_g[j] = (uint32_t)(row * ldb + col) * 2u;
     }
     const char *a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
-    const char *b_base = reinterpret_cast<const char *>(B + n0);
+    const char *b_base = reinterpret_cast<const char *>(GEN ? B : B + n0);
     const int64_t a_step = (int64_t)BK * 2, b_step = (int64_t)BK * ldb * 2;
 
-    auto issue = [&](uint16_t *as, uint16_t *bs, int kt) {
-        const char *ab = a_base + kt * a_step;
-        const char *bb = b_base + kt * b_step;
+    // Step s loads K block s (GEN: block s-1; step 0 is the last block, below).
+    auto issue = [&](uint16_t *as, uint16_t *bs, int s) {
+        const int kb = GEN ? s - 1 : s;
+        const char *ab = a_base + kb * a_step;
+        const char *bb = b_base + kb * b_step;
 #pragma unroll
         for (int j = 0; j < A_BLK; ++j) dma16(ab + a_off[j], as + (wave * A_BLK + j) * 512);
 #pragma unroll
@@ -279,10 +298,51 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // steps re-fetch the final K tile into stages nobody reads any more, and the
     // last step's look-ahead reads a stage whose contents are not used
     // (identical code in every step).  All loads are drained before the epilogue.
-    const int ktiles = K / BK;                           // a multiple of STAGES
+    // GEN: step 0 is the last K block [BK*(ktiles-1), K), through registers
+    // with zero fill, in the same swizzled layout the LDS-direct loads produce.
+    const int ktiles = (K + BK - 1) / BK;   // !GEN: K / BK, a multiple of STAGES
+    if constexpr (GEN) {
+        const int k0 = BK * (ktiles - 1);
+        uint16_t *as = lds_stage<0, A_STAGE>, *bs = lds_stage<STAGES, B_STAGE>;
+        constexpr int NT = FNW * 64;
+#pragma unroll
+        for (int q = tid; q < A_STAGE / 8; q += NT) {
+            const int r = q / CPR, c = q % CPR;
+            const int gm = m0 + r, gk = k0 + 8 * c;
+            uint32_t w[4] = {0, 0, 0, 0};
+            if (gm < M) {
+                const uint16_t *src = A + (int64_t)gm * lda + gk;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (gk + e < K) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            }
+            *reinterpret_cast<u32x4 *>(as + r * BK + ((c ^ swz_a<BK>(r)) << 3)) =
+                u32x4{w[0], w[1], w[2], w[3]};
+        }
+#pragma unroll
+        for (int q = tid; q < B_STAGE / 8; q += NT) {
+            const int r = q / (FBN / 8), c = q % (FBN / 8);
+            const int gk = k0 + r, gn = n0 + 8 * c;
+            uint32_t w[4] = {0, 0, 0, 0};
+            if (gk < K) {
+                const uint16_t *src = B + (int64_t)gk * ldb + gn;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            }
+            *reinterpret_cast<u32x4 *>(bs + r * FBN + ((c ^ swz_b(r)) << 3)) =
+                u32x4{w[0], w[1], w[2], w[3]};
+        }
+    }
+    // (GEN: steps past the last one re-load the last full block, K > BK.)
     unroll<STAGES - 1>([&](auto S) {
-        issue(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>, S);
+        if (!GEN || S > 0)
+            issue(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>,
+                  !GEN || S < ktiles ? (int)S : ktiles - 1);
     });
+    // GEN: stage 0 came through registers (its global loads were waited for
+    // before the LDS writes); the writes must land before the barrier.
+    if constexpr (GEN) __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0)
     wait_vmcnt<(STAGES - 2) * NBLK>();
     barrier_no_fence();
     load_frags(cur, lds_stage<0, A_STAGE>, lds_stage<STAGES, B_STAGE>, 0);
@@ -291,10 +351,11 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             constexpr int N1 = (S + 1) % STAGES;           // next stage (read ahead)
             constexpr int NS = (S + STAGES - 1) % STAGES;  // stage to refill
             const int next = kt + S + STAGES - 1;
-            step(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>,
-                 lds_stage<N1, A_STAGE>, lds_stage<STAGES + N1, B_STAGE>,
-                 lds_stage<NS, A_STAGE>, lds_stage<STAGES + NS, B_STAGE>,
-                 next < ktiles ? next : ktiles - 1);
+            if (!GEN || kt + S < ktiles)
+                step(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>,
+                     lds_stage<N1, A_STAGE>, lds_stage<STAGES + N1, B_STAGE>,
+                     lds_stage<NS, A_STAGE>, lds_stage<STAGES + NS, B_STAGE>,
+                     next < ktiles ? next : ktiles - 1);
         });
     }
     wait_vmcnt<0>();
@@ -340,39 +401,76 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
         u32x4 v = *reinterpret_cast<const u32x4 *>(buf + ((cl ^ (row % CPRC)) << 3));
         if ((row / CPRC) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        *reinterpret_cast<u32x4 *>(cbase + (int64_t)row * ldc + 8 * cl) = v;
+        uint16_t *dst = cbase + (int64_t)row * ldc + 8 * cl;
+        if (!GEN) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+            const int gm = m0 + wm0 + row, gn = n0 + wn0 + 8 * cl;
+            if (gm < M) {
+                if (gn + 8 <= N) {
+                    *reinterpret_cast<u32x4 *>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (gn + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
     }
 }
 
 }  // namespace
 
-// Whole tiles and a whole number of stage rings only; the per-lane 32-bit byte
-// offsets (up to 256 rows of A or BK rows of B past the tile's base) must fit.
+// Whole tiles, a whole number of stage rings and 16-byte alignment: the
+// unguarded instantiation.  The per-lane 32-bit byte offsets (up to 256 rows of
+// A or BK rows of B past a base) must fit.
 bool h16_fast_eligible(const Problem &p)
 {
     return p.aligned && p.M % FBM == 0 && p.N % FBN == 0 &&
-           p.K % (FAST_BK * FAST_STAGES) == 0 && p.lda < (1 << 22) && p.ldb < (1 << 24);
+           p.K % (FAST_BK * FAST_STAGES) == 0 && p.lda < (1 << 22) && p.ldb < (1 << 22);
 }
 
-hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
+// The guarded instantiation: any leading dimensions, N >= 8, two K steps at
+// least, and offsets that fit in 32 bits (A rows are addressed from the tile's
+// first row, B from its first column of the current K block).
+bool h16_general_eligible(const Problem &p)
 {
-    if (!h16_fast_eligible(p)) return hipErrorInvalidValue;
-    const int tiles_m = p.M / FBM, tiles_n = p.N / FBN;
+    return p.M >= 1 && p.N >= 8 && p.K > FAST_BK && p.lda < (1 << 22) && p.ldb < (1 << 22) &&
+           (int64_t)FAST_BK * p.ldb + p.N < (int64_t)1 << 30;
+}
+
+template <bool GEN>
+static hipError_t fast_launch(bool is_bf16, const Problem &p)
+{
+    const int tiles_m = (p.M + FBM - 1) / FBM, tiles_n = (p.N + FBN - 1) / FBN;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
+    const dim3 grid((unsigned)nwg), block(FAST_WM * FAST_WN * 64);
     if (is_bf16)
-        hipLaunchKernelGGL((h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN>),
-                           dim3((unsigned)nwg), dim3(FAST_WM * FAST_WN * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
+        hipLaunchKernelGGL((h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN>),
+                           grid, block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc,
                            tiles_m, tiles_n, group_m);
     else
-        hipLaunchKernelGGL((h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN>),
-                           dim3((unsigned)nwg), dim3(FAST_WM * FAST_WN * 64), 0, p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc,
+        hipLaunchKernelGGL((h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN>),
+                           grid, block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc,
                            tiles_m, tiles_n, group_m);
     return hipGetLastError();
+}
+
+hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_fast_eligible(p)) return hipErrorInvalidValue;
+    return fast_launch<false>(is_bf16, p);
+}
+
+hipError_t h16_general_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_general_eligible(p)) return hipErrorInvalidValue;
+    return fast_launch<true>(is_bf16, p);
 }
 
 }  // namespace gemm

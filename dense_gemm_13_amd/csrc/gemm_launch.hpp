@@ -26,13 +26,16 @@ enum H16Config {
     H16_64x64_W4 = 2,     // 64x64 tile, 4 waves (2 x 2), wave tile 32x32
     H16_32x64_W2 = 3,     // 32x64 tile, 2 waves (1 x 2), wave tile 32x32
     H16_FAST_256x256 = 4, // whole 256x256 tiles, LDS-direct loads, 4 waves of 128x128
-    H16_NUM_CONFIGS = 5
+    H16_GEN_256x256 = 5,  // same kernel, guarded: ragged M/N/K, any leading dimensions
+    H16_NUM_CONFIGS = 6
 };
 
 int h16_pick_config(int M, int N, int K);
 hipError_t h16_launch(bool is_bf16, int config, const Problem &p);
 bool h16_fast_eligible(const Problem &p);
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p);
+bool h16_general_eligible(const Problem &p);
+hipError_t h16_general_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p);
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
 // Set the M x N window of C (element size esize bytes, leading dimension ldc) to zero.

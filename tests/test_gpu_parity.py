@@ -22,8 +22,9 @@ from gpu_helpers import TOL, OUT_DTYPE, compare, reference, run_gemm, say, to_de
 
 pytestmark = pytest.mark.gpu
 
-H16_CONFIGS = (0, 1, 2, 3, 4)
+H16_CONFIGS = (0, 1, 2, 3, 4, 5)
 FAST = 4          # whole 256x256 tiles, K % 128 == 0, aligned
+GENERAL = 5       # the same kernel, guarded: ragged M/N/K, any leading dimensions
 
 
 @pytest.fixture(autouse=True)
@@ -182,6 +183,27 @@ def test_fast_path_whole_tiles(dtype, shape):
     ops = gi.operands(dtype, M, N, K, 40)
     _, got = run_gemm(dtype, ops, M, N, K)
     ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "fast")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape,lds", [
+    ((256, 256, 33), None),            # two K steps, the last one partial
+    ((256, 256, 64), None),            # two full K steps
+    ((300, 264, 200), None),           # 7 K steps: not a multiple of the ring depth
+    ((1, 8, 65), None),                # one row, eight columns
+    ((257, 9, 96), (101, 11, 13)),     # unaligned leading dimensions
+    ((520, 777, 1000), (1003, 779, 781)),
+    ((4097, 4095, 4100), None),        # the ragged workload on this path alone (272 tiles)
+])
+def test_general_path_edges(dtype, shape, lds):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(GENERAL)
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[general] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 41)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "general")
     assert ok, msg
 
 
