@@ -14,6 +14,8 @@
 // LDS: A as rows of k (64 bytes per row, 16-byte chunks XOR-swizzled); B is
 // transposed on the way in (8 k-rows x 4 columns per thread, bytes shuffled in
 // registers) so every lane can read 32 consecutive k of one column.
+#include <cstdlib>
+
 #include "gemm_device.hpp"
 #include "gemm_launch.hpp"
 
@@ -263,6 +265,8 @@ hipError_t launch_cfg(const Problem &p, const float *sa, const float *sb)
 
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b)
 {
+    const char *e = std::getenv("LIBGEMM_FP8_SMALL");   // testing: force the general kernel
+    if (fp8_fast_eligible(p) && !(e && e[0] == '1')) return fp8_fast_launch(p, scale_a, scale_b);
     const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
     if (big >= 128) return launch_cfg<128, 128, 2, 2>(p, scale_a, scale_b);
     return launch_cfg<64, 64, 2, 1>(p, scale_a, scale_b);

@@ -1,0 +1,270 @@
+// FP8 (OCP E4M3) block-scaled GEMM, large-tile path for gfx950: whole 256 x 256
+// tiles, K a multiple of 256, 16-byte aligned A/B/C rows.
+//
+//   C[i][j] = bf16( sum_kb  sa(i/64, kb) * sb(kb, j/64) * sum_{k in block kb} qa(i,k) qb(k,j) )
+//
+// "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3: E4M3
+// operands with one scale per 64 x 64 sub-block; section 5.2 (third pitfall):
+// 32-bit scales.  Same movement of operands as the half-precision large-tile
+// path (gemm_h16_fast.hip): global_load_lds_dwordx4 into a 4-stage LDS ring,
+// one array per stage, the XOR chunk swizzle applied on the global side.
+//
+// One K step is one 64-wide scale block.  Every 32 x 32 output tile of a wave
+// gets one v_mfma_scale_f32_32x32x64_f8f6f4 per step (hardware block scales at
+// 2^0) into a zeroed partial, which is promoted into the fp32 accumulator with
+// one FMA per element by sa * sb of that block.  The promotion runs on the
+// vector ALU, so the accumulators live in VGPRs: 8 waves (two per SIMD), each
+// with a 128 x 64 sub-tile (128 accumulator VGPRs); one wave's MFMAs overlap the
+// other's promotion.
+//
+// B stays in LDS as rows of k (n contiguous, 256-byte rows) and the MFMA operand
+// "32 consecutive k of one column" comes from four ds_read_b64_tr_b8: within a
+// 16-lane group, lanes 2r and 2r+1 address the two 8-byte halves of 16
+// consecutive columns of row r (8 rows), and lane j receives byte j of each of
+// the 8 rows.
+#include <utility>
+
+#include "gemm_device.hpp"
+#include "gemm_launch.hpp"
+
+namespace gemm {
+
+namespace {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void8_t;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+
+constexpr int QBM = 256, QBN = 256, QBK = 64, QSTAGES = 4;
+constexpr int QWM = 2, QWN = 4, QNW = QWM * QWN;       // 8 waves
+constexpr int QWTM = QBM / QWM, QWTN = QBN / QWN;       // 128 x 64 per wave
+constexpr int QFM = QWTM / 32, QFN = QWTN / 32;         // 4 x 2 MFMA tiles
+constexpr int QA_STAGE = QBM * QBK;                      // bytes per stage (16 KiB)
+constexpr int QB_STAGE = QBK * QBN;
+constexpr int QA_BLK = QA_STAGE / 1024 / QNW;            // 1 KiB loads per wave per stage
+constexpr int QB_BLK = QB_STAGE / 1024 / QNW;
+constexpr int QNBLK = QA_BLK + QB_BLK;
+
+template <int TAG>
+__shared__ __attribute__((aligned(1024))) uint8_t q_stage[16384];
+
+__device__ __forceinline__ uint8_t *q_ring(int idx)
+{
+    switch (idx) {
+    case 0: return q_stage<0>;
+    case 1: return q_stage<1>;
+    case 2: return q_stage<2>;
+    case 3: return q_stage<3>;
+    case 4: return q_stage<4>;
+    case 5: return q_stage<5>;
+    case 6: return q_stage<6>;
+    default: return q_stage<7>;
+    }
+}
+
+// A rows: 64 bytes (4 chunks), same pattern as the 64-byte half-precision rows.
+__host__ __device__ __forceinline__ int qswz_a(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// B rows: 256 bytes (16 chunks).  The 8 rows of one transposing read land in 8
+// distinct even chunks (and the neighbouring 16-column group in the odd ones).
+__host__ __device__ __forceinline__ int qswz_b(int k) { return (k & 7) << 1; }
+
+template <int N>
+__device__ __forceinline__ void q_wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void q_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <typename F, int... I>
+__device__ __forceinline__ void q_unroll_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void q_unroll(F &&f)
+{
+    q_unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__global__ void __launch_bounds__(QNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
+                uint16_t *__restrict__ C, int K, int64_t lda, int64_t ldb, int64_t ldc,
+                const float *__restrict__ scale_a, const float *__restrict__ scale_b,
+                int kblocks, int nblocks, int tiles_m, int tiles_n, int group_m)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / QWN) * QWTM;
+    const int wn0 = (wave % QWN) * QWTN;
+    const int l32 = lane & 31, half = lane >> 5;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * QBM, n0 = tn * QBN;
+
+    // ---- this wave's 1 KiB loads.  A block b: 16 rows of 64 bytes, lane ->
+    // row 16b + lane/4, slot lane%4 holding logical chunk slot ^ qswz_a(row).
+    // B block b: 4 rows of 256 bytes, lane -> row 4b + lane/16, slot lane%16.
+    uint32_t a_off[QA_BLK], b_off[QB_BLK];
+#pragma unroll
+    for (int j = 0; j < QA_BLK; ++j) {
+        const int row = 16 * (wave * QA_BLK + j) + (lane >> 2);
+        a_off[j] = (uint32_t)(row * lda + 16 * ((lane & 3) ^ qswz_a(row)));
+    }
+#pragma unroll
+    for (int j = 0; j < QB_BLK; ++j) {
+        const int row = 4 * (wave * QB_BLK + j) + (lane >> 4);
+        b_off[j] = (uint32_t)(row * ldb + 16 * ((lane & 15) ^ qswz_b(row)));
+    }
+    const uint8_t *a_base = A + (int64_t)m0 * lda;
+    const uint8_t *b_base = B + n0;
+    const int64_t b_step = (int64_t)QBK * ldb;
+    auto issue = [&](uint8_t *as, uint8_t *bs, int kt) {
+        const uint8_t *ab = a_base + kt * QBK;
+        const uint8_t *bb = b_base + kt * b_step;
+#pragma unroll
+        for (int j = 0; j < QA_BLK; ++j)
+            __builtin_amdgcn_global_load_lds(ab + a_off[j], (lds_void8_t *)(as + (wave * QA_BLK + j) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < QB_BLK; ++j)
+            __builtin_amdgcn_global_load_lds(bb + b_off[j], (lds_void8_t *)(bs + (wave * QB_BLK + j) * 1024), 16, 0, 0);
+    };
+
+    // ---- fragment addressing (bytes, relative to a stage)
+    // A tile i: lane reads row wm0 + 32i + l32, k bytes 32*half .. +31 (chunks 2h, 2h+1).
+    int a_off0[QFM], a_off1[QFM];
+#pragma unroll
+    for (int i = 0; i < QFM; ++i) {
+        const int row = wm0 + 32 * i + l32;
+        a_off0[i] = row * QBK + (((2 * half) ^ qswz_a(row)) << 4);
+        a_off1[i] = row * QBK + (((2 * half + 1) ^ qswz_a(row)) << 4);
+    }
+    // B tile j, read q: 16-lane group g, lane w: row 32*(g/2) + 8q + w/2, columns
+    // wn0 + 32j + 16*(g%2) + 8*(w%2) .. +7.  (k rows with the same k % 8 share a swizzle.)
+    const int g = lane >> 4, w16 = lane & 15, r8 = w16 >> 1;
+    int b_off_r[QFN];
+#pragma unroll
+    for (int j = 0; j < QFN; ++j) {
+        const int n = wn0 + 32 * j + 16 * (g & 1) + 8 * (w16 & 1);
+        b_off_r[j] = (32 * (g >> 1) + r8) * QBN + (((n >> 4) ^ qswz_b(r8)) << 4) + (n & 15);
+    }
+
+    // Scale rows / column of this wave: A tiles 0,1 and 2,3 are in scale rows mb0 and mb0+1.
+    const int mb0 = (m0 + wm0) / 64, nb = (n0 + wn0) / 64;
+    const float *sa0 = scale_a + (int64_t)mb0 * kblocks, *sa1 = sa0 + kblocks;
+    const float *sbc = scale_b + nb;
+
+    f32x16 acc[QFM][QFN];
+#pragma unroll
+    for (int i = 0; i < QFM; ++i)
+#pragma unroll
+        for (int j = 0; j < QFN; ++j) acc[i][j] = f32x16{};
+
+    auto step = [&](const uint8_t *as, const uint8_t *bs, uint8_t *nas, uint8_t *nbs, int kt,
+                    int next_kt) {
+        q_wait_vmcnt<(QSTAGES - 2) * QNBLK>();
+        q_barrier();
+        issue(nas, nbs, next_kt);
+        const float sb = sbc[(int64_t)kt * nblocks];
+        const float s0 = sa0[kt] * sb, s1 = sa1[kt] * sb;
+        i32x8 af[QFM], bfr[QFN];
+#pragma unroll
+        for (int i = 0; i < QFM; ++i) {
+            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(as + a_off0[i]);
+            const u32x4 x1 = *reinterpret_cast<const u32x4 *>(as + a_off1[i]);
+            af[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < QFN; ++j) {
+            i32x2 r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (lds_i32x2_t *)(bs + b_off_r[j] + 8 * q * QBN));
+            bfr[j] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+        }
+#pragma unroll
+        for (int j = 0; j < QFN; ++j)
+#pragma unroll
+            for (int i = 0; i < QFM; ++i) {
+                // E4M3 for both operands (format 0); block scales 127 = 2^0
+                const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bfr[j], af[i], f32x16{}, 0, 0, 0, 127, 0, 127);
+                const float s = i < 2 ? s0 : s1;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], s, acc[i][j][e]);
+            }
+    };
+
+    const int ktiles = K / QBK;                          // a multiple of QSTAGES
+    q_unroll<QSTAGES - 1>([&](auto S) { issue(q_stage<S>, q_stage<QSTAGES + S>, S); });
+    for (int kt = 0; kt < ktiles; kt += QSTAGES) {
+        q_unroll<QSTAGES>([&](auto S) {
+            constexpr int NS = (S + QSTAGES - 1) % QSTAGES;
+            const int next = kt + S + QSTAGES - 1;
+            step(q_stage<S>, q_stage<QSTAGES + S>, q_stage<NS>, q_stage<QSTAGES + NS>, kt + S,
+                 next < ktiles ? next : ktiles - 1);
+        });
+    }
+    q_wait_vmcnt<0>();
+
+    // ---- epilogue through LDS: each wave's 128 x 64 bf16 sub-tile (16 KiB) goes
+    // to its own ring array (128-byte rows, chunks XORed with row % 8, the 8-byte
+    // half with bit 3 of the row), then out as whole 128-byte row segments.
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
+    q_barrier();
+    uint16_t *st = reinterpret_cast<uint16_t *>(q_ring(wave));
+#pragma unroll
+    for (int i = 0; i < QFM; ++i) {
+        const int row = 32 * i + l32;
+        uint16_t *buf = st + row * QWTN;
+        const int hsw = half ^ ((row >> 3) & 1);
+#pragma unroll
+        for (int j = 0; j < QFN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int chunk = (4 * j + q) ^ (row & 7);
+                *reinterpret_cast<u32x2 *>(buf + chunk * 8 + hsw * 4) =
+                    u32x2{pack2<true>(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                          pack2<true>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            }
+    }
+    uint16_t *const cbase = C + (int64_t)(m0 + wm0) * ldc + n0 + wn0;
+    const int cl = lane & 7;
+#pragma unroll
+    for (int it = 0; it < QWTM / 8; ++it) {
+        const int row = 8 * it + (lane >> 3);
+        u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * QWTN + ((cl ^ (row & 7)) << 3));
+        if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        *reinterpret_cast<u32x4 *>(cbase + (int64_t)row * ldc + 8 * cl) = v;
+    }
+}
+
+}  // namespace
+
+bool fp8_fast_eligible(const Problem &p)
+{
+    return p.M % QBM == 0 && p.N % QBN == 0 && p.K % (QBK * QSTAGES) == 0 &&
+           ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 &&
+           ((uintptr_t)p.C & 15) == 0 && p.lda % 16 == 0 && p.ldb % 16 == 0 && p.ldc % 8 == 0 &&
+           p.lda < (1 << 23) && p.ldb < (1 << 24);
+}
+
+hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b)
+{
+    if (!fp8_fast_eligible(p)) return hipErrorInvalidValue;
+    const int tiles_m = p.M / QBM, tiles_n = p.N / QBN;
+    const int64_t nwg = (int64_t)tiles_m * tiles_n;
+    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    const int group_m = tiles_m < 4 ? tiles_m : 4;
+    hipLaunchKernelGGL(fp8_fast_kernel, dim3((unsigned)nwg), dim3(QNW * 64), 0, p.stream,
+                       static_cast<const uint8_t *>(p.A), static_cast<const uint8_t *>(p.B),
+                       static_cast<uint16_t *>(p.C), p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b,
+                       p.K / 64, p.N / 64, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace gemm

@@ -38,6 +38,8 @@ bool h16_general_eligible(const Problem &p);
 hipError_t h16_general_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p);
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
+bool fp8_fast_eligible(const Problem &p);
+hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);
 // Set the M x N window of C (element size esize bytes, leading dimension ldc) to zero.
 hipError_t zero_launch(void *C, int M, int N, int64_t ldc, int esize, hipStream_t stream);
 

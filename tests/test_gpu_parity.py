@@ -159,6 +159,24 @@ def test_fp8_full_ragged(shape):
     _full_check("fp8", *shape, 5, "fp8_small")
 
 
+@pytest.mark.parametrize("shape", [(256, 256, 256), (768, 512, 1024), (512, 1280, 768)])
+def test_fp8_large_tile_path(shape):
+    """Whole 256x256 tiles and K % 256 == 0 take the large-tile fp8 kernel."""
+    _full_check("fp8", *shape, 6, "fp8_large")
+
+
+def test_fp8_large_tile_permutation_exact():
+    M = K = 512
+    say("[probe] fp8 large-tile A*P")
+    ops, perm = _perm_case("fp8", M, K, 9)
+    _, got = run_gemm("fp8", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "fp8")
+    gotv = oracle.decode(got, "bf16")
+    bad = np.argwhere(gotv != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 @pytest.mark.parametrize("dtype,config,aligned",
                          [(d, c, a) for d in ("bf16", "f16") for c in H16_CONFIGS
                           for a in (True, False)])
