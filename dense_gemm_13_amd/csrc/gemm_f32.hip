@@ -15,6 +15,8 @@
 // walk 32 consecutive rows), B as rows of n exactly as in memory (each lane
 // reads single floats of one row, 32 lanes cover 128 contiguous bytes).  Two
 // stages ping-pong so the next step's loads are in flight during the MFMAs.
+#include <cstdlib>
+
 #include "gemm_device.hpp"
 #include "gemm_launch.hpp"
 
@@ -212,6 +214,8 @@ hipError_t launch_cfg(const Problem &p)
 
 hipError_t f32_launch(const Problem &p)
 {
+    const char *e = std::getenv("LIBGEMM_F32_SMALL");   // testing: force the general kernel
+    if (f32_fast_eligible(p) && !(e && e[0] == '1')) return f32_fast_launch(p);
     const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
     if (big >= 128) return launch_cfg<128, 128, 2, 2>(p);
     return launch_cfg<64, 64, 2, 2>(p);

@@ -37,6 +37,8 @@ hipError_t h16_fast_launch(bool is_bf16, const Problem &p);
 bool h16_general_eligible(const Problem &p);
 hipError_t h16_general_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p);
+bool f32_fast_eligible(const Problem &p);
+hipError_t f32_fast_launch(const Problem &p);
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
 bool fp8_fast_eligible(const Problem &p);
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);

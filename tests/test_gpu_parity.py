@@ -165,6 +165,23 @@ def test_fp8_large_tile_path(shape):
     _full_check("fp8", *shape, 6, "fp8_large")
 
 
+@pytest.mark.parametrize("shape", [(128, 128, 64), (384, 256, 320), (1024, 640, 2048)])
+def test_f32_large_tile_path(shape):
+    """Whole 128x128 tiles and K % 64 == 0 take the large-tile fp32 kernel."""
+    _full_check("f32", *shape, 7, "f32_large")
+
+
+def test_f32_large_tile_permutation_exact():
+    M, K = 384, 512
+    say("[probe] f32 large-tile A*P")
+    ops, perm = _perm_case("f32", M, K, 11)
+    _, got = run_gemm("f32", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "f32")
+    bad = np.argwhere(oracle.decode(got, "f32") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 def test_fp8_large_tile_permutation_exact():
     M = K = 512
     say("[probe] fp8 large-tile A*P")
