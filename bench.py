@@ -51,10 +51,16 @@ def algorithmic_bytes(dtype: str, M: int, N: int, K: int) -> int:
     return b
 
 
-def kernel_source_digest() -> str:
+# Sources that define the headline kernel's machine code: the measured traffic
+# below stays valid while these are unchanged.
+HEADLINE_KERNEL_SOURCES = ("gemm_h16_fast.hip", "gemm_device.hpp")
+
+
+def kernel_source_digest(files=HEADLINE_KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_13_amd", "csrc", "*"))):
-        h.update(os.path.basename(p).encode())
+    for f in files:
+        p = os.path.join(ROOT, "dense_gemm_13_amd", "csrc", f)
+        h.update(f.encode())
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -79,8 +85,9 @@ def measured_traffic(name: str):
 
 
 class Workload:
-    def __init__(self, name, dtype, M, N, K, wid):
-        self.name, self.dtype, self.M, self.N, self.K, self.wid = name, dtype, M, N, K, wid
+    def __init__(self, key, name, dtype, M, N, K, wid):
+        self.key, self.name, self.dtype = key, name, dtype
+        self.M, self.N, self.K, self.wid = M, N, K, wid
 
     def setup(self):
         import numpy as np
@@ -118,48 +125,78 @@ class Workload:
             self.call = lambda: fn(a, b, c, M, N, K, K, N, N, s)
         torch.cuda.synchronize()
 
-    def run(self, steps: int, warmup: int) -> dict:
+    def cold(self, steps: int) -> float:
+        """Mean launch time with L2 and the Infinity Cache flushed before each
+        launch by a 512 MiB write (the operands of every workload fit in the
+        256 MiB Infinity Cache otherwise)."""
+        import torch
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=self.C.device)
+        evs = []
+        for _ in range(steps):
+            flush.fill_(1)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(self.stream)
+            self.call()
+            e.record(self.stream)
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        del flush
+        return sum(s.elapsed_time(e) for s, e in evs) / steps * 1e-3
+
+    def run(self, steps: int, warmup: int, cold_steps: int) -> dict:
+        """Timed region: `steps` back-to-back launches on one stream between two
+        HIP events; the mean launch time is the region over `steps`.  A second,
+        untimed-region pass with an event pair around every launch gives the
+        per-launch median."""
         import torch
         for _ in range(warmup):
             rc = self.call()
             if rc != 0:
                 raise RuntimeError(f"{self.name}: libgemm returned {rc}")
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.call()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        region = e0.elapsed_time(e1) * 1e-3
+        mean = region / steps
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(steps):
             starts[i].record(self.stream)
             self.call()
             ends[i].record(self.stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         per = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
-        region = starts[0].elapsed_time(ends[-1]) * 1e-3
-        mean = sum(per) / len(per)
         median = per[len(per) // 2]
         M, N, K, dt = self.M, self.N, self.K, self.dtype
+        cold = self.cold(cold_steps) if cold_steps > 0 else None
         return {
-            "workload": self.name, "dtype": dt, "M": M, "N": N, "K": K,
+            "workload": self.name, "key": self.key, "dtype": dt, "M": M, "N": N, "K": K,
             "region_s": region, "wall_s": wall,
             "mean_launch_us": mean * 1e6, "median_launch_us": median * 1e6,
-            "tflops": tflops(M, N, K, region / steps),
-            "kernel_tflops": tflops(M, N, K, mean),
+            "tflops": tflops(M, N, K, mean),
             "pct_peak": 100.0 * tflops(M, N, K, mean) / PEAK_TFLOPS[dt],
             "alg_gbs": algorithmic_bytes(dt, M, N, K) / mean / 1e9,
+            "cold_mean_launch_us": cold * 1e6 if cold else None,
+            "cold_tflops": tflops(M, N, K, cold) if cold else None,
         }
 
 
 WORKLOADS = [
-    Workload("bf16 GEMM M=N=K=4096", "bf16", 4096, 4096, 4096, 2),
-    Workload("fp16 GEMM M=N=K=4096", "f16", 4096, 4096, 4096, 2),
-    Workload("fp16 GEMM M=N=K=256", "f16", 256, 256, 256, 1),
-    Workload("bf16 GEMM 1000x1000x1000", "bf16", 1000, 1000, 1000, 3),
-    Workload("bf16 GEMM 4097x4095x4100", "bf16", 4097, 4095, 4100, 3),
-    Workload("bf16 GEMM 8192x64x4096", "bf16", 8192, 64, 4096, 3),
-    Workload("fp32 SGEMM M=N=K=4096", "f32", 4096, 4096, 4096, 4),
-    Workload("fp8 E4M3 64x64-block-scaled GEMM M=N=K=8192, bf16 C", "fp8", 8192, 8192, 8192, 5),
+    Workload("bf16_4096", "bf16 GEMM M=N=K=4096", "bf16", 4096, 4096, 4096, 2),
+    Workload("f16_4096", "fp16 GEMM M=N=K=4096", "f16", 4096, 4096, 4096, 2),
+    Workload("f16_256", "fp16 GEMM M=N=K=256", "f16", 256, 256, 256, 1),
+    Workload("bf16_1000", "bf16 GEMM 1000x1000x1000", "bf16", 1000, 1000, 1000, 3),
+    Workload("bf16_ragged", "bf16 GEMM 4097x4095x4100", "bf16", 4097, 4095, 4100, 3),
+    Workload("bf16_skinny", "bf16 GEMM 8192x64x4096", "bf16", 8192, 64, 4096, 3),
+    Workload("f32_4096", "fp32 SGEMM M=N=K=4096", "f32", 4096, 4096, 4096, 4),
+    Workload("fp8_8192", "fp8 E4M3 64x64-block-scaled GEMM M=N=K=8192, bf16 C", "fp8",
+             8192, 8192, 8192, 5),
 ]
 
 
@@ -184,7 +221,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workloads", choices=("headline", "all"), default="all")
+    ap.add_argument("--workloads", default="all",
+                    help="all | headline | comma-separated keys: "
+                         + ",".join(w.key for w in WORKLOADS))
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="launches timed after a 512 MiB cache-flushing write each (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy (torch.neg) of this many MiB, "
@@ -202,14 +243,23 @@ def main():
     torch.cuda.set_device(0)
 
     headline = WORKLOADS[0]
-    todo = WORKLOADS if args.workloads == "all" else [headline]
+    if args.workloads == "all":
+        todo = WORKLOADS
+    elif args.workloads == "headline":
+        todo = [headline]
+    else:
+        keys = args.workloads.split(",")
+        unknown = set(keys) - {w.key for w in WORKLOADS}
+        if unknown:
+            ap.error(f"unknown workloads: {sorted(unknown)}")
+        todo = [headline] + [w for w in WORKLOADS if w.key in keys and w is not headline]
     results = []
     for w in todo:
         print(f"[bench] {w.name}: setup", file=sys.stderr, flush=True)
         w.setup()
         steps = args.steps if w is headline else max(10, args.steps // 2)
-        r = w.run(steps, args.warmup)
-        print(f"[bench] {w.name}: {r['kernel_tflops']:.1f} TFLOP/s "
+        r = w.run(steps, args.warmup, args.cold_steps)
+        print(f"[bench] {w.name}: {r['tflops']:.1f} TFLOP/s "
               f"({r['pct_peak']:.1f}% peak), {r['mean_launch_us']:.1f} us/launch",
               file=sys.stderr, flush=True)
         results.append(r)
