@@ -28,21 +28,26 @@ __global__ void zero_window_kernel(T *__restrict__ C, int M, int N, int64_t ldc)
 }
 
 constexpr int MAX_DEVICES = 64;
-std::atomic<int> g_device_ok[MAX_DEVICES];   // 0 = unknown, 1 = gfx950, -1 = other
+// Per device: 0 = not looked at yet, -1 = not a gfx950, else its compute-unit
+// count (the number of workgroups of the large-tile kernels one round runs).
+std::atomic<int> g_device_cus[MAX_DEVICES];
 
-int check_device()
+int check_device(int *cus = nullptr)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_DEVICE;
     if (dev >= MAX_DEVICES) return GEMM_ERR_DEVICE;
-    int state = g_device_ok[dev].load(std::memory_order_relaxed);
+    int state = g_device_cus[dev].load(std::memory_order_relaxed);
     if (state == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_DEVICE;
-        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-        g_device_ok[dev].store(state, std::memory_order_relaxed);
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.multiProcessorCount > 0
+                    ? prop.multiProcessorCount
+                    : -1;
+        g_device_cus[dev].store(state, std::memory_order_relaxed);
     }
-    return state == 1 ? GEMM_OK : GEMM_ERR_DEVICE;
+    if (cus) *cus = state;
+    return state > 0 ? GEMM_OK : GEMM_ERR_DEVICE;
 }
 
 bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes)
@@ -95,7 +100,8 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     bool work;
     int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 2, 2, &work);
     if (st != GEMM_OK || !work) return st;
-    if ((st = check_device()) != GEMM_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != GEMM_OK) return st;
     if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 2, stream));
     Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
     p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
@@ -106,15 +112,42 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
         const int forced = std::atoi(e);
         if (forced >= 0 && forced < H16_NUM_CONFIGS &&
             (forced != H16_FAST_256x256 || h16_fast_eligible(p)) &&
-            (forced != H16_GEN_256x256 || h16_general_eligible(p)))
+            (forced != H16_GEN_256x256 || h16_general_eligible(p)) &&
+            (forced != H16_NARROW_32x64 || h16_narrow_eligible(p)) &&
+            (forced != H16_NARROW_GEN || h16_narrow_general_eligible(p)))
             return to_status(h16_launch(is_bf16, forced, p));
     }
     if (h16_fast_eligible(p)) return to_status(h16_launch(is_bf16, H16_FAST_256x256, p));
+    // Tall, narrow products: 32 x 64 tiles with K split over the waves.
+    const int64_t narrow_tiles = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64);
+    if (p.N <= 128 && narrow_tiles >= 128) {
+        if (h16_narrow_eligible(p)) return to_status(h16_launch(is_bf16, H16_NARROW_32x64, p));
+        if (h16_narrow_general_eligible(p))
+            return to_status(h16_launch(is_bf16, H16_NARROW_GEN, p));
+    }
     // Large problems with ragged edges or unaligned rows: the guarded large-tile
-    // kernel.
-    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (p.M >= 256 && p.N >= 256 && big_tiles >= 128 && h16_general_eligible(p))
+    // kernel.  A few rows left below the whole 256-row tiles that would cost an
+    // extra, mostly idle round of workgroups go to the narrow kernel instead.
+    const int64_t tiles_n = (p.N + 255) / 256;
+    const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * tiles_n;
+    if (p.M >= 256 && p.N >= 256 && big_tiles >= 128 && h16_general_eligible(p)) {
+        const int tail = p.M % 256;
+        const int64_t main_tiles = (int64_t)(p.M / 256) * tiles_n;
+        if (tail > 0 && tail <= 64 && (main_tiles + cus - 1) / cus < (big_tiles + cus - 1) / cus) {
+            Problem top = p, bottom = p;
+            top.M = p.M - tail;
+            bottom.M = tail;
+            bottom.A = static_cast<const uint16_t *>(p.A) + (int64_t)top.M * p.lda;
+            bottom.C = static_cast<uint16_t *>(p.C) + (int64_t)top.M * p.ldc;
+            if (h16_narrow_general_eligible(bottom)) {
+                st = to_status(h16_launch(
+                    is_bf16, h16_fast_eligible(top) ? H16_FAST_256x256 : H16_GEN_256x256, top));
+                if (st != GEMM_OK) return st;
+                return to_status(h16_launch(is_bf16, H16_NARROW_GEN, bottom));
+            }
+        }
         return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
+    }
     return to_status(h16_launch(is_bf16, h16_pick_config(p.M, p.N, p.K), p));
 }
 

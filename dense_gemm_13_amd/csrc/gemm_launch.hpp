@@ -27,7 +27,9 @@ enum H16Config {
     H16_32x64_W2 = 3,     // 32x64 tile, 2 waves (1 x 2), wave tile 32x32
     H16_FAST_256x256 = 4, // whole 256x256 tiles, LDS-direct loads, 4 waves of 128x128
     H16_GEN_256x256 = 5,  // same kernel, guarded: ragged M/N/K, any leading dimensions
-    H16_NUM_CONFIGS = 6
+    H16_NARROW_32x64 = 6, // whole 32x64 tiles, 4 waves splitting K (tall, narrow products)
+    H16_NARROW_GEN = 7,   // same kernel, guarded: any M, N >= 8, K, leading dimensions
+    H16_NUM_CONFIGS = 8
 };
 
 int h16_pick_config(int M, int N, int K);
@@ -36,6 +38,10 @@ bool h16_fast_eligible(const Problem &p);
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p);
 bool h16_general_eligible(const Problem &p);
 hipError_t h16_general_launch(bool is_bf16, const Problem &p);
+bool h16_narrow_eligible(const Problem &p);
+hipError_t h16_narrow_launch(bool is_bf16, const Problem &p);
+bool h16_narrow_general_eligible(const Problem &p);
+hipError_t h16_narrow_general_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p);
 bool f32_fast_eligible(const Problem &p);
 hipError_t f32_fast_launch(const Problem &p);

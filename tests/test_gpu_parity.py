@@ -22,9 +22,11 @@ from gpu_helpers import TOL, OUT_DTYPE, compare, reference, run_gemm, say, to_de
 
 pytestmark = pytest.mark.gpu
 
-H16_CONFIGS = (0, 1, 2, 3, 4, 5)
+H16_CONFIGS = (0, 1, 2, 3, 4, 5, 6, 7)
 FAST = 4          # whole 256x256 tiles, K % 128 == 0, aligned
 GENERAL = 5       # the same kernel, guarded: ragged M/N/K, any leading dimensions
+NARROW = 6        # whole 32x64 tiles, K % 64 == 0, K >= 256, aligned; waves split K
+NARROW_GEN = 7    # the same kernel, guarded: any M, N >= 8, K >= 1, any leading dimensions
 
 
 @pytest.fixture(autouse=True)
@@ -218,6 +220,61 @@ def test_fast_path_whole_tiles(dtype, shape):
     ops = gi.operands(dtype, M, N, K, 40)
     _, got = run_gemm(dtype, ops, M, N, K)
     ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "fast")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [
+    (32, 64, 256),        # one tile, one K block per wave
+    (96, 64, 320),        # 5 K blocks: wave 0 takes two, the others one
+    (64, 128, 448),       # 7 blocks: 2,2,2,1 per wave (last ring step skipped)
+    (160, 192, 832),      # 13 blocks: a second trip through the ring for wave 0 only
+    (2048, 64, 1088),     # 17 blocks, 64 row strips
+])
+def test_narrow_path(dtype, shape):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(NARROW)
+    M, N, K = shape
+    say(f"[narrow] {dtype} {M}x{N}x{K}")
+    ops = gi.operands(dtype, M, N, K, 42)
+    _, got = run_gemm(dtype, ops, M, N, K)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "narrow")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 8, 1), None),                     # one row, eight columns, one k
+    ((5, 200, 64), None),                  # one K block: the register-loaded block only
+    ((33, 65, 65), None),                  # two row tiles, two column tiles, partial K block
+    ((31, 64, 300), (303, 67, 71)),        # unaligned leading dimensions
+    ((64, 70, 129), None),                 # 3 K blocks: two waves without LDS-direct blocks
+    ((40, 100, 1000), (1001, 101, 103)),   # 16 blocks: 4 per wave incl. the partial one
+    ((1, 4095, 4100), (4100, 4095, 4095)),  # the tail row of the ragged workload
+])
+def test_narrow_general_path_edges(dtype, shape, lds):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(NARROW_GEN)
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[narrow-general] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 43)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "narrow-general")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("shape,lds", [
+    ((4160, 4096, 256), None),                 # 64-row tail below whole tiles (large-tile path)
+    ((4127, 4000, 300), (301, 4003, 4001)),    # 31-row tail below guarded tiles, unaligned
+])
+def test_row_tail_split(shape, lds):
+    """A few rows below a grid of 256-row tiles whose extra tile row would need
+    a second round of workgroups: those rows are computed by the narrow kernel."""
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[tail-split] bf16 {M}x{N}x{K} {kw}")
+    ops = gi.operands("bf16", M, N, K, 44)
+    _, got = run_gemm("bf16", ops, M, N, K, **kw)
+    ok, msg, _ = compare("bf16", got, reference("bf16", ops, M, N, K), "tail-split")
     assert ok, msg
 
 
