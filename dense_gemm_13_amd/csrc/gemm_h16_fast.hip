@@ -346,16 +346,26 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     wait_vmcnt<(STAGES - 2) * NBLK>();
     barrier_no_fence();
     load_frags(cur, lds_stage<0, A_STAGE>, lds_stage<STAGES, B_STAGE>, 0);
-    for (int kt = 0; kt < ktiles; kt += STAGES) {
-        unroll<STAGES>([&](auto S) {
-            constexpr int N1 = (S + 1) % STAGES;           // next stage (read ahead)
-            constexpr int NS = (S + STAGES - 1) % STAGES;  // stage to refill
-            const int next = kt + S + STAGES - 1;
-            if (!GEN || kt + S < ktiles)
-                step(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>,
-                     lds_stage<N1, A_STAGE>, lds_stage<STAGES + N1, B_STAGE>,
-                     lds_stage<NS, A_STAGE>, lds_stage<STAGES + NS, B_STAGE>,
-                     next < ktiles ? next : ktiles - 1);
+    // Whole turns of the ring without conditions: a step skipped at run time
+    // would let the compiler merge the steps' code, lose track of which stage
+    // array each LDS read addresses and wait for every outstanding load before
+    // it.  GEN: the remaining ktiles % STAGES steps follow, once.
+    auto ring_step = [&](auto S, int kt) {
+        constexpr int N1 = (S + 1) % STAGES;           // next stage (read ahead)
+        constexpr int NS = (S + STAGES - 1) % STAGES;  // stage to refill
+        const int next = kt + S + STAGES - 1;
+        step(lds_stage<S, A_STAGE>, lds_stage<STAGES + S, B_STAGE>,
+             lds_stage<N1, A_STAGE>, lds_stage<STAGES + N1, B_STAGE>,
+             lds_stage<NS, A_STAGE>, lds_stage<STAGES + NS, B_STAGE>,
+             next < ktiles ? next : ktiles - 1);
+    };
+    const int kwhole = GEN ? ktiles - ktiles % STAGES : ktiles;
+    for (int kt = 0; kt < kwhole; kt += STAGES)
+        unroll<STAGES>([&](auto S) { ring_step(S, kt); });
+    if constexpr (GEN) {
+        const int rem = ktiles - kwhole;
+        unroll<STAGES - 1>([&](auto S) {
+            if (S < rem) ring_step(S, kwhole);
         });
     }
     wait_vmcnt<0>();
