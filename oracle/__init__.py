@@ -13,7 +13,8 @@ module only marshals numpy arrays into it.  What it follows:
   same row-major indexing;
 * "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3 and
   section 5.2 (third pitfall): E4M3 operands with one 32-bit scale per 64x64
-  sub-block.
+  sub-block, and the quantiser that makes them (``quantize_fp8``: E4M3 or E5M2,
+  32x32 or 64x64 blocks, scale = block amax / largest FP8 value, RNE).
 
 ``gemm`` returns the exact sum (fp64, k ascending, never rounded to the
 output type).  ``within_tolerance`` is the element-wise acceptance test
@@ -35,6 +36,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 F16, BF16, F32, FP8 = 0, 1, 2, 3
 DTYPES = {"f16": F16, "bf16": BF16, "f32": F32, "fp8": FP8}
 SCALE_BLOCK = 64
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
 
 _lib = None
 
@@ -59,9 +62,15 @@ def bind(lib):
     lib.orc_gemm_entries.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      vp, vp, i64, dp]
     lib.orc_gemm_entries.restype = ctypes.c_int
-    for name in ("orc_decode_f16", "orc_decode_bf16", "orc_decode_e4m3", "orc_decode_f32"):
+    for name in ("orc_decode_f16", "orc_decode_bf16", "orc_decode_e4m3", "orc_decode_e5m2",
+                 "orc_decode_f32"):
         getattr(lib, name).argtypes = [vp, dp, i64]
         getattr(lib, name).restype = None
+    lib.orc_fp8_encode_array.argtypes = [vp, i64, ctypes.c_int, vp]
+    lib.orc_fp8_encode_array.restype = None
+    lib.orc_quantize_fp8.argtypes = [ctypes.c_int, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                     vp, i64, vp]
+    lib.orc_quantize_fp8.restype = ctypes.c_int
     return lib
 
 
@@ -79,22 +88,26 @@ def _raw(x: np.ndarray, dtype: str) -> np.ndarray:
             x = x.view(np.float32)
         else:
             raise TypeError(f"{dtype} operand must be {want}, got {x.dtype}")
-    if x.ndim != 2 or x.strides[1] != x.itemsize:
+    if x.ndim != 2 or (x.shape[1] > 1 and x.strides[1] != x.itemsize):
         raise ValueError("operand must be 2-D with unit column stride")
     return x
 
 
 def _ld(x: np.ndarray) -> int:
+    if x.shape[0] <= 1:
+        return max(x.shape[1], 1)      # numpy may give a lone row any stride
     return x.strides[0] // x.itemsize
 
 
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact fp64 values of raw fp16/bf16 (uint16), e4m3 (uint8) or fp32 bits."""
+    """Exact fp64 values of raw fp16/bf16 (uint16), e4m3 ("fp8" or "e4m3") /
+    e5m2 (uint8) or fp32 bits."""
     lib = _load()
     src = np.ascontiguousarray(bits)
     out = np.empty(src.shape, dtype=np.float64)
     fn = {"f16": lib.orc_decode_f16, "bf16": lib.orc_decode_bf16,
-          "fp8": lib.orc_decode_e4m3, "f32": lib.orc_decode_f32}[dtype]
+          "fp8": lib.orc_decode_e4m3, "e4m3": lib.orc_decode_e4m3,
+          "e5m2": lib.orc_decode_e5m2, "f32": lib.orc_decode_f32}[dtype]
     if dtype == "f32":
         src = src.view(np.uint32)
     fn(src.ctypes.data, out.ctypes.data, src.size)
@@ -168,3 +181,28 @@ def within_tolerance(gpu: np.ndarray, ref: np.ndarray, rtol: float, atol: float)
     worst = int(np.argmax(ratio))
     idx = np.unravel_index(worst, ratio.shape)
     return (not bad.any()), int(bad.sum()), float(ratio.flat[worst]), tuple(int(i) for i in idx)
+
+
+def fp8_encode(y: np.ndarray, fmt: str) -> np.ndarray:
+    """Nearest FP8 codes (ties to even) of finite float32 values within range."""
+    lib = _load()
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib.orc_fp8_encode_array(y.ctypes.data, y.size, FP8_FORMATS[fmt], out.ctypes.data)
+    return out
+
+
+def quantize_fp8(X: np.ndarray, dtype: str, block: int, fmt: str):
+    """Block-scaled FP8 quantisation of a 2-D fp32 (float32) or bf16 (uint16 bits)
+    matrix: returns (codes uint8 of X's shape, scales float32 of
+    (ceil(rows/block), ceil(cols/block)))."""
+    lib = _load()
+    X = _raw(X, dtype)
+    rows, cols = X.shape
+    Q = np.empty((rows, cols), dtype=np.uint8)
+    S = np.empty((-(-rows // block), -(-cols // block)), dtype=np.float32)
+    rc = lib.orc_quantize_fp8(DTYPES[dtype], X.ctypes.data, rows, cols, _ld(X), block,
+                              FP8_FORMATS[fmt], Q.ctypes.data, max(cols, 1), S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"orc_quantize_fp8 failed ({rc})")
+    return Q, S

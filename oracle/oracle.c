@@ -18,6 +18,11 @@
  *     (E4M3) operands, each 64x64 sub-block multiplied by its own scale factor;
  *     section 5.2 (third pitfall): the scales are 32-bit floats.
  *
+ *   - the same section 4.3 and section 5.2: the quantiser that produces such
+ *     operands (orc_quantize_fp8 below): one 32-bit scale per 32x32 or 64x64
+ *     block, the block's largest magnitude over the largest FP8 value, and each
+ *     element divided by its block's scale and stored as FP8 (E4M3 or E5M2).
+ *
  * Every input is decoded bit by bit to an exact double by the decoders below
  * (they do not use compiler half/bfloat/fp8 types).  The sum for each entry runs
  * over k = 0 .. K-1 in ascending order.  Build with -ffp-contract=off and no
@@ -74,6 +79,22 @@ double orc_e4m3_to_f64(uint8_t q)
     return s ? -v : v;
 }
 
+/* OCP FP8 E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa, IEEE-like: exponent
+ * 31 holds the infinities (mantissa 0) and NaNs; largest finite magnitude 57344;
+ * subnormals down to 2^-16. */
+double orc_e5m2_to_f64(uint8_t q)
+{
+    int s = (q >> 7) & 1, e = (q >> 2) & 0x1f, m = q & 3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);                 /* subnormal: m * 2^(1-15-2) */
+    else
+        v = ldexp((double)(4 | m), e - 17);        /* (4+m) * 2^(e-15-2) */
+    return s ? -v : v;
+}
+
 /* IEEE binary32 from its bit pattern, built from the fields as well. */
 double orc_f32_to_f64(uint32_t u)
 {
@@ -101,6 +122,11 @@ void orc_decode_e4m3(const uint8_t *in, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++) out[i] = orc_e4m3_to_f64(in[i]);
 }
+void orc_decode_e5m2(const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_e5m2_to_f64(in[i]);
+}
+
 void orc_decode_f32(const uint32_t *in, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; i++) out[i] = orc_f32_to_f64(in[i]);
@@ -238,5 +264,101 @@ int orc_gemm_entries(int dtype, const void *A, const void *B, const float *scale
                             operand_at(dtype, B, ldb, kk, j, scale_b, sb_cols);
         out[t] = acc;
     }
+    return 0;
+}
+
+/* -------------------------------------------------------- FP8 quantiser */
+
+/* "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3 (FP8
+ * operands with one scale per 32x32 or 64x64 sub-block) and section 5.2, third
+ * pitfall (32-bit scales).  Reading of the steps, all in fp32 arithmetic:
+ *   amax = largest |x| of the block (elements inside the matrix only),
+ *   s    = amax / F with F the largest finite FP8 value (448 for E4M3, 57344
+ *          for E5M2), one IEEE division; s = 1 when amax = 0,
+ *   y    = x / s, one IEEE division per element, clamped to [-F, F],
+ *   q    = the FP8 value nearest to y, ties to the even mantissa, sign kept
+ *          (also when y rounds to zero).
+ * Inputs must be finite. */
+#define ORC_FP8_E4M3 0
+#define ORC_FP8_E5M2 1
+
+/* Nearest FP8 code to a finite y with |y| <= F, ties to even. */
+uint8_t orc_fp8_encode(float y, int fmt)
+{
+    const int mbits = fmt == ORC_FP8_E4M3 ? 3 : 2;
+    const int bias = fmt == ORC_FP8_E4M3 ? 7 : 15;
+    const int emin = 1 - bias;                     /* exponent of the smallest normal */
+    const uint8_t sign = signbit(y) ? 0x80 : 0;
+    const double a = fabs((double)y);
+    int e = emin;                                  /* binade of a; the subnormals share emin's spacing */
+    if (a > 0) {
+        int ex;
+        frexp(a, &ex);                             /* a = f * 2^ex, f in [1/2, 1) */
+        if (ex - 1 > e) e = ex - 1;
+    }
+    const double quantum = ldexp(1.0, e - mbits);  /* spacing of the FP8 values there */
+    double n = rint(a / quantum);                  /* exact quotient; rint: nearest, ties to even */
+    if (n >= ldexp(1.0, mbits + 1)) {              /* rounded up to the next binade's first value */
+        e += 1;
+        n = ldexp(1.0, mbits);
+    }
+    int expfield, mant;
+    if (n < ldexp(1.0, mbits)) {                   /* subnormal (e == emin) */
+        expfield = 0;
+        mant = (int)n;
+    } else {
+        expfield = e + bias;
+        mant = (int)n - (1 << mbits);
+    }
+    return (uint8_t)(sign | (expfield << mbits) | mant);
+}
+
+void orc_fp8_encode_array(const float *y, int64_t n, int fmt, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_fp8_encode(y[i], fmt);
+}
+
+static float input_f32(int dtype, const void *X, int64_t ld, int64_t r, int64_t c)
+{
+    if (dtype == ORC_BF16) return (float)orc_bf16_to_f64(((const uint16_t *)X)[r * ld + c]);
+    uint32_t u;
+    memcpy(&u, (const uint32_t *)X + r * ld + c, 4);
+    return (float)orc_f32_to_f64(u);
+}
+
+/* X: rows x cols, row-major with leading dimension ldx, fp32 (ORC_F32) or bf16
+ * (ORC_BF16) bits.  Q: rows x cols FP8 codes, leading dimension ldq.  scales:
+ * ceil(rows/block) x ceil(cols/block) fp32, row-major and contiguous.
+ * Returns 0, or -1 for arguments it does not handle. */
+int orc_quantize_fp8(int dtype, const void *X, int64_t rows, int64_t cols, int64_t ldx,
+                     int block, int fmt, uint8_t *Q, int64_t ldq, float *scales)
+{
+    if ((dtype != ORC_F32 && dtype != ORC_BF16) || (block != 32 && block != 64) ||
+        (fmt != ORC_FP8_E4M3 && fmt != ORC_FP8_E5M2) || rows < 0 || cols < 0 ||
+        ldx < cols || ldq < cols)
+        return -1;
+    const float fmax = fmt == ORC_FP8_E4M3 ? 448.0f : 57344.0f;
+    const int64_t br = (rows + block - 1) / block, bc = (cols + block - 1) / block;
+    for (int64_t bi = 0; bi < br; bi++)
+        for (int64_t bj = 0; bj < bc; bj++) {
+            const int64_t r0 = bi * block, c0 = bj * block;
+            const int64_t r1 = r0 + block < rows ? r0 + block : rows;
+            const int64_t c1 = c0 + block < cols ? c0 + block : cols;
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; r++)
+                for (int64_t c = c0; c < c1; c++) {
+                    const float a = fabsf(input_f32(dtype, X, ldx, r, c));
+                    if (a > amax) amax = a;
+                }
+            const float s = amax > 0.0f ? amax / fmax : 1.0f;
+            scales[bi * bc + bj] = s;
+            for (int64_t r = r0; r < r1; r++)
+                for (int64_t c = c0; c < c1; c++) {
+                    float y = input_f32(dtype, X, ldx, r, c) / s;
+                    if (y > fmax) y = fmax;
+                    if (y < -fmax) y = -fmax;
+                    Q[r * ldq + c] = orc_fp8_encode(y, fmt);
+                }
+        }
     return 0;
 }

@@ -9,7 +9,10 @@ Independent sources used here:
 * library decoders: numpy float16, torch bfloat16 / float8_e4m3fn, numpy float32;
 * closed forms: A*I = A, I*B = B, P*B = row-permuted B, all-ones -> K,
   rank-1 (u 1^T)(1 z^T) = K u z^T, K = 1 outer product, K = 0 -> 0;
-* exact rational brute force (fractions.Fraction) on tiny inputs.
+* exact rational brute force (fractions.Fraction) on tiny inputs;
+* for the FP8 quantiser: torch's float8_e4m3fn / float8_e5m2 casts and decodings,
+  brute-force nearest-value search over every FP8 code, exact-midpoint quotients,
+  power-of-two block patterns and the independent input recipe in gemm_inputs.
 """
 from __future__ import annotations
 
@@ -265,8 +268,168 @@ def pin_tolerance_checker(orc) -> list:
     return fails
 
 
+# ------------------------------------------------------------- FP8 quantiser
+
+FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def torch_fp8_table(fmt: str):
+    """(codes, values) of every finite code, decoded by torch."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(FP8_TORCH[fmt]).to(torch.float64).numpy()
+    fin = np.isfinite(vals)
+    return codes[fin], vals[fin]
+
+
+def brute_nearest(y: np.ndarray, fmt: str) -> np.ndarray:
+    """Nearest finite FP8 code by exhaustive search, ties to the even code, the
+    sign of y kept for zero results."""
+    codes, vals = torch_fp8_table(fmt)
+    out = np.empty(y.shape, dtype=np.uint8)
+    for t, v in enumerate(np.asarray(y, dtype=np.float64).ravel()):
+        d = np.abs(vals - v)
+        best = d.min()
+        cand = codes[d == best]
+        cand = cand[[bool(np.signbit(vals[codes.tolist().index(c)]) == np.signbit(v)) or
+                     vals[codes.tolist().index(c)] != 0 for c in cand]]
+        even = [c for c in cand if c % 2 == 0]
+        out.flat[t] = (even or list(cand))[0]
+    return out
+
+
+def pin_fp8_encode(orc) -> list:
+    fails = []
+    rng = np.random.default_rng(11)
+    for fmt in ("e4m3", "e5m2"):
+        codes, vals = torch_fp8_table(fmt)
+        # every finite code decodes like torch and encodes back to itself
+        d = orc.decode(np.arange(256, dtype=np.uint8), fmt)
+        t = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(FP8_TORCH[fmt]).to(torch.float64).numpy()
+        if not np.all((d == t) | (np.isnan(d) & np.isnan(t))):
+            fails.append(f"{fmt}: decoder differs from torch")
+        if not np.array_equal(orc.fp8_encode(vals.astype(np.float32), fmt), codes):
+            fails.append(f"{fmt}: a finite value does not encode to its own code")
+        # midpoints between neighbouring values and their fp32 neighbours
+        pos = np.unique(vals[vals >= 0])
+        mids = (pos[:-1] + pos[1:]) / 2
+        y = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                            np.nextafter(mids.astype(np.float32), np.float32(np.inf)).astype(np.float64)])
+        y = np.concatenate([y, -y, [pos[1] / 4, -pos[1] / 4, -0.0]]).astype(np.float32)
+        want = brute_nearest(y, fmt)
+        got = orc.fp8_encode(y, fmt)
+        bad = np.nonzero(got != want)[0]
+        if bad.size:
+            fails.append(f"{fmt}: midpoint rounding of {y[bad[0]]!r} gave {got[bad[0]]:#x}, want {want[bad[0]]:#x}")
+        # random values within range agree with torch's cast (round to nearest even)
+        r = (rng.standard_normal(20000) * rng.choice([1e-3, 1.0, 30.0], 20000)).astype(np.float32)
+        r = np.clip(r, -FP8_MAX[fmt], FP8_MAX[fmt]).astype(np.float32)
+        tc = torch.from_numpy(r).to(FP8_TORCH[fmt]).view(torch.uint8).numpy()
+        if not np.array_equal(orc.fp8_encode(r, fmt), tc):
+            fails.append(f"{fmt}: random values differ from torch's cast")
+    return fails
+
+
+def _lib_quantize(x: np.ndarray, block: int, fmt: str):
+    """Block quantiser from library pieces: numpy amax / fp32 divide / clip and
+    torch's FP8 cast for the rounding."""
+    rows, cols = x.shape
+    br, bc = -(-rows // block), -(-cols // block)
+    S = np.empty((br, bc), np.float32)
+    y = np.empty_like(x)
+    F = np.float32(FP8_MAX[fmt])
+    for i in range(br):
+        for j in range(bc):
+            blk = x[i * block:(i + 1) * block, j * block:(j + 1) * block]
+            amax = np.abs(blk).max()
+            s = np.float32(amax / F) if amax > 0 else np.float32(1.0)
+            S[i, j] = s
+            y[i * block:(i + 1) * block, j * block:(j + 1) * block] = np.clip(blk / s, -F, F)
+    q = torch.from_numpy(np.ascontiguousarray(y)).to(FP8_TORCH[fmt]).view(torch.uint8).numpy()
+    return q, S
+
+
+def pin_quantize_fp8(orc) -> list:
+    fails = []
+    rng = np.random.default_rng(12)
+    # 1. the independent input recipe (E4M3) and the library-piece quantiser
+    for (rows, cols), block in (((100, 130), 64), ((70, 33), 32), ((64, 64), 64), ((1, 1), 32)):
+        x = rng.standard_normal((rows, cols)).astype(np.float32)
+        q, S = orc.quantize_fp8(x, "f32", block, "e4m3")
+        q2, S2 = gi.blockscale_e4m3(x, block)
+        if not (np.array_equal(q, q2) and np.array_equal(S, S2)):
+            fails.append(f"quantize e4m3 {rows}x{cols}/{block}: differs from the input recipe")
+        for fmt in ("e4m3", "e5m2"):
+            q, S = orc.quantize_fp8(x * np.float32(1000.0), "f32", block, fmt)
+            q3, S3 = _lib_quantize(x * np.float32(1000.0), block, fmt)
+            if not (np.array_equal(q, q3) and np.array_equal(S, S3)):
+                fails.append(f"quantize {fmt} {rows}x{cols}/{block}: differs from library pieces")
+    # 2. block position: block (i, j) = base * 2^(i + 3j) on a 3 x 5 grid
+    for block in (32, 64):
+        base = rng.standard_normal((block, block)).astype(np.float32)
+        x = np.block([[base * np.float32(2.0 ** (i + 3 * j)) for j in range(5)] for i in range(3)])
+        x = np.ascontiguousarray(x[: 3 * block - 5, : 5 * block - 7])   # ragged last blocks
+        q, S = orc.quantize_fp8(x, "f32", block, "e4m3")
+        want = S[0, 0] * np.array([[2.0 ** (i + 3 * j) for j in range(5)] for i in range(3)])
+        if not np.array_equal(S[:2, :4].astype(np.float64), want[:2, :4]):
+            fails.append(f"block {block}: scales do not follow the block positions")
+        if not np.array_equal(q[:block, :block], q[block:2 * block, 3 * block:4 * block]):
+            fails.append(f"block {block}: equal blocks quantised differently")
+    # 3. exact-midpoint quotients: x = s * m with m halfway between two FP8 values
+    #    and s = amax / 448 exact, so x / s = m exactly and must round to the even code
+    for sc in (3.0, 5.0, 7.0, 11.0):
+        codes, vals = torch_fp8_table("e4m3")
+        pos = np.unique(vals[vals > 0])
+        mids = ((pos[:-1] + pos[1:]) / 2)[8:60]
+        m = np.stack([np.concatenate([[448.0], mids]), np.concatenate([[-448.0], -mids])])
+        x = np.ascontiguousarray((m * sc).astype(np.float32))    # 2 x 53: one 64x64 block
+        q, S = orc.quantize_fp8(x, "f32", 64, "e4m3")
+        if S.shape != (1, 1) or S[0, 0] != np.float32(sc):
+            fails.append(f"midpoints: scale {S.ravel()[0]} != {sc}")
+        want = brute_nearest(m, "e4m3")
+        bad = np.argwhere(q != want)
+        if bad.size:
+            r, c = bad[0]
+            fails.append(f"midpoints x{sc}: element {r},{c} rounded to {q[r, c]:#x}, want {want[r, c]:#x}")
+    # 4. padding beyond the columns is never read; zero blocks get scale 1
+    x = np.full((40, 80), 1e30, np.float32)
+    x[:, :70] = rng.standard_normal((40, 70)).astype(np.float32)
+    x[:, 64:70] = 0.0
+    x[33:, :] = 1e30
+    q, S = orc.quantize_fp8(x[:33, :70], "f32", 32, "e4m3")
+    q_ref, S_ref = orc.quantize_fp8(np.ascontiguousarray(x[:33, :70]), "f32", 32, "e4m3")
+    if not (np.array_equal(q, q_ref) and np.array_equal(S, S_ref)) or not np.all(np.isfinite(S)):
+        fails.append("quantize reads past the columns it was given")
+    if S[0, 2] != 1.0 or np.any(q[:32, 64:70] != 0):
+        fails.append("a block of zeros must get scale 1 and +0 codes")
+    # 5. invariants: the amax element lands on +-F; reconstruction error bound
+    for fmt, mb in (("e4m3", 3), ("e5m2", 2)):
+        x = (rng.standard_normal((96, 96)) * 10).astype(np.float32)
+        q, S = orc.quantize_fp8(x, "f32", 32, fmt)
+        dq = orc.decode(q, fmt)
+        for i in range(3):
+            for j in range(3):
+                b = dq[32 * i:32 * i + 32, 32 * j:32 * j + 32]
+                if np.abs(b).max() != FP8_MAX[fmt]:
+                    fails.append(f"{fmt}: block ({i},{j}) largest code is not +-{FP8_MAX[fmt]}")
+        rec = dq * np.kron(S.astype(np.float64), np.ones((32, 32)))
+        sub = 2.0 ** (-9 if fmt == "e4m3" else -16)
+        bound = np.abs(x) * 2.0 ** -(mb + 1) * (1 + 1e-6) + np.kron(S, np.ones((32, 32))) * sub
+        if np.any(np.abs(rec - x) > bound):
+            fails.append(f"{fmt}: reconstruction error beyond half a step")
+    # 6. bf16 input = fp32 input of the same values
+    xb = gi.uniform_h16(50, 70, 13, "bf16")
+    xf = np.ascontiguousarray(lib_decode(xb, "bf16").astype(np.float32) * np.float32(4.0))
+    xb3 = gi.to_bf16_bits(xf)
+    qa, Sa = orc.quantize_fp8(xb3, "bf16", 64, "e4m3")
+    qb, Sb = orc.quantize_fp8(xf, "f32", 64, "e4m3")
+    if not (np.array_equal(qa, qb) and np.array_equal(Sa, Sb)):
+        fails.append("bf16 input differs from fp32 input of the same values")
+    return fails
+
+
 ALL_PINS = (pin_decoders, pin_closed_forms, pin_bruteforce, pin_scale_blocks, pin_entries,
-            pin_tolerance_checker)
+            pin_tolerance_checker, pin_fp8_encode, pin_quantize_fp8)
 
 
 def run_all(orc) -> list:

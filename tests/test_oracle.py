@@ -38,6 +38,14 @@ def test_tolerance_checker(orc):
     assert pins.pin_tolerance_checker(orc) == []
 
 
+def test_fp8_encoder(orc):
+    assert pins.pin_fp8_encode(orc) == []
+
+
+def test_fp8_quantiser(orc):
+    assert pins.pin_quantize_fp8(orc) == []
+
+
 def test_thread_count_does_not_change_result(orc):
     import gemm_inputs as gi
     A = gi.uniform_h16(67, 45, 1, "bf16")
@@ -76,6 +84,19 @@ MUTANTS = {
     "scale_block_32": ("#define ORC_SCALE_BLOCK 64", "#define ORC_SCALE_BLOCK 32"),
     "entries_wrong_scale_cols": ("int64_t sb_cols = (N + ORC_SCALE_BLOCK",
                                  "int64_t sb_cols = (K + ORC_SCALE_BLOCK"),
+    # FP8 quantiser
+    "e5m2_decoder_bias": ("ldexp((double)(4 | m), e - 17)", "ldexp((double)(4 | m), e - 16)"),
+    "encode_ties_away": ("double n = rint(a / quantum);", "double n = floor(a / quantum + 0.5);"),
+    "encode_truncates": ("double n = rint(a / quantum);", "double n = floor(a / quantum);"),
+    "encode_no_binade_carry": ("if (n >= ldexp(1.0, mbits + 1)) {", "if (0) {"),
+    "encode_sign_dropped": ("signbit(y) ? 0x80 : 0", "0"),
+    "quant_scale_wrong_max": ("fmt == ORC_FP8_E4M3 ? 448.0f : 57344.0f;",
+                              "fmt == ORC_FP8_E4M3 ? 240.0f : 57344.0f;"),
+    "quant_multiplies": ("input_f32(dtype, X, ldx, r, c) / s;", "input_f32(dtype, X, ldx, r, c) * s;"),
+    "quant_scale_grid_transposed": ("scales[bi * bc + bj] = s;", "scales[bj * br + bi] = s;"),
+    "quant_amax_signed": ("const float a = fabsf(input_f32(dtype, X, ldx, r, c));",
+                          "const float a = input_f32(dtype, X, ldx, r, c);"),
+    "quant_zero_scale": ("amax > 0.0f ? amax / fmax : 1.0f", "amax > 0.0f ? amax / fmax : 0.5f"),
 }
 
 _RUNNER = r"""
