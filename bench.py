@@ -5,7 +5,8 @@ the dense matrix-core peak, on seeded synthetic matrices resident in HBM.
 A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
 (row-major A and B, fp32 accumulation, bf16 C).  The other workloads (fp16
 4096^3, the ragged bf16 shapes, fp32 4096^3, fp8 block-scaled 8192^3, fp16
-256^3) are measured in the same run and listed under "workloads".
+256^3, and the FP8 block quantiser on the fp8 workload's 8192 x 8192 operand)
+are measured in the same run and listed under "workloads".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
 
@@ -173,8 +174,11 @@ class Workload:
         torch.cuda.synchronize()
         per = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
         median = per[len(per) // 2]
-        M, N, K, dt = self.M, self.N, self.K, self.dtype
         cold = self.cold(cold_steps) if cold_steps > 0 else None
+        return self.report(region, wall, mean, median, cold)
+
+    def report(self, region, wall, mean, median, cold) -> dict:
+        M, N, K, dt = self.M, self.N, self.K, self.dtype
         return {
             "workload": self.name, "key": self.key, "dtype": dt, "M": M, "N": N, "K": K,
             "region_s": region, "wall_s": wall,
@@ -185,6 +189,57 @@ class Workload:
             "cold_mean_launch_us": cold * 1e6 if cold else None,
             "cold_tflops": tflops(M, N, K, cold) if cold else None,
         }
+
+    def summary(self, r) -> str:
+        return (f"{r['tflops']:.1f} TFLOP/s ({r['pct_peak']:.1f}% peak), "
+                f"{r['mean_launch_us']:.1f} us/launch")
+
+
+class QuantWorkload(Workload):
+    """The block-scaled FP8 quantiser on a rows x cols fp32 matrix (the step
+    that makes the fp8 GEMM's operands).  HBM-bound: reported as algorithmic
+    GB/s (input read once, codes and scales written once) against 8 TB/s."""
+
+    def __init__(self, key, name, rows, cols, block, fmt, seed):
+        super().__init__(key, name, "f32", rows, cols, 0, 0)
+        self.block, self.fmt, self.seed = block, fmt, seed
+
+    def setup(self):
+        import torch
+
+        import dense_gemm_13_amd as dg
+        import gemm_inputs as gi
+        dev = torch.device("cuda:0")
+        rows, cols, blk = self.M, self.N, self.block
+        self.A = torch.from_numpy(gi.normal_f32(rows, cols, self.seed)).to(dev)
+        self.C = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        self.B = torch.empty((-(-rows // blk), -(-cols // blk)), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        fn, fmt = dg.lib.gemm_quantize_fp8, dg.FP8_FORMATS[self.fmt]
+        x, q, sc = self.A.data_ptr(), self.C.data_ptr(), self.B.data_ptr()
+        self.call = lambda: fn(x, 0, rows, cols, cols, blk, fmt, q, cols, sc, s)
+        torch.cuda.synchronize()
+
+    def alg_bytes(self) -> int:
+        rows, cols, blk = self.M, self.N, self.block
+        return rows * cols * (4 + 1) + 4 * (-(-rows // blk)) * (-(-cols // blk))
+
+    def report(self, region, wall, mean, median, cold) -> dict:
+        gbs = self.alg_bytes() / mean / 1e9
+        return {
+            "workload": self.name, "key": self.key, "dtype": "f32->" + self.fmt,
+            "rows": self.M, "cols": self.N, "block": self.block,
+            "region_s": region, "wall_s": wall,
+            "mean_launch_us": mean * 1e6, "median_launch_us": median * 1e6,
+            "alg_gbs": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+            "cold_mean_launch_us": cold * 1e6 if cold else None,
+            "cold_alg_gbs": self.alg_bytes() / cold / 1e9 if cold else None,
+        }
+
+    def summary(self, r) -> str:
+        return (f"{r['alg_gbs']:.0f} GB/s ({r['pct_hbm_peak']:.1f}% of HBM peak), "
+                f"{r['mean_launch_us']:.1f} us/launch")
 
 
 WORKLOADS = [
@@ -197,6 +252,8 @@ WORKLOADS = [
     Workload("f32_4096", "fp32 SGEMM M=N=K=4096", "f32", 4096, 4096, 4096, 4),
     Workload("fp8_8192", "fp8 E4M3 64x64-block-scaled GEMM M=N=K=8192, bf16 C", "fp8",
              8192, 8192, 8192, 5),
+    QuantWorkload("quant_8192", "FP8 E4M3 64x64 block quantiser, 8192x8192 fp32 N(0,1)",
+                  8192, 8192, 64, "e4m3", 1005),
 ]
 
 
@@ -259,9 +316,7 @@ def main():
         w.setup()
         steps = args.steps if w is headline else max(10, args.steps // 2)
         r = w.run(steps, args.warmup, args.cold_steps)
-        print(f"[bench] {w.name}: {r['tflops']:.1f} TFLOP/s "
-              f"({r['pct_peak']:.1f}% peak), {r['mean_launch_us']:.1f} us/launch",
-              file=sys.stderr, flush=True)
+        print(f"[bench] {w.name}: {w.summary(r)}", file=sys.stderr, flush=True)
         results.append(r)
         if w is not headline:
             del w.A, w.B, w.C

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in include/libgemm.h):
     gemm_bf16(A, B, C=None, stream=None)
     gemm_f32(A, B, C=None, stream=None)
     gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None)
+    gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
 A is M x K and B is K x N (row-major: unit column stride; the row stride is the
 leading dimension).  C, when given, must be M x N with unit column stride; it is
 allocated when omitted.  Work is enqueued on `stream` (default: the current
@@ -27,9 +28,11 @@ LIB_PATH = os.path.join(_HERE, "libgemm.so")
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM_ERR_LD",
                 -4: "GEMM_ERR_ALIGN", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_DEVICE",
-                -7: "GEMM_ERR_LAUNCH"}
+                -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG"}
 ENTRY_POINTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled",
-                "gemm_status_string", "gemm_version")
+                "gemm_quantize_fp8", "gemm_status_string", "gemm_version")
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}          # enum gemm_fp8_format
+QUANT_INPUTS = {"f32": 0, "bf16": 1}          # enum gemm_quant_input
 
 
 class GemmError(RuntimeError):
@@ -55,6 +58,9 @@ def _load():
         fn.restype = ctypes.c_int
     h.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
     h.gemm_fp8_blockscaled.restype = ctypes.c_int
+    h.gemm_quantize_fp8.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                    vp, i64, vp, vp]
+    h.gemm_quantize_fp8.restype = ctypes.c_int
     h.gemm_status_string.argtypes = [ctypes.c_int]
     h.gemm_status_string.restype = ctypes.c_char_p
     h.gemm_version.argtypes = []
@@ -158,5 +164,37 @@ def gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None):
     return C
 
 
-__all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "status_string",
-           "GemmError", "lib", "LIB_PATH"]
+def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None):
+    """Block-scaled FP8 quantisation of a 2-D float32 or bfloat16 tensor.
+
+    Returns (Q, scales): Q holds the FP8 codes (uint8, X's shape; E4M3 or E5M2),
+    scales is the contiguous float32 ceil(rows/block) x ceil(cols/block) grid of
+    per-block scales (block 32 or 64).  With the defaults, quantising A (M x K)
+    and B (K x N) gives gemm_fp8_blockscaled's operands and scales.
+    """
+    torch = _torch()
+    in_type = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(X.dtype)
+    if in_type is None:
+        raise TypeError("gemm_quantize_fp8: X must be float32 or bfloat16")
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"gemm_quantize_fp8: fmt must be one of {sorted(FP8_FORMATS)}")
+    rows, cols = X.shape
+    shape = (-(-rows // block), -(-cols // block)) if block > 0 else (0, 0)
+    if Q is None:
+        Q = torch.empty((rows, cols), dtype=torch.uint8, device=X.device)
+    if scales is None:
+        scales = torch.empty(shape, dtype=torch.float32, device=X.device)
+    if Q.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2) or \
+            tuple(Q.shape) != (rows, cols):
+        raise ValueError(f"gemm_quantize_fp8: Q must be uint8 of shape ({rows}, {cols})")
+    if scales.dtype != torch.float32 or tuple(scales.shape) != shape or \
+            not scales.is_contiguous():
+        raise ValueError(f"gemm_quantize_fp8: scales must be contiguous float32 {shape}")
+    _check(lib.gemm_quantize_fp8(X.data_ptr(), QUANT_INPUTS[in_type], rows, cols, _ld(X), block,
+                                 FP8_FORMATS[fmt], Q.data_ptr(), _ld(Q), scales.data_ptr(),
+                                 _stream_handle(stream, X.device)), "gemm_quantize_fp8")
+    return Q, scales
+
+
+__all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "gemm_quantize_fp8",
+           "status_string", "GemmError", "lib", "LIB_PATH"]

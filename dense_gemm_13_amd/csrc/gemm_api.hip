@@ -221,6 +221,31 @@ extern "C" int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C,
     return to_status(fp8_launch(p, scale_a, scale_b));
 }
 
+extern "C" int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols,
+                                 int64_t ldx, int block, int fmt, uint8_t *Q, int64_t ldq,
+                                 float *scales, hipStream_t stream)
+{
+    if (in_type != GEMM_QUANT_IN_F32 && in_type != GEMM_QUANT_IN_BF16) return GEMM_ERR_ARG;
+    if (block != 32 && block != 64) return GEMM_ERR_ARG;
+    if (fmt != GEMM_FP8_E4M3 && fmt != GEMM_FP8_E5M2) return GEMM_ERR_ARG;
+    if (rows < 0 || cols < 0 || rows > DIM_LIMIT || cols > DIM_LIMIT) return GEMM_ERR_DIM;
+    if (ldx < cols || ldq < cols || ldx > (int64_t)1 << 40 || ldq > (int64_t)1 << 40)
+        return GEMM_ERR_LD;
+    if (rows == 0 || cols == 0) return GEMM_OK;
+    if (X == nullptr || Q == nullptr || scales == nullptr) return GEMM_ERR_NULL;
+    const int64_t esize = in_type == GEMM_QUANT_IN_BF16 ? 2 : 4;
+    if ((uintptr_t)X % esize || ((uintptr_t)scales & 3)) return GEMM_ERR_ALIGN;
+    const int64_t xb = span_bytes(rows, cols, ldx, esize), qb = span_bytes(rows, cols, ldq, 1);
+    const int64_t sb = ((rows + block - 1) / block) * ((cols + block - 1) / block) * 4;
+    if (overlaps(Q, qb, X, xb) || overlaps(scales, sb, X, xb) || overlaps(scales, sb, Q, qb))
+        return GEMM_ERR_ALIAS;
+    int st;
+    if ((st = check_device()) != GEMM_OK) return st;
+    QuantProblem p{X, in_type == GEMM_QUANT_IN_BF16, (int)rows, (int)cols, ldx, block, fmt,
+                   Q, ldq, scales, stream};
+    return to_status(quant_fp8_launch(p));
+}
+
 extern "C" const char *gemm_status_string(int status)
 {
     switch (status) {
@@ -229,9 +254,10 @@ extern "C" const char *gemm_status_string(int status)
     case GEMM_ERR_DIM: return "M, N or K is negative or too large";
     case GEMM_ERR_LD: return "leading dimension smaller than the row (lda < K, ldb < N or ldc < N)";
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
-    case GEMM_ERR_ALIAS: return "C overlaps an input";
+    case GEMM_ERR_ALIAS: return "an output overlaps an input (or the two quantiser outputs overlap)";
     case GEMM_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_ERR_ARG: return "unsupported option (input type, block size or FP8 format)";
     default: return "unknown status";
     }
 }

@@ -48,6 +48,20 @@ hipError_t f32_fast_launch(const Problem &p);
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
 bool fp8_fast_eligible(const Problem &p);
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);
+// One quantiser call after argument checking: rows, cols >= 1, block 32 or 64,
+// fmt 0 (E4M3) or 1 (E5M2).
+struct QuantProblem {
+    const void *X;
+    bool in_bf16;
+    int rows, cols;
+    int64_t ldx;
+    int block, fmt;
+    uint8_t *Q;
+    int64_t ldq;
+    float *scales;
+    hipStream_t stream;
+};
+hipError_t quant_fp8_launch(const QuantProblem &p);
 // Set the M x N window of C (element size esize bytes, leading dimension ldc) to zero.
 hipError_t zero_launch(void *C, int M, int N, int64_t ldc, int esize, hipStream_t stream);
 

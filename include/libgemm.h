@@ -46,10 +46,18 @@ enum gemm_status {
     GEMM_ERR_DIM = -2,     /* M, N or K negative, or larger than the library supports */
     GEMM_ERR_LD = -3,      /* lda < K, ldb < N or ldc < N */
     GEMM_ERR_ALIGN = -4,   /* a pointer is not aligned to its element size */
-    GEMM_ERR_ALIAS = -5,   /* C overlaps an input */
+    GEMM_ERR_ALIAS = -5,   /* an output overlaps an input (or another output) */
     GEMM_ERR_DEVICE = -6,  /* the current device is not a gfx950 GPU, or it cannot be queried */
-    GEMM_ERR_LAUNCH = -7   /* the kernel launch was rejected by the runtime */
+    GEMM_ERR_LAUNCH = -7,  /* the kernel launch was rejected by the runtime */
+    GEMM_ERR_ARG = -8      /* an option argument (input type, block size, FP8 format) is not supported */
 };
+
+/* FP8 formats (OCP): E4M3 ("E4M3FN": bias 7, largest finite 448, no infinities)
+ * and E5M2 (bias 15, largest finite 57344). */
+enum gemm_fp8_format { GEMM_FP8_E4M3 = 0, GEMM_FP8_E5M2 = 1 };
+
+/* Element types the FP8 quantiser reads. */
+enum gemm_quant_input { GEMM_QUANT_IN_F32 = 0, GEMM_QUANT_IN_BF16 = 1 };
 
 /* fp16 (IEEE binary16) A, B and C; fp32 accumulation; C rounded to nearest-even.
  * "[CUDA 优化实战] hgemm - 超越 cuBLAS", sections 1-4 (the half-precision kernels). */
@@ -80,6 +88,31 @@ int gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int
 int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N,
                          int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                          const float *scale_a, const float *scale_b, hipStream_t stream);
+
+/* Block-scaled FP8 quantiser: the step that produces gemm_fp8_blockscaled's
+ * operands.  X is rows x cols, row-major with leading dimension ldx (elements),
+ * fp32 (in_type GEMM_QUANT_IN_F32) or bfloat16 (GEMM_QUANT_IN_BF16).  For every
+ * block x block block (block 32 or 64; blocks at ragged edges are partial):
+ *   amax = the largest |x| of the block's elements,
+ *   s    = amax / F in fp32 (F = 448 for E4M3, 57344 for E5M2); s = 1 if amax = 0,
+ *   Q[i*ldq + j] = the FP8 code (fmt) nearest to clamp(x(i,j) / s, -F, F) in fp32,
+ *                  ties to the even code, sign kept for results that round to 0,
+ *   scales[(i/block) * ceil(cols/block) + j/block] = s   (row-major, contiguous).
+ * With block 64 and E4M3, an M x K matrix gives exactly gemm_fp8_blockscaled's A
+ * and scale_a, and a K x N matrix its B and scale_b.
+ * "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3 (FP8
+ * operands with one scale per 32x32 or 64x64 sub-block) and section 5.2, third
+ * pitfall (32-bit scales).  The pages only say that each block is scaled into
+ * the FP8 range; the amax / F scale and the round-to-nearest-even encoding are
+ * the plain reading of that.
+ * X must be finite.  X, Q and scales are caller-owned device pointers (X aligned
+ * to its element size, scales to 4 bytes); Q and scales must not overlap X or
+ * each other.  rows == 0 or cols == 0 is a no-op.  Bytes of Q between cols and
+ * ldq are never written.  Errors: GEMM_ERR_ARG for an unknown in_type, block or
+ * fmt, else as for the GEMM entry points. */
+int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols, int64_t ldx,
+                      int block, int fmt, uint8_t *Q, int64_t ldq, float *scales,
+                      hipStream_t stream);
 
 /* Static, NUL-terminated description of a gemm_status value. */
 const char *gemm_status_string(int status);

@@ -31,17 +31,27 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = dg.status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert dg.status_string(-99) == "unknown status"
     assert lib.gemm_version() >= 100
 
 
+def _enum(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"enum\s+" + name + r"\s*\{(.*?)\}", text, flags=re.S).group(1)
+    return {n: int(v) for n, v in re.findall(r"(GEMM_\w+)\s*=\s*(-?\d+)", body)}
+
+
 def test_enum_values_match_header():
-    text = open(HEADER).read()
-    for name, val in re.findall(r"(GEMM_\w+)\s*=\s*(-?\d+)", text):
-        assert dg.STATUS_NAMES[int(val)] == name
+    status = _enum("gemm_status")
+    assert len(status) == len(dg.STATUS_NAMES)
+    for name, val in status.items():
+        assert dg.STATUS_NAMES[val] == name
+    assert _enum("gemm_fp8_format") == {"GEMM_FP8_" + k.upper(): v for k, v in dg.FP8_FORMATS.items()}
+    assert _enum("gemm_quant_input") == {"GEMM_QUANT_IN_" + k.upper(): v
+                                         for k, v in dg.QUANT_INPUTS.items()}
 
 
 # Fake, never-dereferenced device addresses: 4 KiB aligned and far apart.
@@ -97,6 +107,34 @@ def test_fp8_argument_errors():
     assert call(a=0, b=0, c=0, sa=0, sb=0, M=0) == 0
 
 
+def test_quantize_argument_errors():
+    fn = lib.gemm_quantize_fp8
+    X, Q, S = A, B, SA
+
+    def call(x=X, it=0, rows=64, cols=64, ldx=64, block=64, fmt=0, q=Q, ldq=64, s=S):
+        return fn(x, it, rows, cols, ldx, block, fmt, q, ldq, s, None)
+
+    assert call(it=2) == -8
+    assert call(block=16) == -8
+    assert call(block=128) == -8
+    assert call(fmt=2) == -8
+    assert call(rows=-1) == -2
+    assert call(cols=1 << 31) == -2
+    assert call(ldx=63) == -3
+    assert call(ldq=10) == -3
+    assert call(x=0) == -1
+    assert call(q=0) == -1
+    assert call(s=0) == -1
+    assert call(x=X + 2) == -4             # fp32 input needs 4-byte alignment
+    assert call(x=X + 2, it=1) != -4       # bf16 input: 2 bytes are enough
+    assert call(s=S + 2) == -4
+    assert call(q=X + 64) == -5            # codes over the input
+    assert call(s=X + 128) == -5           # scales over the input
+    assert call(s=Q + 8) == -5             # scales over the codes
+    assert call(x=0, q=0, s=0, rows=0) == 0
+    assert call(x=0, q=0, s=0, cols=0, ldx=0, ldq=0) == 0
+
+
 def test_no_gpu_is_reported_as_device_error():
     import torch
     if torch.cuda.is_available():
@@ -104,6 +142,7 @@ def test_no_gpu_is_reported_as_device_error():
     assert h16(lib.gemm_bf16) == -6
     # K == 0 still needs the device (it zeroes C)
     assert h16(lib.gemm_bf16, a=0, b=0, K=0, lda=0) == -6
+    assert lib.gemm_quantize_fp8(A, 0, 64, 64, 64, 64, 0, B, 64, SA, None) == -6
 
 
 def test_tensor_binding_validates_before_calling():
