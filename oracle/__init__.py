@@ -14,7 +14,11 @@ module only marshals numpy arrays into it.  What it follows:
 * "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 4.3 and
   section 5.2 (third pitfall): E4M3 operands with one 32-bit scale per 64x64
   sub-block, and the quantiser that makes them (``quantize_fp8``: E4M3 or E5M2,
-  32x32 or 64x64 blocks, scale = block amax / largest FP8 value, RNE).
+  32x32 or 64x64 blocks, scale = block amax / largest FP8 value, RNE);
+* the same article, section 1.1 (a fully connected layer is a product plus a
+  bias per output feature), and the relu epilogue of the vendor kernel in
+  "[CUDA 优化实战] hgemm - 超越 cuBLAS" section 5: ``epilogue`` applies
+  out = act(alpha * prod + beta * C_prior + bias[column]) to the exact product.
 
 ``gemm`` returns the exact sum (fp64, k ascending, never rounded to the
 output type).  ``within_tolerance`` is the element-wise acceptance test
@@ -71,6 +75,9 @@ def bind(lib):
     lib.orc_quantize_fp8.argtypes = [ctypes.c_int, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                      vp, i64, vp]
     lib.orc_quantize_fp8.restype = ctypes.c_int
+    lib.orc_epilogue.argtypes = [ctypes.c_int, vp, i64, i64, ctypes.c_double, ctypes.c_double,
+                                 vp, i64, vp, ctypes.c_int, vp]
+    lib.orc_epilogue.restype = ctypes.c_int
     return lib
 
 
@@ -206,3 +213,38 @@ def quantize_fp8(X: np.ndarray, dtype: str, block: int, fmt: str):
     if rc != 0:
         raise RuntimeError(f"orc_quantize_fp8 failed ({rc})")
     return Q, S
+
+
+ACTIVATIONS = {"none": 0, "relu": 1}
+
+
+def epilogue(out_dtype: str, prod: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+             c_prior: np.ndarray | None = None, bias: np.ndarray | None = None,
+             act: str = "none") -> np.ndarray:
+    """Exact (fp64) act(alpha * prod + beta * c_prior + bias[j]) of an M x N
+    product.  out_dtype is C's type ("f16", "bf16", "f32"; the fp8 GEMM writes
+    "bf16"); c_prior holds C's raw bits before the call (read only when beta != 0);
+    bias is None or N float32 values; act is "none" or "relu".  alpha and beta
+    are taken as fp32 values, as the library receives them."""
+    lib = _load()
+    prod = np.ascontiguousarray(prod, dtype=np.float64)
+    M, N = prod.shape
+    cb = None
+    ldc = max(N, 1)
+    if c_prior is not None:
+        cb = _raw(c_prior, out_dtype)
+        if cb.shape[0] < M or cb.shape[1] < N:
+            raise ValueError("c_prior smaller than the product")
+        ldc = _ld(cb) if M > 1 else max(cb.shape[1], 1)
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        if b.shape != (N,):
+            raise ValueError("bias must hold one value per column")
+    out = np.empty((M, N), dtype=np.float64)
+    rc = lib.orc_epilogue(DTYPES[out_dtype], prod.ctypes.data, M, N,
+                          float(np.float32(alpha)), float(np.float32(beta)), _ptr(cb), ldc,
+                          _ptr(b), ACTIVATIONS[act], out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"orc_epilogue failed ({rc})")
+    return out

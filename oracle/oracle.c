@@ -362,3 +362,42 @@ int orc_quantize_fp8(int dtype, const void *X, int64_t rows, int64_t cols, int64
         }
     return 0;
 }
+
+/* ---------------------------------------------------- fused epilogue */
+
+/* The step after the product, applied entry by entry to the exact sum:
+ *   out[i][j] = act( alpha * prod[i][j] + beta * c(i, j) + bias[j] )
+ * "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析", section 1.1: a
+ * fully connected layer is a matrix product plus a bias, one bias value per
+ * output feature, i.e. per column j of C (C = X * W with X of batch x inputs and
+ * W of inputs x outputs).  "[CUDA 优化实战] hgemm - 超越 cuBLAS", section 5: the
+ * vendor kernel it compares against carries a relu in its epilogue, so the
+ * activation is max(v, 0) applied last.  alpha and beta are the usual scales
+ * of the product and of the C already in memory; the pages name neither, so
+ * their reading is the plain BLAS one: c(i, j) is the prior output value decoded
+ * from the output type's bits (row-major, leading dimension ldc) and it is read
+ * only when beta != 0, so a C that holds garbage (even NaN) is fine then.
+ * bias may be NULL (no bias).  act: 0 = none, 1 = relu.
+ * prod and out are M x N fp64 with leading dimension N (out may be prod).
+ * out_dtype: ORC_F16, ORC_BF16 or ORC_F32.  Returns 0, or -1 on bad arguments. */
+int orc_epilogue(int out_dtype, const double *prod, int64_t M, int64_t N, double alpha,
+                 double beta, const void *c_bits, int64_t ldc, const float *bias, int act,
+                 double *out)
+{
+    if (M < 0 || N < 0 || ldc < N || (act != 0 && act != 1)) return -1;
+    if (out_dtype != ORC_F16 && out_dtype != ORC_BF16 && out_dtype != ORC_F32) return -1;
+    if (beta != 0.0 && !c_bits && M > 0 && N > 0) return -1;
+    for (int64_t i = 0; i < M; i++)
+        for (int64_t j = 0; j < N; j++) {
+            double v = alpha * prod[i * N + j];
+            if (beta != 0.0) v = v + beta * operand_at(out_dtype, c_bits, ldc, i, j, NULL, 0);
+            if (bias) {
+                uint32_t bbits;
+                memcpy(&bbits, &bias[j], 4);
+                v = v + orc_f32_to_f64(bbits);
+            }
+            if (act == 1 && !(v > 0.0)) v = 0.0;
+            out[i * N + j] = v;
+        }
+    return 0;
+}

@@ -12,7 +12,10 @@ Independent sources used here:
 * exact rational brute force (fractions.Fraction) on tiny inputs;
 * for the FP8 quantiser: torch's float8_e4m3fn / float8_e5m2 casts and decodings,
   brute-force nearest-value search over every FP8 code, exact-midpoint quotients,
-  power-of-two block patterns and the independent input recipe in gemm_inputs.
+  power-of-two block patterns and the independent input recipe in gemm_inputs;
+* for the fused epilogue: hand-derived closed forms on all-ones products with a
+  per-column bias, a row- and column-dependent prior C in a NaN-padded buffer,
+  relu thresholds and a NaN-filled prior that beta = 0 must leave unread.
 """
 from __future__ import annotations
 
@@ -428,8 +431,80 @@ def pin_quantize_fp8(orc) -> list:
     return fails
 
 
+# ------------------------------------------------------------ fused epilogue
+
+_NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
+
+
+def _prior(out: str, vals: np.ndarray, ldc: int) -> np.ndarray:
+    """C's bits before the call: `vals` (exactly representable) in the first
+    columns, NaN in the padding up to ldc (a reader that ignores ldc picks it up)."""
+    M, N = vals.shape
+    if out == "f32":
+        buf = np.full((M, ldc), np.nan, dtype=np.float32)
+        buf[:, :N] = vals
+    else:
+        buf = np.full((M, ldc), _NAN_BITS[out], dtype=np.uint16)
+        buf[:, :N] = encode(vals, out)
+    return buf
+
+
+def pin_epilogue(orc) -> list:
+    """act(alpha * A*B + beta * C_prior + bias[j]) on structured inputs whose
+    results follow in closed form (worked out by hand, below), for every output
+    type: all-ones products (every entry = K), per-column bias, a prior C that
+    varies with row and column and sits in a padded buffer, relu thresholds on
+    either side of zero, and a NaN-filled prior that must not be read when
+    beta = 0."""
+    fails = []
+    M, N, K = 5, 7, 9
+    i = np.arange(M, dtype=np.float64)[:, None]
+    j = np.arange(N, dtype=np.float64)[None, :]
+    for out in ("f16", "bf16", "f32"):
+        op = "f32" if out == "f32" else out
+        ones_a, ones_b = encode(np.ones((M, K)), op), encode(np.ones((K, N)), op)
+        prod = orc.gemm(op, ones_a, ones_b, M, N, K)              # = K everywhere
+        prior_vals = (i - 2.0 * j) + 0.375                        # exact in every type
+        prior = _prior(out, prior_vals, N + 3)
+        bias = (np.arange(N) / 4.0).astype(np.float32)
+        cases = [
+            # alpha * K + beta * (i - 2j + 3/8) + j/4 with alpha = 2, beta = -1/2:
+            # 18 - i/2 + j - 3/16 + j/4
+            ("scales, prior, bias", dict(alpha=2.0, beta=-0.5, c_prior=prior, bias=bias),
+             18.0 - 0.5 * i + 1.25 * j - 0.1875),
+            # no prior read: alpha = 1/2 -> K/2 + j/4
+            ("bias only", dict(alpha=0.5, bias=bias), 4.5 + 0.25 * j + 0 * i),
+            # relu after the bias: v = K + (j - 3 - K) = j - 3
+            ("relu after bias", dict(bias=(np.arange(N) - 3.0 - K).astype(np.float32),
+                                     act="relu"), np.maximum(j - 3.0, 0.0) + 0 * i),
+            # relu of a negated product: v = -K + (K + 1 - j) = 1 - j
+            ("relu, negative alpha", dict(alpha=-1.0, bias=(K + 1.0 - np.arange(N))
+                                          .astype(np.float32), act="relu"),
+             np.maximum(1.0 - j, 0.0) + 0 * i),
+            # beta = 0: a NaN-filled C must not be read
+            ("beta 0 ignores C", dict(alpha=1.0, beta=0.0,
+                                      c_prior=_prior(out, np.full((M, N), np.nan), N)),
+             np.full((M, N), float(K))),
+            # only the prior: alpha = 0, beta = 4 -> 4i - 8j + 3/2
+            ("prior only", dict(alpha=0.0, beta=4.0, c_prior=prior),
+             4.0 * i - 8.0 * j + 1.5),
+        ]
+        for name, kw, want in cases:
+            got = orc.epilogue(out, prod, **kw)
+            if not np.array_equal(got, want):
+                bad = np.argwhere(got != want)[0]
+                fails.append(f"epilogue {out} {name}: at {tuple(bad)} got "
+                             f"{got[tuple(bad)]} want {want[tuple(bad)]}")
+        # identity settings leave any product unchanged
+        rnd = orc.gemm(op, *[random_operand(r, c, op, s)[0] for r, c, s in
+                             ((M, K, 11), (K, N, 12))], M, N, K)
+        if not np.array_equal(orc.epilogue(out, rnd), rnd):
+            fails.append(f"epilogue {out}: alpha=1, beta=0, no bias, no act changed the product")
+    return fails
+
+
 ALL_PINS = (pin_decoders, pin_closed_forms, pin_bruteforce, pin_scale_blocks, pin_entries,
-            pin_tolerance_checker, pin_fp8_encode, pin_quantize_fp8)
+            pin_tolerance_checker, pin_fp8_encode, pin_quantize_fp8, pin_epilogue)
 
 
 def run_all(orc) -> list:

@@ -46,6 +46,10 @@ def test_fp8_quantiser(orc):
     assert pins.pin_quantize_fp8(orc) == []
 
 
+def test_epilogue(orc):
+    assert pins.pin_epilogue(orc) == []
+
+
 def test_thread_count_does_not_change_result(orc):
     import gemm_inputs as gi
     A = gi.uniform_h16(67, 45, 1, "bf16")
@@ -97,6 +101,26 @@ MUTANTS = {
     "quant_amax_signed": ("const float a = fabsf(input_f32(dtype, X, ldx, r, c));",
                           "const float a = input_f32(dtype, X, ldx, r, c);"),
     "quant_zero_scale": ("amax > 0.0f ? amax / fmax : 1.0f", "amax > 0.0f ? amax / fmax : 0.5f"),
+    # fused epilogue
+    "epi_alpha_dropped": ("double v = alpha * prod[i * N + j];", "double v = prod[i * N + j];"),
+    "epi_beta_sign": ("v = v + beta * operand_at", "v = v - beta * operand_at"),
+    "epi_prior_read_when_beta_zero": ("if (beta != 0.0) v = v + beta", "v = v + beta"),
+    "epi_prior_ignores_ldc": ("operand_at(out_dtype, c_bits, ldc, i, j",
+                              "operand_at(out_dtype, c_bits, N, i, j"),
+    "epi_prior_wrong_type": ("operand_at(out_dtype, c_bits", "operand_at(ORC_BF16, c_bits"),
+    "epi_bias_by_row": ("memcpy(&bbits, &bias[j], 4);", "memcpy(&bbits, &bias[i], 4);"),
+    "epi_relu_is_abs": ("if (act == 1 && !(v > 0.0)) v = 0.0;", "if (act == 1 && !(v > 0.0)) v = -v;"),
+    "epi_relu_before_bias": ("""            if (bias) {
+                uint32_t bbits;
+                memcpy(&bbits, &bias[j], 4);
+                v = v + orc_f32_to_f64(bbits);
+            }
+            if (act == 1 && !(v > 0.0)) v = 0.0;""", """            if (act == 1 && !(v > 0.0)) v = 0.0;
+            if (bias) {
+                uint32_t bbits;
+                memcpy(&bbits, &bias[j], 4);
+                v = v + orc_f32_to_f64(bbits);
+            }"""),
 }
 
 _RUNNER = r"""
