@@ -5,8 +5,9 @@ the dense matrix-core peak, on seeded synthetic matrices resident in HBM.
 A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
 (row-major A and B, fp32 accumulation, bf16 C).  The other workloads (fp16
 4096^3, the ragged bf16 shapes, fp32 4096^3, fp8 block-scaled 8192^3, fp16
-256^3, and the FP8 block quantiser on the fp8 workload's 8192 x 8192 operand)
-are measured in the same run and listed under "workloads".
+256^3, the 4096^3 bf16 product with a fused bias + relu epilogue and with a
+fused residual add, and the FP8 block quantiser on the fp8 workload's
+8192 x 8192 operand) are measured in the same run and listed under "workloads".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
 
@@ -242,6 +243,43 @@ class QuantWorkload(Workload):
                 f"{r['mean_launch_us']:.1f} us/launch")
 
 
+class EpilogueWorkload(Workload):
+    """A GEMM through its fused-epilogue entry point: a fully connected layer
+    C = relu(A*B + bias) (alpha 1, beta 0, one fp32 bias per column), or with
+    beta != 0 a residual add of the prior C as well."""
+
+    def __init__(self, key, name, dtype, M, N, K, wid, beta=0.0):
+        super().__init__(key, name, dtype, M, N, K, wid)
+        self.beta = beta
+
+    def setup(self):
+        import torch
+
+        import dense_gemm_13_amd as dg
+        import gemm_inputs as gi
+        super().setup()
+        dev = self.C.device
+        self.bias = torch.from_numpy(gi.uniform_f32(1, self.N, 7000 + self.wid)[0]).to(dev)
+        self.C.zero_()
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        M, N, K = self.M, self.N, self.K
+        a, b, c, bias = self.A.data_ptr(), self.B.data_ptr(), self.C.data_ptr(), self.bias.data_ptr()
+        fn = getattr(dg.lib, f"gemm_{self.dtype}_epilogue")
+        relu = dg.ACTIVATIONS["relu"]
+        beta = self.beta
+        self.call = lambda: fn(a, b, c, M, N, K, K, N, N, 1.0, beta, bias, relu, s)
+        torch.cuda.synchronize()
+
+    def report(self, region, wall, mean, median, cold) -> dict:
+        r = super().report(region, wall, mean, median, cold)
+        # the prior C is read once more when beta != 0
+        extra = OUT_BYTES[self.dtype] * self.M * self.N if self.beta != 0 else 0
+        r["alg_gbs"] = (algorithmic_bytes(self.dtype, self.M, self.N, self.K) + extra
+                        + 4 * self.N) / mean / 1e9
+        r["epilogue"] = f"relu(A*B + {'C + ' if self.beta else ''}bias)"
+        return r
+
+
 WORKLOADS = [
     Workload("bf16_4096", "bf16 GEMM M=N=K=4096", "bf16", 4096, 4096, 4096, 2),
     Workload("f16_4096", "fp16 GEMM M=N=K=4096", "f16", 4096, 4096, 4096, 2),
@@ -252,6 +290,10 @@ WORKLOADS = [
     Workload("f32_4096", "fp32 SGEMM M=N=K=4096", "f32", 4096, 4096, 4096, 4),
     Workload("fp8_8192", "fp8 E4M3 64x64-block-scaled GEMM M=N=K=8192, bf16 C", "fp8",
              8192, 8192, 8192, 5),
+    EpilogueWorkload("bf16_4096_bias_relu", "bf16 GEMM M=N=K=4096, fused relu(A*B + bias)",
+                     "bf16", 4096, 4096, 4096, 2),
+    EpilogueWorkload("bf16_4096_residual", "bf16 GEMM M=N=K=4096, fused relu(A*B + C + bias)",
+                     "bf16", 4096, 4096, 4096, 2, beta=1.0),
     QuantWorkload("quant_8192", "FP8 E4M3 64x64 block quantiser, 8192x8192 fp32 N(0,1)",
                   8192, 8192, 64, "e4m3", 1005),
 ]

@@ -10,6 +10,12 @@ Entry points (same names as the C ABI in include/libgemm.h):
     gemm_f32(A, B, C=None, stream=None)
     gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None)
     gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
+    gemm_f16_epilogue / gemm_bf16_epilogue / gemm_f32_epilogue(A, B, C=None, alpha=1.0,
+        beta=0.0, bias=None, activation="none", stream=None)
+    gemm_fp8_blockscaled_epilogue(A, B, scale_a, scale_b, C=None, alpha=1.0, beta=0.0,
+        bias=None, activation="none", stream=None)
+The *_epilogue calls write act(alpha * A@B + beta * C + bias[column]) (fp32,
+one rounding); C must be given when beta != 0 (its prior contents are read).
 A is M x K and B is K x N (row-major: unit column stride; the row stride is the
 leading dimension).  C, when given, must be M x N with unit column stride; it is
 allocated when omitted.  Work is enqueued on `stream` (default: the current
@@ -30,7 +36,10 @@ STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM
                 -4: "GEMM_ERR_ALIGN", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_DEVICE",
                 -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG"}
 ENTRY_POINTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled",
-                "gemm_quantize_fp8", "gemm_status_string", "gemm_version")
+                "gemm_f16_epilogue", "gemm_bf16_epilogue", "gemm_f32_epilogue",
+                "gemm_fp8_blockscaled_epilogue", "gemm_quantize_fp8", "gemm_status_string",
+                "gemm_version")
+ACTIVATIONS = {"none": 0, "relu": 1}          # enum gemm_activation
 FP8_FORMATS = {"e4m3": 0, "e5m2": 1}          # enum gemm_fp8_format
 QUANT_INPUTS = {"f32": 0, "bf16": 1}          # enum gemm_quant_input
 
@@ -58,6 +67,14 @@ def _load():
         fn.restype = ctypes.c_int
     h.gemm_fp8_blockscaled.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, vp]
     h.gemm_fp8_blockscaled.restype = ctypes.c_int
+    f32, ci = ctypes.c_float, ctypes.c_int
+    for name in ("gemm_f16_epilogue", "gemm_bf16_epilogue", "gemm_f32_epilogue"):
+        fn = getattr(h, name)
+        fn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, vp, ci, vp]
+        fn.restype = ctypes.c_int
+    h.gemm_fp8_blockscaled_epilogue.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
+                                                f32, f32, vp, ci, vp]
+    h.gemm_fp8_blockscaled_epilogue.restype = ctypes.c_int
     h.gemm_quantize_fp8.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                     vp, i64, vp, vp]
     h.gemm_quantize_fp8.restype = ctypes.c_int
@@ -103,7 +120,24 @@ def _check(status: int, where: str):
         raise GemmError(status, where)
 
 
-def _h16(name, want_dtype, A, B, C, stream):
+def _epilogue_args(name, C, N, alpha, beta, bias, activation, device):
+    """(alpha, beta, bias pointer, activation id) of a *_epilogue call."""
+    torch = _torch()
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"{name}: activation must be one of {sorted(ACTIVATIONS)}")
+    if beta != 0.0 and C is None:
+        raise ValueError(f"{name}: beta != 0 reads C, so C must be given")
+    bptr = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or tuple(bias.shape) != (N,) or not bias.is_contiguous() \
+                or bias.device != device:
+            raise ValueError(f"{name}: bias must be a contiguous float32 vector of {N} values "
+                             "on C's device")
+        bptr = bias.data_ptr()
+    return float(alpha), float(beta), bptr, ACTIVATIONS[activation]
+
+
+def _h16(name, want_dtype, A, B, C, stream, epilogue=None):
     torch = _torch()
     if A.dtype != want_dtype or B.dtype != want_dtype:
         raise TypeError(f"{name}: A and B must be {want_dtype}")
@@ -111,12 +145,15 @@ def _h16(name, want_dtype, A, B, C, stream):
     K2, N = B.shape
     if K2 != K:
         raise ValueError(f"{name}: inner dimensions differ ({K} vs {K2})")
+    extra = ()
+    if epilogue is not None:
+        extra = _epilogue_args(name, C, N, *epilogue, A.device)
     if C is None:
         C = torch.empty((M, N), dtype=want_dtype, device=A.device)
     if C.dtype != want_dtype or tuple(C.shape) != (M, N):
         raise ValueError(f"{name}: C must be {want_dtype} of shape ({M}, {N})")
     _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A), _ld(B),
-                              _ld(C), _stream_handle(stream, A.device)), name)
+                              _ld(C), *extra, _stream_handle(stream, A.device)), name)
     return C
 
 
@@ -135,6 +172,32 @@ def gemm_f32(A, B, C=None, stream=None):
     return _h16("gemm_f32", _torch().float32, A, B, C, stream)
 
 
+def _fp8(name, A, B, scale_a, scale_b, C, stream, epilogue=None):
+    torch = _torch()
+    if A.dtype not in (torch.uint8, torch.float8_e4m3fn) or B.dtype != A.dtype:
+        raise TypeError(f"{name}: A and B must be uint8 or float8_e4m3fn")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"{name}: inner dimensions differ ({K} vs {K2})")
+    cdiv = lambda a, b: -(-a // b)
+    for s, shape, nm in ((scale_a, (cdiv(M, 64), cdiv(K, 64)), "scale_a"),
+                         (scale_b, (cdiv(K, 64), cdiv(N, 64)), "scale_b")):
+        if s.dtype != torch.float32 or tuple(s.shape) != shape or not s.is_contiguous():
+            raise ValueError(f"{name}: {nm} must be contiguous float32 {shape}")
+    extra = ()
+    if epilogue is not None:
+        extra = _epilogue_args(name, C, N, *epilogue, A.device)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, N):
+        raise ValueError(f"{name}: C must be bfloat16 of shape ({M}, {N})")
+    _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A), _ld(B),
+                              _ld(C), scale_a.data_ptr(), scale_b.data_ptr(), *extra,
+                              _stream_handle(stream, A.device)), name)
+    return C
+
+
 def gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None):
     """C = (A * scale_a) @ (B * scale_b) with E4M3 codes and one fp32 scale per 64 x 64 block.
 
@@ -142,26 +205,38 @@ def gemm_fp8_blockscaled(A, B, scale_a, scale_b, C=None, stream=None):
     scale_a: ceil(M/64) x ceil(K/64) float32, scale_b: ceil(K/64) x ceil(N/64)
     float32, both contiguous.  C: M x N bfloat16.
     """
-    torch = _torch()
-    if A.dtype not in (torch.uint8, torch.float8_e4m3fn) or B.dtype != A.dtype:
-        raise TypeError("gemm_fp8_blockscaled: A and B must be uint8 or float8_e4m3fn")
-    M, K = A.shape
-    K2, N = B.shape
-    if K2 != K:
-        raise ValueError(f"gemm_fp8_blockscaled: inner dimensions differ ({K} vs {K2})")
-    cdiv = lambda a, b: -(-a // b)
-    for s, shape, nm in ((scale_a, (cdiv(M, 64), cdiv(K, 64)), "scale_a"),
-                         (scale_b, (cdiv(K, 64), cdiv(N, 64)), "scale_b")):
-        if s.dtype != torch.float32 or tuple(s.shape) != shape or not s.is_contiguous():
-            raise ValueError(f"gemm_fp8_blockscaled: {nm} must be contiguous float32 {shape}")
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, N):
-        raise ValueError(f"gemm_fp8_blockscaled: C must be bfloat16 of shape ({M}, {N})")
-    _check(lib.gemm_fp8_blockscaled(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A),
-                                    _ld(B), _ld(C), scale_a.data_ptr(), scale_b.data_ptr(),
-                                    _stream_handle(stream, A.device)), "gemm_fp8_blockscaled")
-    return C
+    return _fp8("gemm_fp8_blockscaled", A, B, scale_a, scale_b, C, stream)
+
+
+def gemm_f16_epilogue(A, B, C=None, alpha=1.0, beta=0.0, bias=None, activation="none",
+                      stream=None):
+    """C = act(alpha * A@B + beta * C + bias[column]) for float16 A, B, C.
+
+    bias: None or a float32 vector of N values; activation: "none" or "relu".
+    """
+    return _h16("gemm_f16_epilogue", _torch().float16, A, B, C, stream,
+                (alpha, beta, bias, activation))
+
+
+def gemm_bf16_epilogue(A, B, C=None, alpha=1.0, beta=0.0, bias=None, activation="none",
+                       stream=None):
+    """C = act(alpha * A@B + beta * C + bias[column]) for bfloat16 A, B, C."""
+    return _h16("gemm_bf16_epilogue", _torch().bfloat16, A, B, C, stream,
+                (alpha, beta, bias, activation))
+
+
+def gemm_f32_epilogue(A, B, C=None, alpha=1.0, beta=0.0, bias=None, activation="none",
+                      stream=None):
+    """C = act(alpha * A@B + beta * C + bias[column]) for float32 A, B, C."""
+    return _h16("gemm_f32_epilogue", _torch().float32, A, B, C, stream,
+                (alpha, beta, bias, activation))
+
+
+def gemm_fp8_blockscaled_epilogue(A, B, scale_a, scale_b, C=None, alpha=1.0, beta=0.0,
+                                  bias=None, activation="none", stream=None):
+    """C = act(alpha * (A*scale_a)@(B*scale_b) + beta * C + bias[column]), bfloat16 C."""
+    return _fp8("gemm_fp8_blockscaled_epilogue", A, B, scale_a, scale_b, C, stream,
+                (alpha, beta, bias, activation))
 
 
 def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None):
@@ -196,5 +271,6 @@ def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
     return Q, scales
 
 
-__all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "gemm_quantize_fp8",
-           "status_string", "GemmError", "lib", "LIB_PATH"]
+__all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "gemm_f16_epilogue",
+           "gemm_bf16_epilogue", "gemm_f32_epilogue", "gemm_fp8_blockscaled_epilogue",
+           "gemm_quantize_fp8", "status_string", "GemmError", "lib", "LIB_PATH"]

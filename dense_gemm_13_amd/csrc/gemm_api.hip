@@ -10,6 +10,9 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <cmath>
+
+#include "gemm_device.hpp"
 #include "gemm_launch.hpp"
 #include "libgemm.h"
 
@@ -17,14 +20,31 @@ namespace gemm {
 
 namespace {
 
-// Set the M x N window of C to zero (the K == 0 case: every sum is empty).
-template <typename T>
-__global__ void zero_window_kernel(T *__restrict__ C, int M, int N, int64_t ldc)
+// The K == 0 case, every sum empty: the M x N window of C becomes zero, or with
+// an epilogue act(beta * c_prior + bias[column]).
+template <int OUT, bool EPI>
+__global__ void empty_sum_kernel(void *C, int M, int N, int64_t ldc, Epilogue epi)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)M * N) return;
-    const int64_t m = idx / N, n = idx % N;
-    C[m * ldc + n] = T(0);
+    const int64_t m = idx / N;
+    const int n = (int)(idx % N);
+    float v = 0.f;
+    if constexpr (EPI) {
+        const size_t row_bytes = (size_t)m * ldc * (OUT == OUT_F32 ? 4 : 2);
+        const void *row = static_cast<const char *>(C) + row_bytes;
+        float x = v;
+        if (epi.beta != 0.f) x = epi.beta * load_out<OUT>(row, n);
+        if (epi.bias) x += epi.bias[n];
+        if (epi.relu) x = x > 0.f ? x : 0.f;
+        v = x;
+    }
+    if constexpr (OUT == OUT_F32)
+        static_cast<float *>(C)[m * ldc + n] = v;
+    else if constexpr (OUT == OUT_BF16)
+        static_cast<uint16_t *>(C)[m * ldc + n] = to_bf16_bits(v);
+    else
+        static_cast<uint16_t *>(C)[m * ldc + n] = to_f16_bits(v);
 }
 
 constexpr int MAX_DEVICES = 64;
@@ -94,16 +114,39 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
 
+// Checks of the epilogue options (before any other check) and, once the call
+// has work, of the bias vector against C.  *epi is filled from the options.
+int check_epilogue_options(float alpha, float beta, int activation, Epilogue *epi)
+{
+    if (activation != GEMM_ACT_NONE && activation != GEMM_ACT_RELU) return GEMM_ERR_ARG;
+    if (!std::isfinite(alpha) || !std::isfinite(beta)) return GEMM_ERR_ARG;
+    *epi = Epilogue{alpha, beta, nullptr, activation == GEMM_ACT_RELU ? 1 : 0};
+    return GEMM_OK;
+}
+
+int check_bias(const float *bias, const void *C, int64_t M, int64_t N, int64_t ldc,
+               int64_t esize_out)
+{
+    if (bias == nullptr) return GEMM_OK;
+    if ((uintptr_t)bias & 3) return GEMM_ERR_ALIGN;
+    if (overlaps(C, span_bytes(M, N, ldc, esize_out), bias, N * 4)) return GEMM_ERR_ALIAS;
+    return GEMM_OK;
+}
+
 int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, int64_t N,
-              int64_t K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+              int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const Epilogue *epi,
+              hipStream_t stream)
 {
     bool work;
     int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 2, 2, &work);
     if (st != GEMM_OK || !work) return st;
+    if (epi && (st = check_bias(epi->bias, C, M, N, ldc, 2)) != GEMM_OK) return st;
     int cus = 0;
     if ((st = check_device(&cus)) != GEMM_OK) return st;
-    if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 2, stream));
-    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
+    if (K == 0)
+        return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, is_bf16 ? OUT_BF16 : OUT_F16,
+                                          epi, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, epi};
     p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
                 ldc % 8 == 0;
     // Tuning / testing override: LIBGEMM_H16_CONFIG=<H16Config id> (the large-tile
@@ -153,54 +196,51 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
 
 }  // namespace
 
-hipError_t zero_launch(void *C, int M, int N, int64_t ldc, int esize, hipStream_t stream)
+template <int OUT>
+static void empty_sum_typed(dim3 grid, dim3 block, void *C, int M, int N, int64_t ldc,
+                            const Epilogue *epi, hipStream_t stream)
+{
+    if (epi)
+        hipLaunchKernelGGL((empty_sum_kernel<OUT, true>), grid, block, 0, stream, C, M, N, ldc, *epi);
+    else
+        hipLaunchKernelGGL((empty_sum_kernel<OUT, false>), grid, block, 0, stream, C, M, N, ldc,
+                           Epilogue{1.f, 0.f, nullptr, 0});
+}
+
+hipError_t empty_sum_launch(void *C, int M, int N, int64_t ldc, int out, const Epilogue *epi,
+                            hipStream_t stream)
 {
     const int64_t total = (int64_t)M * N;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (esize == 2)
-        hipLaunchKernelGGL(zero_window_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0,
-                           stream, static_cast<uint16_t *>(C), M, N, ldc);
-    else
-        hipLaunchKernelGGL(zero_window_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0,
-                           stream, static_cast<float *>(C), M, N, ldc);
+    const dim3 grid((unsigned)blocks), block(threads);
+    if (out == OUT_F32) empty_sum_typed<OUT_F32>(grid, block, C, M, N, ldc, epi, stream);
+    else if (out == OUT_BF16) empty_sum_typed<OUT_BF16>(grid, block, C, M, N, ldc, epi, stream);
+    else empty_sum_typed<OUT_F16>(grid, block, C, M, N, ldc, epi, stream);
     return hipGetLastError();
 }
 
-}  // namespace gemm
+namespace {
 
-using namespace gemm;
-
-extern "C" int gemm_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
-                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
-{
-    return h16_entry(false, A, B, C, M, N, K, lda, ldb, ldc, stream);
-}
-
-extern "C" int gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
-                         int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
-{
-    return h16_entry(true, A, B, C, M, N, K, lda, ldb, ldc, stream);
-}
-
-extern "C" int gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
-                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+int f32_entry(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+              int64_t lda, int64_t ldb, int64_t ldc, const Epilogue *epi, hipStream_t stream)
 {
     bool work;
     int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 4, 4, &work);
     if (st != GEMM_OK || !work) return st;
+    if (epi && (st = check_bias(epi->bias, C, M, N, ldc, 4)) != GEMM_OK) return st;
     if ((st = check_device()) != GEMM_OK) return st;
-    if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 4, stream));
-    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
+    if (K == 0) return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, OUT_F32, epi, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, epi};
     p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
                 ldc % 4 == 0;
     return to_status(f32_launch(p));
 }
 
-extern "C" int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
-                                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                                    const float *scale_a, const float *scale_b, hipStream_t stream)
+int fp8_entry(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N, int64_t K,
+              int64_t lda, int64_t ldb, int64_t ldc, const float *scale_a, const float *scale_b,
+              const Epilogue *epi, hipStream_t stream)
 {
     bool work;
     int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 1, 2, &work);
@@ -213,12 +253,90 @@ extern "C" int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C,
         const int64_t sbb = ((K + 63) / 64) * ((N + 63) / 64) * 4;
         if (overlaps(C, cb, scale_a, sab) || overlaps(C, cb, scale_b, sbb)) return GEMM_ERR_ALIAS;
     }
+    if (epi && (st = check_bias(epi->bias, C, M, N, ldc, 2)) != GEMM_OK) return st;
     if ((st = check_device()) != GEMM_OK) return st;
-    if (K == 0) return to_status(zero_launch(C, (int)M, (int)N, ldc, 2, stream));
-    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream};
+    if (K == 0) return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, OUT_BF16, epi, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, epi};
     p.aligned = aligned16(A) && ((uintptr_t)B & 3) == 0 && aligned16(C) && lda % 16 == 0 &&
                 ldb % 4 == 0 && ldc % 8 == 0;
     return to_status(fp8_launch(p, scale_a, scale_b));
+}
+
+}  // namespace
+
+}  // namespace gemm
+
+using namespace gemm;
+
+extern "C" int gemm_f16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    return h16_entry(false, A, B, C, M, N, K, lda, ldb, ldc, nullptr, stream);
+}
+
+extern "C" int gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    return h16_entry(true, A, B, C, M, N, K, lda, ldb, ldc, nullptr, stream);
+}
+
+extern "C" int gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    return f32_entry(A, B, C, M, N, K, lda, ldb, ldc, nullptr, stream);
+}
+
+extern "C" int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
+                                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                    const float *scale_a, const float *scale_b, hipStream_t stream)
+{
+    return fp8_entry(A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, nullptr, stream);
+}
+
+extern "C" int gemm_f16_epilogue(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float alpha,
+                                 float beta, const float *bias, int activation, hipStream_t stream)
+{
+    Epilogue epi;
+    const int st = check_epilogue_options(alpha, beta, activation, &epi);
+    if (st != GEMM_OK) return st;
+    epi.bias = bias;
+    return h16_entry(false, A, B, C, M, N, K, lda, ldb, ldc, &epi, stream);
+}
+
+extern "C" int gemm_bf16_epilogue(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                                  int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float alpha,
+                                  float beta, const float *bias, int activation, hipStream_t stream)
+{
+    Epilogue epi;
+    const int st = check_epilogue_options(alpha, beta, activation, &epi);
+    if (st != GEMM_OK) return st;
+    epi.bias = bias;
+    return h16_entry(true, A, B, C, M, N, K, lda, ldb, ldc, &epi, stream);
+}
+
+extern "C" int gemm_f32_epilogue(const float *A, const float *B, float *C, int64_t M, int64_t N,
+                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float alpha,
+                                 float beta, const float *bias, int activation, hipStream_t stream)
+{
+    Epilogue epi;
+    const int st = check_epilogue_options(alpha, beta, activation, &epi);
+    if (st != GEMM_OK) return st;
+    epi.bias = bias;
+    return f32_entry(A, B, C, M, N, K, lda, ldb, ldc, &epi, stream);
+}
+
+extern "C" int gemm_fp8_blockscaled_epilogue(const uint8_t *A, const uint8_t *B, void *C,
+                                             int64_t M, int64_t N, int64_t K, int64_t lda,
+                                             int64_t ldb, int64_t ldc, const float *scale_a,
+                                             const float *scale_b, float alpha, float beta,
+                                             const float *bias, int activation, hipStream_t stream)
+{
+    Epilogue epi;
+    const int st = check_epilogue_options(alpha, beta, activation, &epi);
+    if (st != GEMM_OK) return st;
+    epi.bias = bias;
+    return fp8_entry(A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, &epi, stream);
 }
 
 extern "C" int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols,
@@ -257,9 +375,11 @@ extern "C" const char *gemm_status_string(int status)
     case GEMM_ERR_ALIAS: return "an output overlaps an input (or the two quantiser outputs overlap)";
     case GEMM_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
-    case GEMM_ERR_ARG: return "unsupported option (input type, block size or FP8 format)";
+    case GEMM_ERR_ARG:
+        return "unsupported option (input type, block size, FP8 format, activation, or a "
+               "non-finite alpha or beta)";
     default: return "unknown status";
     }
 }
 
-extern "C" int gemm_version(void) { return 100; }
+extern "C" int gemm_version(void) { return 200; }

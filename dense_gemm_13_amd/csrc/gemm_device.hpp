@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_launch.hpp"
+
 namespace gemm {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -75,6 +77,129 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi)
         return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
     else
         return (uint32_t)to_f16_bits(lo) | ((uint32_t)to_f16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------ fused epilogue
+
+enum OutType { OUT_F16 = 0, OUT_BF16 = 1, OUT_F32 = 2 };
+
+// fp32 value of element n of a C row of type OUT.
+template <int OUT>
+__device__ __forceinline__ float load_out(const void *row, int n)
+{
+    if constexpr (OUT == OUT_F32) {
+        return static_cast<const float *>(row)[n];
+    } else {
+        const uint16_t bits = static_cast<const uint16_t *>(row)[n];
+        if constexpr (OUT == OUT_BF16) return __uint_as_float((uint32_t)bits << 16);
+        else return (float)__builtin_bit_cast(_Float16, bits);
+    }
+}
+
+// The fused epilogue on W consecutive fp32 results v[0..W) of one row of C,
+// columns n .. n+W-1, of which the first `cnt` are inside the matrix (cnt <= 0:
+// none).  Those become
+//   act(alpha * v + beta * c_prior + bias[column])
+// with the prior C read only when beta != 0 and only inside the matrix.  A
+// fully connected layer is a product plus one bias per output feature
+// ("深度学习加速核心：GEMM优化从分块到TensorCore的实战解析" section 1.1); the relu
+// is the epilogue of the vendor kernel "[CUDA 优化实战] hgemm - 超越 cuBLAS"
+// compares against (section 5).  The three steps are separate so that a kernel
+// can load the bias once per column and the prior C of a whole row block ahead
+// of the arithmetic.
+
+// bias[n .. n+W) (0 past cnt or without a bias); one vector load when all W are
+// inside and aligned.
+template <int W>
+__device__ __forceinline__ void epilogue_bias(const Epilogue &e, int n, int cnt, float *b)
+{
+    static_assert(W == 4 || W == 8, "epilogue width");
+    if (e.bias && cnt >= W && ((uintptr_t)(e.bias + n) & 15) == 0) {
+#pragma unroll
+        for (int h = 0; h < W / 4; ++h) {
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(e.bias + n + 4 * h);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) b[4 * h + t] = x[t];
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < W; ++t) b[t] = e.bias && t < cnt ? e.bias[n + t] : 0.f;
+    }
+}
+
+// The prior C at row[n .. n+W) as fp32 (0 past cnt or when beta == 0); 16-bit
+// types are read W at a time when all are inside and the address is aligned.
+template <int OUT, int W>
+__device__ __forceinline__ void epilogue_prior(const Epilogue &e, const void *row, int n, int cnt,
+                                               float *c)
+{
+    static_assert(W == 4 || W == 8, "epilogue width");
+    if (e.beta == 0.f) {
+#pragma unroll
+        for (int t = 0; t < W; ++t) c[t] = 0.f;
+        return;
+    }
+    if constexpr (OUT != OUT_F32) {
+        const uint16_t *p = static_cast<const uint16_t *>(row) + n;
+        if (cnt >= W && ((uintptr_t)p & (2 * W - 1)) == 0) {
+            uint32_t w[W / 2];
+            if constexpr (W == 4) {
+                const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+                w[0] = x[0]; w[1] = x[1];
+            } else {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(p);
+                w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+            }
+#pragma unroll
+            for (int t = 0; t < W; ++t) {
+                const uint16_t bits = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+                if constexpr (OUT == OUT_BF16) c[t] = __uint_as_float((uint32_t)bits << 16);
+                else c[t] = (float)__builtin_bit_cast(_Float16, bits);
+            }
+            return;
+        }
+    } else {
+        const float *p = static_cast<const float *>(row) + n;
+        if (cnt >= W && ((uintptr_t)p & 15) == 0) {
+#pragma unroll
+            for (int h = 0; h < W / 4; ++h) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(p + 4 * h);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) c[4 * h + t] = x[t];
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < W; ++t) c[t] = t < cnt ? load_out<OUT>(row, n + t) : 0.f;
+}
+
+// v = act(alpha * v + beta * c + b) for the first cnt entries.
+template <int W>
+__device__ __forceinline__ void epilogue_apply(const Epilogue &e, float *v, const float *b,
+                                               const float *c, int cnt)
+{
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+        if (t < cnt) {
+            float x = e.alpha * v[t];
+            if (e.beta != 0.f) x = fmaf(e.beta, c[t], x);
+            x += b[t];
+            if (e.relu) x = x > 0.f ? x : 0.f;
+            v[t] = x;
+        }
+    }
+}
+
+// All three steps for one group of W entries (`row` points at column 0).
+template <int OUT, int W>
+__device__ __forceinline__ void epilogue_row(const Epilogue &e, float *v, const void *row, int n,
+                                             int cnt)
+{
+    float b[W], c[W];
+    epilogue_bias<W>(e, n, cnt, b);
+    epilogue_prior<OUT, W>(e, row, n, cnt, c);
+    epilogue_apply<W>(e, v, b, c, cnt);
 }
 
 // -------------------------------------------------------------- MFMA wrappers

@@ -37,11 +37,12 @@ __device__ __forceinline__ f32x4 load4_guarded(const float *p, bool row_ok, int 
     return f32x4{v[0], v[1], v[2], v[3]};
 }
 
-template <int BM, int BN, int WM, int WN, bool ALIGNED>
+// EPI: the fused epilogue is applied to the results by the lane that stores them.
+template <int BM, int BN, int WM, int WN, bool ALIGNED, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 f32_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float *__restrict__ C,
                 int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m,
-                int tiles_n, int group_m)
+                int tiles_n, int group_m, Epilogue epi)
 {
     constexpr int BK = F32_BK;
     constexpr int NT = WM * WN * 64;
@@ -176,8 +177,10 @@ f32_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + j * 32 + 8 * g + 4 * half;
-                const f32x4 v{total[i][j][4 * g], total[i][j][4 * g + 1], total[i][j][4 * g + 2],
-                              total[i][j][4 * g + 3]};
+                float ev[4] = {total[i][j][4 * g], total[i][j][4 * g + 1], total[i][j][4 * g + 2],
+                               total[i][j][4 * g + 3]};
+                if constexpr (EPI) epilogue_row<OUT_F32, 4>(epi, ev, crow, n, N - n);
+                const f32x4 v{ev[0], ev[1], ev[2], ev[3]};
                 if (ALIGNED && n + 4 <= N) {
                     *reinterpret_cast<f32x4 *>(crow + n) = v;
                 } else {
@@ -190,8 +193,8 @@ f32_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const Problem &p)
+template <int BM, int BN, int WM, int WN, bool EPI>
+hipError_t launch_cfg_epi(const Problem &p)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
@@ -201,13 +204,22 @@ hipError_t launch_cfg(const Problem &p)
     const float *A = static_cast<const float *>(p.A);
     const float *B = static_cast<const float *>(p.B);
     float *C = static_cast<float *>(p.C);
+    const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (p.aligned)
-        hipLaunchKernelGGL((f32_gemm_kernel<BM, BN, WM, WN, true>), grid, block, 0, p.stream, A, B,
-                           C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m);
+        hipLaunchKernelGGL((f32_gemm_kernel<BM, BN, WM, WN, true, EPI>), grid, block, 0, p.stream,
+                           A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m,
+                           epi);
     else
-        hipLaunchKernelGGL((f32_gemm_kernel<BM, BN, WM, WN, false>), grid, block, 0, p.stream, A,
-                           B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m);
+        hipLaunchKernelGGL((f32_gemm_kernel<BM, BN, WM, WN, false, EPI>), grid, block, 0, p.stream,
+                           A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m,
+                           epi);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(const Problem &p)
+{
+    return p.epi ? launch_cfg_epi<BM, BN, WM, WN, true>(p) : launch_cfg_epi<BM, BN, WM, WN, false>(p);
 }
 
 }  // namespace

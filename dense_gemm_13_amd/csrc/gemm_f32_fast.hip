@@ -42,10 +42,12 @@ __host__ __device__ __forceinline__ int swz_bf(int k) { return ((k >> 2) & 1) <<
 
 __device__ __forceinline__ void s_barrier_nf() { asm volatile("s_barrier" ::: "memory"); }
 
+// EPI: the fused epilogue is applied to the results by the lane that stores them.
+template <bool EPI>
 __global__ void __launch_bounds__(SNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float *__restrict__ C,
                 int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n,
-                int group_m)
+                int group_m, Epilogue epi)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -164,10 +166,14 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
 #pragma unroll
         for (int j = 0; j < SFN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<f32x4 *>(crow + 32 * j + 8 * g) =
-                    f32x4{total[i][j][4 * g], total[i][j][4 * g + 1], total[i][j][4 * g + 2],
-                          total[i][j][4 * g + 3]};
+            for (int g = 0; g < 4; ++g) {
+                float ev[4] = {total[i][j][4 * g], total[i][j][4 * g + 1], total[i][j][4 * g + 2],
+                               total[i][j][4 * g + 3]};
+                if constexpr (EPI)
+                    epilogue_row<OUT_F32, 4>(epi, ev, C + (int64_t)(m0 + wm0 + 32 * i + l32) * ldc,
+                                             n0 + wn0 + 4 * half + 32 * j + 8 * g, 4);
+                *reinterpret_cast<f32x4 *>(crow + 32 * j + 8 * g) = f32x4{ev[0], ev[1], ev[2], ev[3]};
+            }
     }
 }
 
@@ -186,10 +192,15 @@ hipError_t f32_fast_launch(const Problem &p)
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    hipLaunchKernelGGL(f32_fast_kernel, dim3((unsigned)nwg), dim3(SNW * 64), 0, p.stream,
-                       static_cast<const float *>(p.A), static_cast<const float *>(p.B),
-                       static_cast<float *>(p.C), p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
-                       group_m);
+    const float *A = static_cast<const float *>(p.A), *B = static_cast<const float *>(p.B);
+    float *C = static_cast<float *>(p.C);
+    if (p.epi)
+        hipLaunchKernelGGL(f32_fast_kernel<true>, dim3((unsigned)nwg), dim3(SNW * 64), 0, p.stream,
+                           A, B, C, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m, *p.epi);
+    else
+        hipLaunchKernelGGL(f32_fast_kernel<false>, dim3((unsigned)nwg), dim3(SNW * 64), 0,
+                           p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m,
+                           Epilogue{1.f, 0.f, nullptr, 0});
     return hipGetLastError();
 }
 

@@ -47,12 +47,14 @@ __device__ __forceinline__ uint32_t load4b_guarded(const uint8_t *p, bool row_ok
     return w;
 }
 
-template <int BM, int BN, int WM, int WN, bool ALIGNED>
+// EPI: the fused epilogue is applied to the fp32 results before rounding, by
+// the lane that stores them.
+template <int BM, int BN, int WM, int WN, bool ALIGNED, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 fp8_gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
                 int64_t ldc, const float *__restrict__ scale_a, const float *__restrict__ scale_b,
-                int tiles_m, int tiles_n, int group_m)
+                int tiles_m, int tiles_n, int group_m, Epilogue epi)
 {
     constexpr int BK = FP8_BK;
     constexpr int NT = WM * WN * 64;
@@ -223,8 +225,10 @@ fp8_gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + j * 32 + 8 * g + 4 * half;
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                float ev[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                               acc[i][j][4 * g + 3]};
+                if constexpr (EPI) epilogue_row<OUT_BF16, 4>(epi, ev, crow, n, N - n);
+                const float v0 = ev[0], v1 = ev[1], v2 = ev[2], v3 = ev[3];
                 if (ALIGNED && n + 4 <= N) {
                     *reinterpret_cast<u32x2 *>(crow + n) =
                         u32x2{pack2<true>(v0, v1), pack2<true>(v2, v3)};
@@ -239,8 +243,8 @@ fp8_gemm_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     }
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const Problem &p, const float *sa, const float *sb)
+template <int BM, int BN, int WM, int WN, bool EPI>
+hipError_t launch_cfg_epi(const Problem &p, const float *sa, const float *sb)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
@@ -250,15 +254,23 @@ hipError_t launch_cfg(const Problem &p, const float *sa, const float *sb)
     const uint8_t *A = static_cast<const uint8_t *>(p.A);
     const uint8_t *B = static_cast<const uint8_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
+    const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (p.aligned)
-        hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, true>), grid, block, 0, p.stream, A, B,
-                           C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, sa, sb, tiles_m, tiles_n,
-                           group_m);
+        hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, true, EPI>), grid, block, 0, p.stream,
+                           A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, sa, sb, tiles_m, tiles_n,
+                           group_m, epi);
     else
-        hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, false>), grid, block, 0, p.stream, A,
-                           B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, sa, sb, tiles_m, tiles_n,
-                           group_m);
+        hipLaunchKernelGGL((fp8_gemm_kernel<BM, BN, WM, WN, false, EPI>), grid, block, 0, p.stream,
+                           A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, sa, sb, tiles_m, tiles_n,
+                           group_m, epi);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(const Problem &p, const float *sa, const float *sb)
+{
+    return p.epi ? launch_cfg_epi<BM, BN, WM, WN, true>(p, sa, sb)
+                 : launch_cfg_epi<BM, BN, WM, WN, false>(p, sa, sb);
 }
 
 }  // namespace

@@ -87,11 +87,15 @@ __device__ __forceinline__ void q_unroll(F &&f)
     q_unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// EPI: the fused epilogue is applied to the fp32 accumulators before they are
+// rounded; the lane that reads an entry's prior C does not store it, but the
+// store depends through LDS on the value that read produced.
+template <bool EPI>
 __global__ void __launch_bounds__(QNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 uint16_t *__restrict__ C, int K, int64_t lda, int64_t ldb, int64_t ldc,
                 const float *__restrict__ scale_a, const float *__restrict__ scale_b,
-                int kblocks, int nblocks, int tiles_m, int tiles_n, int group_m)
+                int kblocks, int nblocks, int tiles_m, int tiles_n, int group_m, Epilogue epi)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -217,11 +221,41 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
     q_barrier();
     uint16_t *st = reinterpret_cast<uint16_t *>(q_ring(wave));
+    // EPI: the bias of this lane's columns, loaded once for all its rows.
+    [[maybe_unused]] float ebias[EPI ? QFN : 1][4][4];
+    if constexpr (EPI) {
+#pragma unroll
+        for (int j = 0; j < QFN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                epilogue_bias<4>(epi, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4, ebias[j][q]);
+    }
 #pragma unroll
     for (int i = 0; i < QFM; ++i) {
         const int row = 32 * i + l32;
         uint16_t *buf = st + row * QWTN;
         const int hsw = half ^ ((row >> 3) & 1);
+        if constexpr (EPI) {
+            // The prior C of the row's entries first, then the arithmetic.
+            const uint16_t *crow = C + (int64_t)(m0 + wm0 + row) * ldc;
+            float prior[QFN][4][4];
+#pragma unroll
+            for (int j = 0; j < QFN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    epilogue_prior<OUT_BF16, 4>(epi, crow, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4,
+                                                prior[j][q]);
+#pragma unroll
+            for (int j = 0; j < QFN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                  acc[i][j][4 * q + 3]};
+                    epilogue_apply<4>(epi, v, ebias[j][q], prior[j][q], 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = v[e];
+                }
+        }
 #pragma unroll
         for (int j = 0; j < QFN; ++j)
 #pragma unroll
@@ -260,10 +294,16 @@ hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    hipLaunchKernelGGL(fp8_fast_kernel, dim3((unsigned)nwg), dim3(QNW * 64), 0, p.stream,
-                       static_cast<const uint8_t *>(p.A), static_cast<const uint8_t *>(p.B),
-                       static_cast<uint16_t *>(p.C), p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b,
-                       p.K / 64, p.N / 64, tiles_m, tiles_n, group_m);
+    const uint8_t *A = static_cast<const uint8_t *>(p.A), *B = static_cast<const uint8_t *>(p.B);
+    uint16_t *C = static_cast<uint16_t *>(p.C);
+    if (p.epi)
+        hipLaunchKernelGGL(fp8_fast_kernel<true>, dim3((unsigned)nwg), dim3(QNW * 64), 0, p.stream,
+                           A, B, C, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b, p.K / 64, p.N / 64,
+                           tiles_m, tiles_n, group_m, *p.epi);
+    else
+        hipLaunchKernelGGL(fp8_fast_kernel<false>, dim3((unsigned)nwg), dim3(QNW * 64), 0,
+                           p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b, p.K / 64,
+                           p.N / 64, tiles_m, tiles_n, group_m, Epilogue{1.f, 0.f, nullptr, 0});
     return hipGetLastError();
 }
 

@@ -49,11 +49,13 @@ __device__ __forceinline__ u32x4 load8_guarded(const uint16_t *p, bool row_ok, i
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <bool IS_BF16, int BM, int BN, int WM, int WN, bool ALIGNED>
+// EPI: the fused epilogue is applied to the fp32 results before rounding, by
+// the lane that stores them.
+template <bool IS_BF16, int BM, int BN, int WM, int WN, bool ALIGNED, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64)
 h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
-                int64_t ldc, int tiles_m, int tiles_n, int group_m)
+                int64_t ldc, int tiles_m, int tiles_n, int group_m, Epilogue epi)
 {
     constexpr int BK = H16_BK;
     constexpr int NT = WM * WN * 64;
@@ -201,8 +203,11 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + j * 32 + 8 * g + 4 * half;
-                const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-                const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+                float ev[4] = {acc[i][j][4 * g + 0], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                               acc[i][j][4 * g + 3]};
+                if constexpr (EPI)
+                    epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(epi, ev, crow, n, N - n);
+                const float v0 = ev[0], v1 = ev[1], v2 = ev[2], v3 = ev[3];
                 if (ALIGNED && n + 4 <= N) {
                     *reinterpret_cast<u32x2 *>(crow + n) =
                         u32x2{pack2<IS_BF16>(v0, v1), pack2<IS_BF16>(v2, v3)};
@@ -218,8 +223,8 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     }
 }
 
-template <bool IS_BF16, int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const Problem &p)
+template <bool IS_BF16, int BM, int BN, int WM, int WN, bool EPI>
+hipError_t launch_cfg_epi(const Problem &p)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
@@ -229,15 +234,23 @@ hipError_t launch_cfg(const Problem &p)
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
+    const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (p.aligned)
-        hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, true>), grid, block, 0,
+        hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, true, EPI>), grid, block, 0,
                            p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m,
-                           tiles_n, group_m);
+                           tiles_n, group_m, epi);
     else
-        hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, false>), grid, block, 0,
+        hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, false, EPI>), grid, block, 0,
                            p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m,
-                           tiles_n, group_m);
+                           tiles_n, group_m, epi);
     return hipGetLastError();
+}
+
+template <bool IS_BF16, int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(const Problem &p)
+{
+    return p.epi ? launch_cfg_epi<IS_BF16, BM, BN, WM, WN, true>(p)
+                 : launch_cfg_epi<IS_BF16, BM, BN, WM, WN, false>(p);
 }
 
 template <bool IS_BF16>

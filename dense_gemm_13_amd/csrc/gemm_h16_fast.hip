@@ -121,11 +121,16 @@ __device__ __forceinline__ uint16_t *ring_array(int idx)
 //     that is not B's last, i.e. inside the operand;
 //   * steps are guarded when the number of K steps is not a multiple of the
 //     ring depth, and C stores are masked to the M x N window.
-template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN>
+//
+// EPI: the fused epilogue is applied to the fp32 accumulators before they are
+// rounded (each lane reads the bias and, for beta != 0, the prior C of the
+// entries it holds; it never stores them itself, but the store of an entry
+// depends through LDS on the value this read produced).
+template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
-                int64_t ldc, int tiles_m, int tiles_n, int group_m)
+                int64_t ldc, int tiles_m, int tiles_n, int group_m, Epilogue epi)
 {
     constexpr int FNW = WM * WN;
     constexpr int FWTM = FBM / WM, FWTN = FBN / WN;      // wave sub-tile
@@ -388,19 +393,51 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     uint16_t *st[ARR];
 #pragma unroll
     for (int a = 0; a < ARR; ++a) st[a] = ring_array<8192>(wave * ARR + a);
+    // EPI, whole tiles: the bias of this lane's columns, loaded once for all
+    // its rows.
+    [[maybe_unused]] float ebias[EPI && !GEN ? FFN : 1][4][4];
+    if constexpr (EPI && !GEN) {
+#pragma unroll
+        for (int j = 0; j < FFN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                epilogue_bias<4>(epi, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4, ebias[j][q]);
+    }
 #pragma unroll
     for (int i = 0; i < FFM; ++i) {
         const int row = 32 * i + l32;
         uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
         const int hsw = half ^ ((row / CPRC) & 1);
+        [[maybe_unused]] const int gm = m0 + wm0 + row;
+        [[maybe_unused]] const uint16_t *crow = C + (int64_t)gm * ldc;
+        // EPI, whole tiles: the prior C of the row's entries first (all loads in
+        // flight at once), then the arithmetic.  The guarded variant, short of
+        // registers, takes each group of 4 entries on its own.
+        [[maybe_unused]] float prior[EPI && !GEN ? FFN : 1][4][4];
+        if constexpr (EPI && !GEN) {
+#pragma unroll
+            for (int j = 0; j < FFN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    epilogue_prior<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(
+                        epi, crow, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4, prior[j][q]);
+        }
 #pragma unroll
         for (int j = 0; j < FFN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]};
+                if constexpr (EPI && GEN) {
+                    const int gn = n0 + wn0 + 32 * j + 8 * q + 4 * half;
+                    if (gm < M)
+                        epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(epi, v, crow, gn, N - gn);
+                } else if constexpr (EPI) {
+                    epilogue_apply<4>(epi, v, ebias[j][q], prior[j][q], 4);
+                }
                 const int chunk = (4 * j + q) ^ (row % CPRC);
                 *reinterpret_cast<u32x2 *>(buf + chunk * 8 + hsw * 4) =
-                    u32x2{pack2<IS_BF16>(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                          pack2<IS_BF16>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                    u32x2{pack2<IS_BF16>(v[0], v[1]), pack2<IS_BF16>(v[2], v[3])};
             }
     }
     uint16_t *const cbase = C + (int64_t)(m0 + wm0) * ldc + n0 + wn0;
@@ -449,7 +486,7 @@ bool h16_general_eligible(const Problem &p)
            (int64_t)FAST_BK * p.ldb + p.N < (int64_t)1 << 30;
 }
 
-template <bool GEN>
+template <bool GEN, bool EPI>
 static hipError_t fast_launch(bool is_bf16, const Problem &p)
 {
     const int tiles_m = (p.M + FBM - 1) / FBM, tiles_n = (p.N + FBN - 1) / FBN;
@@ -460,27 +497,28 @@ static hipError_t fast_launch(bool is_bf16, const Problem &p)
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const dim3 grid((unsigned)nwg), block(FAST_WM * FAST_WN * 64);
+    const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (is_bf16)
-        hipLaunchKernelGGL((h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN>),
-                           grid, block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc,
-                           tiles_m, tiles_n, group_m);
+        hipLaunchKernelGGL(
+            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI>), grid, block,
+            0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m, epi);
     else
-        hipLaunchKernelGGL((h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN>),
-                           grid, block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc,
-                           tiles_m, tiles_n, group_m);
+        hipLaunchKernelGGL(
+            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI>), grid, block,
+            0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m, epi);
     return hipGetLastError();
 }
 
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_fast_eligible(p)) return hipErrorInvalidValue;
-    return fast_launch<false>(is_bf16, p);
+    return p.epi ? fast_launch<false, true>(is_bf16, p) : fast_launch<false, false>(is_bf16, p);
 }
 
 hipError_t h16_general_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_general_eligible(p)) return hipErrorInvalidValue;
-    return fast_launch<true>(is_bf16, p);
+    return p.epi ? fast_launch<true, true>(is_bf16, p) : fast_launch<true, false>(is_bf16, p);
 }
 
 }  // namespace gemm

@@ -69,11 +69,13 @@ __device__ __forceinline__ uint16_t *a_stage() { return nl_stage<S, NNW * NA_WAV
 template <int S>
 __device__ __forceinline__ uint16_t *b_stage() { return nl_stage<NSTAGES + S, NNW * NB_WAVE>; }
 
-template <bool IS_BF16, bool GEN>
+// EPI: the fused epilogue is applied to the reduced fp32 sums before rounding
+// (the thread that reads an entry's prior C is the one that stores it).
+template <bool IS_BF16, bool GEN, bool EPI>
 __global__ void __launch_bounds__(NNW * 64)
 h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                   uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
-                  int64_t ldc, int tiles_n)
+                  int64_t ldc, int tiles_n, Epilogue epi)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -244,6 +246,11 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
             for (int e = 0; e < 4; ++e) s[4 * h + e] += v[e];
         }
     }
+    if constexpr (EPI) {
+        if (!GEN || m0 + row < M)
+            epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 8>(epi, s, C + (int64_t)(m0 + row) * ldc,
+                                                          n0 + 8 * c8, GEN ? N - n0 - 8 * c8 : 8);
+    }
     const u32x4 out{pack2<IS_BF16>(s[0], s[1]), pack2<IS_BF16>(s[2], s[3]),
                     pack2<IS_BF16>(s[4], s[5]), pack2<IS_BF16>(s[6], s[7])};
     uint16_t *dst = C + (int64_t)(m0 + row) * ldc + n0 + 8 * c8;
@@ -280,7 +287,7 @@ bool h16_narrow_general_eligible(const Problem &p)
            (int64_t)NBK * p.ldb + p.N < ((int64_t)1 << 31);
 }
 
-template <bool GEN>
+template <bool GEN, bool EPI>
 static hipError_t narrow_launch(bool is_bf16, const Problem &p)
 {
     const int tiles_n = (p.N + NBN - 1) / NBN;
@@ -289,25 +296,28 @@ static hipError_t narrow_launch(bool is_bf16, const Problem &p)
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
+    const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (is_bf16)
-        hipLaunchKernelGGL((h16_narrow_kernel<true, GEN>), dim3((unsigned)nwg), dim3(NNW * 64), 0,
-                           p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_n);
+        hipLaunchKernelGGL((h16_narrow_kernel<true, GEN, EPI>), dim3((unsigned)nwg),
+                           dim3(NNW * 64), 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb,
+                           p.ldc, tiles_n, epi);
     else
-        hipLaunchKernelGGL((h16_narrow_kernel<false, GEN>), dim3((unsigned)nwg), dim3(NNW * 64), 0,
-                           p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_n);
+        hipLaunchKernelGGL((h16_narrow_kernel<false, GEN, EPI>), dim3((unsigned)nwg),
+                           dim3(NNW * 64), 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb,
+                           p.ldc, tiles_n, epi);
     return hipGetLastError();
 }
 
 hipError_t h16_narrow_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_narrow_eligible(p)) return hipErrorInvalidValue;
-    return narrow_launch<false>(is_bf16, p);
+    return p.epi ? narrow_launch<false, true>(is_bf16, p) : narrow_launch<false, false>(is_bf16, p);
 }
 
 hipError_t h16_narrow_general_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_narrow_general_eligible(p)) return hipErrorInvalidValue;
-    return narrow_launch<true>(is_bf16, p);
+    return p.epi ? narrow_launch<true, true>(is_bf16, p) : narrow_launch<true, false>(is_bf16, p);
 }
 
 }  // namespace gemm

@@ -6,6 +6,16 @@
 
 namespace gemm {
 
+// Fused epilogue of one call: every output value v becomes
+//   act(alpha * v + beta * c_prior + bias[column])
+// in fp32 before it is rounded to C's type; c_prior (C before the call) is read
+// only when beta != 0, bias is nullptr for none, relu is 0 or 1.
+struct Epilogue {
+    float alpha, beta;
+    const float *bias;
+    int relu;
+};
+
 // One GEMM call after argument checking: every size fits in int, K >= 1,
 // M >= 1, N >= 1.  `aligned` says the 16-byte vector paths are legal for this
 // call (pointer and leading-dimension alignment as required by the dtype).
@@ -17,6 +27,7 @@ struct Problem {
     int64_t lda, ldb, ldc;
     bool aligned;
     hipStream_t stream;
+    const Epilogue *epi;   // nullptr: plain C = A*B
 };
 
 // Half-precision tile configurations (rows x cols of C per workgroup, waves).
@@ -62,7 +73,10 @@ struct QuantProblem {
     hipStream_t stream;
 };
 hipError_t quant_fp8_launch(const QuantProblem &p);
-// Set the M x N window of C (element size esize bytes, leading dimension ldc) to zero.
-hipError_t zero_launch(void *C, int M, int N, int64_t ldc, int esize, hipStream_t stream);
+// K == 0: every sum is empty.  Sets the M x N window of C (out: 0 fp16, 1 bf16,
+// 2 fp32; leading dimension ldc) to zero, or with an epilogue to
+// act(beta * c_prior + bias[column]).
+hipError_t empty_sum_launch(void *C, int M, int N, int64_t ldc, int out, const Epilogue *epi,
+                            hipStream_t stream);
 
 }  // namespace gemm

@@ -1,16 +1,17 @@
 /*
  * libgemm -- dense GEMM C = A * B on AMD Instinct MI355X (gfx950).
  *
- * The operation (all four entry points):
+ * The operation (the four GEMM entry points):
  *   C[i*ldc + j] = round_out( sum_{k<K} a(i,k) * b(k,j) )   for 0 <= i < M, 0 <= j < N,
  * with a(i,k) = A[i*lda + k] and b(k,j) = B[k*ldb + j]: A is M x K and B is K x N,
  * both row-major, as in "[CUDA 优化实战] hgemm - 超越 cuBLAS" sections 0-1 (both
  * operands row-major, fp16/bf16 inputs, fp32 accumulator, results rounded to the
  * output type with round-to-nearest-even) and in the register-tiling section of
  * "CUDA GEMM 优化实践笔记" (fp32 SGEMM, same indexing).  The sum is accumulated in
- * fp32 in an order of the library's choosing.  There is no alpha, beta, bias or
- * transpose: C is overwritten.  Bytes of C outside the M x N window (the padding
- * between N and ldc) are never written.
+ * fp32 in an order of the library's choosing.  There is no transpose, and C is
+ * overwritten; the *_epilogue variants below add alpha, beta, a bias and relu.
+ * Bytes of C outside the M x N window (the padding between N and ldc) are never
+ * written.
  *
  * Conventions shared by every entry point:
  *   - A, B, C (and the fp8 scales) are DEVICE pointers owned by the caller, on the
@@ -49,7 +50,7 @@ enum gemm_status {
     GEMM_ERR_ALIAS = -5,   /* an output overlaps an input (or another output) */
     GEMM_ERR_DEVICE = -6,  /* the current device is not a gfx950 GPU, or it cannot be queried */
     GEMM_ERR_LAUNCH = -7,  /* the kernel launch was rejected by the runtime */
-    GEMM_ERR_ARG = -8      /* an option argument (input type, block size, FP8 format) is not supported */
+    GEMM_ERR_ARG = -8      /* an option (input type, block size, FP8 format, activation, alpha/beta) is not supported */
 };
 
 /* FP8 formats (OCP): E4M3 ("E4M3FN": bias 7, largest finite 448, no infinities)
@@ -58,6 +59,9 @@ enum gemm_fp8_format { GEMM_FP8_E4M3 = 0, GEMM_FP8_E5M2 = 1 };
 
 /* Element types the FP8 quantiser reads. */
 enum gemm_quant_input { GEMM_QUANT_IN_F32 = 0, GEMM_QUANT_IN_BF16 = 1 };
+
+/* Activations of the fused epilogue. */
+enum gemm_activation { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1 };
 
 /* fp16 (IEEE binary16) A, B and C; fp32 accumulation; C rounded to nearest-even.
  * "[CUDA 优化实战] hgemm - 超越 cuBLAS", sections 1-4 (the half-precision kernels). */
@@ -88,6 +92,43 @@ int gemm_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int
 int gemm_fp8_blockscaled(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N,
                          int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                          const float *scale_a, const float *scale_b, hipStream_t stream);
+
+/* Fused epilogue variants of the four GEMMs.  Same operands, layouts, checks
+ * and rules as the plain entry points above, except that every entry of the
+ * M x N window becomes
+ *   C[i*ldc + j] = round_out( act( alpha * s(i,j) + beta * c(i,j) + bias[j] ) )
+ * with s(i,j) the fp32-accumulated sum of the plain entry point, c(i,j) the
+ * value C[i*ldc + j] held before the call, and the whole expression evaluated
+ * in fp32 before the one rounding to C's type.
+ *   - A fully connected layer is a product plus one bias per output feature,
+ *     "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析" section 1.1: bias
+ *     is a device vector of N fp32 values, one per column of C (NULL: no bias).
+ *   - activation: GEMM_ACT_NONE, or GEMM_ACT_RELU = max(x, 0) applied last, the
+ *     epilogue of the vendor kernel "[CUDA 优化实战] hgemm - 超越 cuBLAS" section 5
+ *     compares against.
+ *   - alpha, beta: host fp32 scalars (the pages name neither; they are the usual
+ *     scales of the product and of the prior C).  When beta == 0, C is not read,
+ *     so it may hold anything, NaN included.
+ *   - K == 0: every sum is empty, so C becomes act(beta * c + bias[j]).
+ * Errors: GEMM_ERR_ARG for an unknown activation or a non-finite alpha or beta
+ * (checked before anything else); then those of the plain entry point; then,
+ * for a call with work to do, GEMM_ERR_ALIGN for a bias not 4-byte aligned and
+ * GEMM_ERR_ALIAS for a bias overlapping C.  The bias is read only, caller-owned
+ * and on the device. */
+int gemm_f16_epilogue(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc, float alpha, float beta,
+                      const float *bias, int activation, hipStream_t stream);
+int gemm_bf16_epilogue(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, float alpha, float beta,
+                       const float *bias, int activation, hipStream_t stream);
+int gemm_f32_epilogue(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc, float alpha, float beta,
+                      const float *bias, int activation, hipStream_t stream);
+int gemm_fp8_blockscaled_epilogue(const uint8_t *A, const uint8_t *B, void *C, int64_t M,
+                                  int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                                  const float *scale_a, const float *scale_b, float alpha,
+                                  float beta, const float *bias, int activation,
+                                  hipStream_t stream);
 
 /* Block-scaled FP8 quantiser: the step that produces gemm_fp8_blockscaled's
  * operands.  X is rows x cols, row-major with leading dimension ldx (elements),

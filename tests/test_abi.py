@@ -52,6 +52,8 @@ def test_enum_values_match_header():
     assert _enum("gemm_fp8_format") == {"GEMM_FP8_" + k.upper(): v for k, v in dg.FP8_FORMATS.items()}
     assert _enum("gemm_quant_input") == {"GEMM_QUANT_IN_" + k.upper(): v
                                          for k, v in dg.QUANT_INPUTS.items()}
+    assert _enum("gemm_activation") == {"GEMM_ACT_" + k.upper(): v
+                                        for k, v in dg.ACTIVATIONS.items()}
 
 
 # Fake, never-dereferenced device addresses: 4 KiB aligned and far apart.
@@ -107,6 +109,40 @@ def test_fp8_argument_errors():
     assert call(a=0, b=0, c=0, sa=0, sb=0, M=0) == 0
 
 
+BIAS = 0x60000000
+
+
+def epi(fn, a=A, b=B, c=C, M=64, N=64, K=64, alpha=1.0, beta=0.0, bias=BIAS, act=0, lda=None,
+        ldb=None, ldc=None, fp8=False):
+    dims = (M, N, K, K if lda is None else lda, N if ldb is None else ldb, N if ldc is None else ldc)
+    scales = (SA, SB) if fp8 else ()
+    return fn(a, b, c, *dims, *scales, alpha, beta, bias, act, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_f16_epilogue", "gemm_bf16_epilogue", "gemm_f32_epilogue",
+                                  "gemm_fp8_blockscaled_epilogue"])
+def test_epilogue_argument_errors(name):
+    fn = getattr(lib, name)
+    fp8 = "fp8" in name
+    call = lambda **kw: epi(fn, fp8=fp8, **kw)
+    out_esize = 4 if "f32" in name else 2
+    assert call(act=2) == -8
+    assert call(act=-1) == -8
+    assert call(alpha=float("nan")) == -8
+    assert call(beta=float("inf")) == -8
+    # option errors come first, even for an empty problem
+    assert call(M=0, act=7) == -8
+    # then the plain entry point's checks
+    assert call(M=-1) == -2
+    assert call(ldc=10) == -3
+    assert call(c=0) == -1
+    # then the bias: 4-byte alignment, no overlap with C
+    assert call(bias=BIAS + 2) == -4
+    assert call(bias=C + 64 * out_esize * 3) == -5
+    # empty problems: nothing checked past the options, nothing launched
+    assert call(a=0, b=0, c=0, M=0, bias=BIAS + 2) == 0
+
+
 def test_quantize_argument_errors():
     fn = lib.gemm_quantize_fp8
     X, Q, S = A, B, SA
@@ -143,6 +179,8 @@ def test_no_gpu_is_reported_as_device_error():
     # K == 0 still needs the device (it zeroes C)
     assert h16(lib.gemm_bf16, a=0, b=0, K=0, lda=0) == -6
     assert lib.gemm_quantize_fp8(A, 0, 64, 64, 64, 64, 0, B, 64, SA, None) == -6
+    assert epi(lib.gemm_bf16_epilogue) == -6
+    assert epi(lib.gemm_fp8_blockscaled_epilogue, fp8=True, K=0, lda=0) == -6
 
 
 def test_tensor_binding_validates_before_calling():
@@ -155,3 +193,12 @@ def test_tensor_binding_validates_before_calling():
         dg.gemm_f16(a, torch.zeros(3, 2, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         dg.gemm_bf16(a.t(), torch.zeros(4, 2, dtype=torch.bfloat16))
+    b2 = torch.zeros(3, 2, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):       # beta != 0 reads C, which is missing
+        dg.gemm_bf16_epilogue(a, b2, beta=1.0)
+    with pytest.raises(ValueError):       # unknown activation
+        dg.gemm_bf16_epilogue(a, b2, activation="gelu")
+    with pytest.raises(ValueError):       # bias length must be N
+        dg.gemm_bf16_epilogue(a, b2, bias=torch.zeros(3))
+    with pytest.raises(ValueError):       # bias must be float32
+        dg.gemm_bf16_epilogue(a, b2, bias=torch.zeros(2, dtype=torch.bfloat16))
