@@ -6,8 +6,10 @@ A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
 (row-major A and B, fp32 accumulation, bf16 C).  The other workloads (fp16
 4096^3, the ragged bf16 shapes, fp32 4096^3, fp8 block-scaled 8192^3, fp16
 256^3, the 4096^3 bf16 product with a fused bias + relu epilogue and with a
-fused residual add, and the FP8 block quantiser on the fp8 workload's
-8192 x 8192 operand) are measured in the same run and listed under "workloads".
+fused residual add, the MFMA-only ceiling of the headline kernel, the seven
+rungs of the optimisation ladder on fp16 4096^3, and the FP8 block quantiser on
+the fp8 workload's 8192 x 8192 operand) are measured in the same run and listed
+under "workloads".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
 
@@ -243,6 +245,44 @@ class QuantWorkload(Workload):
                 f"{r['mean_launch_us']:.1f} us/launch")
 
 
+class LadderWorkload(Workload):
+    """One rung of the optimisation ladder (gemm_h16_ladder) on the same
+    operands as the plain workload; `rung` None is the MFMA-only ceiling kernel
+    (the large-tile kernel's MFMA sequence with register-held operands, which
+    writes (K/32) * A[:, :32] * B[:32, :], not the product)."""
+
+    def __init__(self, key, name, dtype, M, N, K, wid, rung, max_steps=None):
+        super().__init__(key, name, dtype, M, N, K, wid)
+        self.rung, self.max_steps = rung, max_steps
+
+    def setup(self):
+        import torch
+
+        import dense_gemm_13_amd as dg
+        super().setup()
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        M, N, K = self.M, self.N, self.K
+        a, b, c = self.A.data_ptr(), self.B.data_ptr(), self.C.data_ptr()
+        bf = int(self.dtype == "bf16")
+        if self.rung is None:
+            fn = dg.lib.gemm_h16_mfma_ceiling
+            self.call = lambda: fn(bf, a, b, c, M, N, K, K, N, N, s)
+        else:
+            fn, r = dg.lib.gemm_h16_ladder, self.rung
+            self.call = lambda: fn(r, bf, a, b, c, M, N, K, K, N, N, s)
+        torch.cuda.synchronize()
+
+    def run(self, steps, warmup, cold_steps):
+        if self.max_steps:
+            steps, warmup, cold_steps = min(steps, self.max_steps), min(warmup, 1), 0
+        return super().run(steps, warmup, cold_steps)
+
+    def report(self, region, wall, mean, median, cold) -> dict:
+        r = super().report(region, wall, mean, median, cold)
+        r["rung"] = "mfma_only_ceiling" if self.rung is None else self.rung
+        return r
+
+
 class EpilogueWorkload(Workload):
     """A GEMM through its fused-epilogue entry point: a fully connected layer
     C = relu(A*B + bias) (alpha 1, beta 0, one fp32 bias per column), or with
@@ -294,6 +334,16 @@ WORKLOADS = [
                      "bf16", 4096, 4096, 4096, 2),
     EpilogueWorkload("bf16_4096_residual", "bf16 GEMM M=N=K=4096, fused relu(A*B + C + bias)",
                      "bf16", 4096, 4096, 4096, 2, beta=1.0),
+    LadderWorkload("bf16_4096_mfma_ceiling", "bf16 M=N=K=4096 MFMA-only ceiling (the "
+                   "large-tile kernel's MFMAs, register-held operands, no memory traffic)",
+                   "bf16", 4096, 4096, 4096, 2, None),
+] + [
+    LadderWorkload(f"ladder_{r}", f"fp16 GEMM M=N=K=4096, ladder rung {r} ({name})", "f16",
+                   4096, 4096, 4096, 2, r, max_steps=5 if r <= 2 else None)
+    for r, name in enumerate(("naive", "64x64 LDS tiles", "register tiles, conflict-free LDS",
+                              "MFMA, one LDS stage", "MFMA + double buffer",
+                              "MFMA + double buffer + swizzle", "library kernel"))
+] + [
     QuantWorkload("quant_8192", "FP8 E4M3 64x64 block quantiser, 8192x8192 fp32 N(0,1)",
                   8192, 8192, 64, "e4m3", 1005),
 ]
@@ -375,6 +425,7 @@ def main():
               file=sys.stderr, flush=True)
         del src, dst
     h = results[0]
+    ceiling = next((r for r in results if r.get("rung") == "mfma_only_ceiling"), None)
     steps = args.steps
     flops = 2 * headline.M * headline.N * headline.K
     out = {
@@ -403,6 +454,12 @@ def main():
             "traffic": measured_traffic("bf16_4096"),
         },
         "kernel_source_digest": kernel_source_digest(),
+        # the same MFMA instruction sequence with register-held operands and no
+        # memory traffic: what the matrix cores sustain on these operand values
+        "mfma_only_ceiling": None if ceiling is None else {
+            "tflops": round(ceiling["tflops"], 2),
+            "mean_launch_us": round(ceiling["mean_launch_us"], 2),
+            "headline_frac_of_ceiling": round(h["tflops"] / ceiling["tflops"], 4)},
         "workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                       for r in results],
     }

@@ -14,6 +14,8 @@ Entry points (same names as the C ABI in include/libgemm.h):
         beta=0.0, bias=None, activation="none", stream=None)
     gemm_fp8_blockscaled_epilogue(A, B, scale_a, scale_b, C=None, alpha=1.0, beta=0.0,
         bias=None, activation="none", stream=None)
+    gemm_h16_ladder(rung, A, B, C=None, stream=None)      (measurement only)
+    gemm_h16_mfma_ceiling(A, B, C=None, stream=None)      (measurement only)
 The *_epilogue calls write act(alpha * A@B + beta * C + bias[column]) (fp32,
 one rounding); C must be given when beta != 0 (its prior contents are read).
 A is M x K and B is K x N (row-major: unit column stride; the row stride is the
@@ -37,8 +39,10 @@ STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM
                 -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG"}
 ENTRY_POINTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled",
                 "gemm_f16_epilogue", "gemm_bf16_epilogue", "gemm_f32_epilogue",
-                "gemm_fp8_blockscaled_epilogue", "gemm_quantize_fp8", "gemm_status_string",
-                "gemm_version")
+                "gemm_fp8_blockscaled_epilogue", "gemm_quantize_fp8", "gemm_h16_ladder",
+                "gemm_h16_mfma_ceiling", "gemm_status_string", "gemm_version")
+LADDER_RUNGS = {"naive": 0, "lds_tiled": 1, "register_tiled": 2, "mfma": 3,
+                "mfma_double_buffer": 4, "mfma_swizzle": 5, "library": 6}   # enum gemm_ladder_rung
 ACTIVATIONS = {"none": 0, "relu": 1}          # enum gemm_activation
 FP8_FORMATS = {"e4m3": 0, "e5m2": 1}          # enum gemm_fp8_format
 QUANT_INPUTS = {"f32": 0, "bf16": 1}          # enum gemm_quant_input
@@ -78,6 +82,10 @@ def _load():
     h.gemm_quantize_fp8.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                     vp, i64, vp, vp]
     h.gemm_quantize_fp8.restype = ctypes.c_int
+    h.gemm_h16_ladder.argtypes = [ci, ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    h.gemm_h16_ladder.restype = ctypes.c_int
+    h.gemm_h16_mfma_ceiling.argtypes = [ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    h.gemm_h16_mfma_ceiling.restype = ctypes.c_int
     h.gemm_status_string.argtypes = [ctypes.c_int]
     h.gemm_status_string.restype = ctypes.c_char_p
     h.gemm_version.argtypes = []
@@ -239,6 +247,42 @@ def gemm_fp8_blockscaled_epilogue(A, B, scale_a, scale_b, C=None, alpha=1.0, bet
                 (alpha, beta, bias, activation))
 
 
+def _h16_pair(name, A, B, C):
+    torch = _torch()
+    if A.dtype not in (torch.float16, torch.bfloat16) or B.dtype != A.dtype:
+        raise TypeError(f"{name}: A and B must both be float16 or both bfloat16")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"{name}: inner dimensions differ ({K} vs {K2})")
+    if C is None:
+        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    if C.dtype != A.dtype or tuple(C.shape) != (M, N):
+        raise ValueError(f"{name}: C must be {A.dtype} of shape ({M}, {N})")
+    return M, N, K, int(A.dtype == torch.bfloat16), C
+
+
+def gemm_h16_ladder(rung, A, B, C=None, stream=None):
+    """C = A @ B by one rung of the measured optimisation ladder (a name of
+    LADDER_RUNGS or its number); float16 or bfloat16 operands."""
+    r = LADDER_RUNGS[rung] if isinstance(rung, str) else int(rung)
+    M, N, K, bf, C = _h16_pair("gemm_h16_ladder", A, B, C)
+    _check(lib.gemm_h16_ladder(r, bf, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A),
+                               _ld(B), _ld(C), _stream_handle(stream, A.device)),
+           "gemm_h16_ladder")
+    return C
+
+
+def gemm_h16_mfma_ceiling(A, B, C=None, stream=None):
+    """The large-tile kernel's MFMA sequence with register-held operands (no
+    memory traffic); writes C = (K/32) * A[:, :32] @ B[:32, :]."""
+    M, N, K, bf, C = _h16_pair("gemm_h16_mfma_ceiling", A, B, C)
+    _check(lib.gemm_h16_mfma_ceiling(bf, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                                     _ld(A), _ld(B), _ld(C), _stream_handle(stream, A.device)),
+           "gemm_h16_mfma_ceiling")
+    return C
+
+
 def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None):
     """Block-scaled FP8 quantisation of a 2-D float32 or bfloat16 tensor.
 
@@ -273,4 +317,5 @@ def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
 
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "gemm_f16_epilogue",
            "gemm_bf16_epilogue", "gemm_f32_epilogue", "gemm_fp8_blockscaled_epilogue",
-           "gemm_quantize_fp8", "status_string", "GemmError", "lib", "LIB_PATH"]
+           "gemm_quantize_fp8", "gemm_h16_ladder", "gemm_h16_mfma_ceiling", "status_string",
+           "GemmError", "lib", "LIB_PATH"]

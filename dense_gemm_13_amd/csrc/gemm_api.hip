@@ -339,6 +339,51 @@ extern "C" int gemm_fp8_blockscaled_epilogue(const uint8_t *A, const uint8_t *B,
     return fp8_entry(A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, &epi, stream);
 }
 
+extern "C" int gemm_h16_ladder(int rung, int is_bf16, const void *A, const void *B, void *C,
+                               int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                               int64_t ldc, hipStream_t stream)
+{
+    if (rung < GEMM_LADDER_NAIVE || rung > GEMM_LADDER_LIBRARY) return GEMM_ERR_ARG;
+    if (is_bf16 != 0 && is_bf16 != 1) return GEMM_ERR_ARG;
+    if (rung == GEMM_LADDER_LIBRARY)
+        return h16_entry(is_bf16 == 1, A, B, C, M, N, K, lda, ldb, ldc, nullptr, stream);
+    bool work;
+    int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 2, 2, &work);
+    if (st != GEMM_OK || !work) return st;
+    // one grid row per 16 (naive) or 64 (tiled) rows of C, at most 65535 of them
+    if (rung <= GEMM_LADDER_REGISTER_TILED && M > 65535LL * (rung == GEMM_LADDER_NAIVE ? 16 : 64))
+        return GEMM_ERR_DIM;
+    if ((st = check_device()) != GEMM_OK) return st;
+    if (K == 0)
+        return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, is_bf16 ? OUT_BF16 : OUT_F16,
+                                          nullptr, stream));
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, nullptr};
+    p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
+                ldc % 8 == 0;
+    if (rung <= GEMM_LADDER_REGISTER_TILED) return to_status(ladder_valu_launch(rung, is_bf16, p));
+    return to_status(h16_ladder_launch(rung, is_bf16, p));
+}
+
+extern "C" int gemm_h16_mfma_ceiling(int is_bf16, const void *A, const void *B, void *C,
+                                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                                     int64_t ldc, hipStream_t stream)
+{
+    if (is_bf16 != 0 && is_bf16 != 1) return GEMM_ERR_ARG;
+    bool work;
+    int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 2, 2, &work);
+    if (st != GEMM_OK || !work) return st;
+    if (M % 256 || N % 256 || K % 32) return GEMM_ERR_DIM;
+    Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, nullptr};
+    p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 8 == 0 && ldb % 8 == 0 &&
+                ldc % 8 == 0;
+    if (!p.aligned) return GEMM_ERR_ALIGN;
+    if ((st = check_device()) != GEMM_OK) return st;
+    if (K == 0)
+        return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, is_bf16 ? OUT_BF16 : OUT_F16,
+                                          nullptr, stream));
+    return to_status(mfma_ceiling_launch(is_bf16, p));
+}
+
 extern "C" int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols,
                                  int64_t ldx, int block, int fmt, uint8_t *Q, int64_t ldq,
                                  float *scales, hipStream_t stream)

@@ -51,7 +51,12 @@ __device__ __forceinline__ u32x4 load8_guarded(const uint16_t *p, bool row_ok, i
 
 // EPI: the fused epilogue is applied to the fp32 results before rounding, by
 // the lane that stores them.
-template <bool IS_BF16, int BM, int BN, int WM, int WN, bool ALIGNED, bool EPI>
+// DBUF, SWZ (both on for the library's own calls) switch off the two-stage LDS
+// ring and the XOR swizzle, for the measured optimisation ladder: without DBUF
+// each K step loads, stores to LDS, synchronises and multiplies in turn; without
+// SWZ the 16-byte chunks sit in LDS in their natural order.
+template <bool IS_BF16, int BM, int BN, int WM, int WN, bool ALIGNED, bool EPI, bool DBUF = true,
+          bool SWZ = true>
 __global__ void __launch_bounds__(WM * WN * 64)
 h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
@@ -68,8 +73,9 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(A_ITERS >= 1 && A_ITERS * NT == BM * (BK / 8), "A loader");
     static_assert(BR != 0 && B_ITERS >= 1, "B loader");
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t As[DBUF ? 2 : 1][BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[DBUF ? 2 : 1][BN * BK];
+    auto swz8 = [](int row) { return SWZ ? gemm::swz8(row) : 0; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -181,15 +187,25 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
 
     const int ktiles = (K + BK - 1) / BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int t = 0; t < ktiles; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < ktiles) load_tile((t + 1) * BK);
-        compute(cur);
-        if (t + 1 < ktiles) store_tile(cur ^ 1);
+    if constexpr (DBUF) {
+        load_tile(0);
+        store_tile(0);
         __syncthreads();
+        for (int t = 0; t < ktiles; ++t) {
+            const int cur = t & 1;
+            if (t + 1 < ktiles) load_tile((t + 1) * BK);
+            compute(cur);
+            if (t + 1 < ktiles) store_tile(cur ^ 1);
+            __syncthreads();
+        }
+    } else {
+        for (int t = 0; t < ktiles; ++t) {
+            load_tile(t * BK);
+            store_tile(0);
+            __syncthreads();
+            compute(0);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: lane holds C[m][n..n+3] for n = 8g + 4*half (+ tile offsets)
@@ -265,7 +281,51 @@ hipError_t launch_typed(int config, const Problem &p)
     }
 }
 
+// Rungs of the measured optimisation ladder that use this kernel: 128 x 128
+// tiles of 4 waves, MFMA; rung 3 plain LDS, one stage; rung 4 with the two-stage
+// ring; rung 5 with the ring and the swizzle (the library's own 128 x 128 kernel).
+template <bool IS_BF16>
+hipError_t ladder_typed(int rung, const Problem &p)
+{
+    constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int64_t nwg = (int64_t)tiles_m * tiles_n;
+    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    const int group_m = tiles_m < 4 ? tiles_m : 4;
+    const dim3 grid((unsigned)nwg), block(WM * WN * 64);
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+    uint16_t *C = static_cast<uint16_t *>(p.C);
+    const Epilogue none{1.f, 0.f, nullptr, 0};
+#define LADDER_LAUNCH(AL, DB, SW)                                                                  \
+    hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, AL, false, DB, SW>), grid, block, \
+                       0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, \
+                       group_m, none)
+    switch (rung) {
+    case 3:
+        if (p.aligned) LADDER_LAUNCH(true, false, false);
+        else LADDER_LAUNCH(false, false, false);
+        break;
+    case 4:
+        if (p.aligned) LADDER_LAUNCH(true, true, false);
+        else LADDER_LAUNCH(false, true, false);
+        break;
+    case 5:
+        if (p.aligned) LADDER_LAUNCH(true, true, true);
+        else LADDER_LAUNCH(false, true, true);
+        break;
+    default: return hipErrorInvalidValue;
+    }
+#undef LADDER_LAUNCH
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t h16_ladder_launch(int rung, bool is_bf16, const Problem &p)
+{
+    return is_bf16 ? ladder_typed<true>(rung, p) : ladder_typed<false>(rung, p);
+}
 
 // Largest tile that still gives the chip at least half a workgroup per CU.
 int h16_pick_config(int M, int N, int K)

@@ -53,6 +53,13 @@ bool h16_narrow_eligible(const Problem &p);
 hipError_t h16_narrow_launch(bool is_bf16, const Problem &p);
 bool h16_narrow_general_eligible(const Problem &p);
 hipError_t h16_narrow_general_launch(bool is_bf16, const Problem &p);
+// The measured optimisation ladder (fp16 or bf16): rungs 0-2 on the vector
+// ALUs, rungs 3-5 the 128 x 128 MFMA kernel with its ring / swizzle switched,
+// and the MFMA-only ceiling of the large-tile kernel.
+hipError_t ladder_valu_launch(int rung, bool is_bf16, const Problem &p);
+hipError_t h16_ladder_launch(int rung, bool is_bf16, const Problem &p);
+bool mfma_ceiling_eligible(const Problem &p);
+hipError_t mfma_ceiling_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p);
 bool f32_fast_eligible(const Problem &p);
 hipError_t f32_fast_launch(const Problem &p);

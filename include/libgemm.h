@@ -155,6 +155,51 @@ int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols, in
                       int block, int fmt, uint8_t *Q, int64_t ldq, float *scales,
                       hipStream_t stream);
 
+/* Rungs of the measured optimisation ladder (gemm_h16_ladder). */
+enum gemm_ladder_rung {
+    GEMM_LADDER_NAIVE = 0,           /* one thread per entry, operands from global memory */
+    GEMM_LADDER_LDS_TILED = 1,       /* 64 x 64 tiles staged in LDS, operands read from LDS */
+    GEMM_LADDER_REGISTER_TILED = 2,  /* + 4 x 4 outputs per thread from register-held fragments,
+                                        bank-conflict-free LDS layout */
+    GEMM_LADDER_MFMA = 3,            /* matrix cores: 128 x 128 tiles, 4 waves, one LDS stage */
+    GEMM_LADDER_MFMA_DOUBLE_BUFFER = 4,  /* + two-stage LDS ring (loads overlap the MFMAs) */
+    GEMM_LADDER_MFMA_SWIZZLE = 5,    /* + XOR-swizzled 16-byte LDS chunks */
+    GEMM_LADDER_LIBRARY = 6          /* the library's own dispatch (gemm_f16 / gemm_bf16) */
+};
+
+/* The optimisation ladder, for measurement: the same product as gemm_f16
+ * (is_bf16 = 0) or gemm_bf16 (is_bf16 = 1), computed by the kernel of one rung
+ * of "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析" section 5.3 (plain
+ * triple loop; 64 x 64 shared-memory tiles; register caching with bank
+ * conflicts avoided; matrix-core instructions; double buffering; swizzled
+ * layout), with the kernel design of sections 3.1-3.2 for the tiled rungs and
+ * the last steps of "[CUDA 优化实战] hgemm - 超越 cuBLAS" for the top rung (the
+ * library's LDS-direct, coalesced-store kernel).  Rungs 0-2 run on the vector
+ * ALUs (fp32 FMAs, k ascending); rungs 3-6 on the matrix cores.  Every rung
+ * takes every shape and layout gemm_f16 takes, except that rungs 0-2 allow at
+ * most 65535 grid rows (M <= 1048560 for rung 0, M <= 4194240 for rungs 1-2;
+ * else GEMM_ERR_DIM).  Same checks, errors and ownership as gemm_f16; an
+ * unknown rung or is_bf16 gives GEMM_ERR_ARG. */
+int gemm_h16_ladder(int rung, int is_bf16, const void *A, const void *B, void *C, int64_t M,
+                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                    hipStream_t stream);
+
+/* MFMA-only ceiling of the large-tile fp16 (is_bf16 = 0) or bf16 kernel, for
+ * measurement: one workgroup of 4 waves per 256 x 256 tile issues exactly that
+ * kernel's matrix-core instructions for an M x N x K product (K/16 steps of 16
+ * v_mfma_f32_32x32x16 per wave, in the same order) on operand fragments loaded
+ * once from A[:, 0:32] and B[0:32, :] and held in registers, alternating the
+ * k = 0..15 and k = 16..31 halves step by step, with no memory traffic in the
+ * loop.  Its time is what the matrix cores sustain on these operand values at
+ * the clock the chip holds under that load.  It writes
+ *   C = round( (K/32) * A[:, 0:32] * B[0:32, :] )    (fp32 accumulation),
+ * needs M and N multiples of 256, K a multiple of 32 (else GEMM_ERR_DIM) and
+ * 16-byte aligned A, B, C with leading dimensions multiples of 8 (else
+ * GEMM_ERR_ALIGN).  Otherwise as gemm_f16. */
+int gemm_h16_mfma_ceiling(int is_bf16, const void *A, const void *B, void *C, int64_t M,
+                          int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                          hipStream_t stream);
+
 /* Static, NUL-terminated description of a gemm_status value. */
 const char *gemm_status_string(int status);
 

@@ -54,6 +54,8 @@ def test_enum_values_match_header():
                                          for k, v in dg.QUANT_INPUTS.items()}
     assert _enum("gemm_activation") == {"GEMM_ACT_" + k.upper(): v
                                         for k, v in dg.ACTIVATIONS.items()}
+    assert _enum("gemm_ladder_rung") == {"GEMM_LADDER_" + k.upper(): v
+                                         for k, v in dg.LADDER_RUNGS.items()}
 
 
 # Fake, never-dereferenced device addresses: 4 KiB aligned and far apart.
@@ -141,6 +143,32 @@ def test_epilogue_argument_errors(name):
     assert call(bias=C + 64 * out_esize * 3) == -5
     # empty problems: nothing checked past the options, nothing launched
     assert call(a=0, b=0, c=0, M=0, bias=BIAS + 2) == 0
+
+
+def test_ladder_and_ceiling_argument_errors():
+    lad, ceil = lib.gemm_h16_ladder, lib.gemm_h16_mfma_ceiling
+
+    def L(rung=0, bf=0, M=64, N=64, K=64, a=A, c=C, lda=None):
+        return lad(rung, bf, a, B, c, M, N, K, K if lda is None else lda, N, N, None)
+
+    assert L(rung=-1) == -8
+    assert L(rung=7) == -8
+    assert L(bf=2) == -8
+    assert L(M=-1) == -2
+    assert L(lda=3) == -3
+    assert L(c=0) == -1
+    assert L(M=65535 * 16 + 1) == -2                # naive: too many grid rows
+    assert L(rung=1, M=65535 * 64 + 1) == -2
+    assert L(M=0, a=0, c=0) == 0
+
+    def Q(bf=0, M=256, N=256, K=64, a=A):
+        return ceil(bf, a, B, C, M, N, K, K, N, N, None)
+
+    assert Q(bf=5) == -8
+    assert Q(M=100) == -2
+    assert Q(K=48) == -2
+    assert Q(a=A + 2) == -4
+    assert Q(M=0) == 0
 
 
 def test_quantize_argument_errors():
