@@ -18,7 +18,11 @@ module only marshals numpy arrays into it.  What it follows:
 * the same article, section 1.1 (a fully connected layer is a product plus a
   bias per output feature), and the relu epilogue of the vendor kernel in
   "[CUDA 优化实战] hgemm - 超越 cuBLAS" section 5: ``epilogue`` applies
-  out = act(alpha * prod + beta * C_prior + bias[column]) to the exact product.
+  out = act(alpha * prod + beta * C_prior + bias[column]) to the exact product;
+* the same article, section 1.1 (a convolution becomes a GEMM through im2col):
+  ``conv2d_nhwc`` computes the convolution by its definition (NHWC input, HWIO
+  weights, zero padding, stride, dilation), and ``im2col_nhwc`` builds the
+  im2col matrix, for bit-exact checks of a packing kernel.
 
 ``gemm`` returns the exact sum (fp64, k ascending, never rounded to the
 output type).  ``within_tolerance`` is the element-wise acceptance test
@@ -78,6 +82,12 @@ def bind(lib):
     lib.orc_epilogue.argtypes = [ctypes.c_int, vp, i64, i64, ctypes.c_double, ctypes.c_double,
                                  vp, i64, vp, ctypes.c_int, vp]
     lib.orc_epilogue.restype = ctypes.c_int
+    lib.orc_conv2d_output_size.argtypes = [vp, vp, vp]
+    lib.orc_conv2d_output_size.restype = ctypes.c_int
+    lib.orc_conv2d_nhwc.argtypes = [ctypes.c_int, vp, vp, vp, vp]
+    lib.orc_conv2d_nhwc.restype = ctypes.c_int
+    lib.orc_im2col_nhwc.argtypes = [ctypes.c_int, vp, vp, vp, i64]
+    lib.orc_im2col_nhwc.restype = ctypes.c_int
     return lib
 
 
@@ -247,4 +257,56 @@ def epilogue(out_dtype: str, prod: np.ndarray, alpha: float = 1.0, beta: float =
                           _ptr(b), ACTIVATIONS[act], out.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"orc_epilogue failed ({rc})")
+    return out
+
+
+CONV_KEYS = ("n", "h", "w", "c_in", "c_out", "kh", "kw", "stride_h", "stride_w", "pad_h",
+             "pad_w", "dil_h", "dil_w")
+
+
+def conv_geom(**kw) -> np.ndarray:
+    """The 13 convolution sizes in the oracle's order (stride, dilation default 1,
+    padding 0)."""
+    d = {"stride_h": 1, "stride_w": 1, "pad_h": 0, "pad_w": 0, "dil_h": 1, "dil_w": 1}
+    d.update(kw)
+    return np.array([d[k] for k in CONV_KEYS], dtype=np.int64)
+
+
+def conv2d_output_size(geom: np.ndarray):
+    lib = _load()
+    g = np.ascontiguousarray(geom, dtype=np.int64)
+    ho, wo = ctypes.c_int64(), ctypes.c_int64()
+    if lib.orc_conv2d_output_size(g.ctypes.data, ctypes.addressof(ho), ctypes.addressof(wo)) != 0:
+        raise ValueError("bad convolution geometry")
+    return ho.value, wo.value
+
+
+def conv2d_nhwc(dtype: str, X: np.ndarray, Wt: np.ndarray, geom: np.ndarray) -> np.ndarray:
+    """Exact (fp64) NHWC convolution of raw X (n*h*w x c_in bits, any shape with
+    that many elements) by raw HWIO weights; returns (n, Ho, Wo, c_out) float64."""
+    lib = _load()
+    g = np.ascontiguousarray(geom, dtype=np.int64)
+    ho, wo = conv2d_output_size(g)
+    n, h, w, ci, co, kh, kw = (int(v) for v in g[:7])
+    X = np.ascontiguousarray(_raw(np.ascontiguousarray(X).reshape(n * h * w, ci), dtype))
+    Wt = np.ascontiguousarray(_raw(np.ascontiguousarray(Wt).reshape(kh * kw * ci, co), dtype))
+    out = np.empty((n, ho, wo, co), dtype=np.float64)
+    if lib.orc_conv2d_nhwc(DTYPES[dtype], X.ctypes.data, Wt.ctypes.data, g.ctypes.data,
+                           out.ctypes.data) != 0:
+        raise RuntimeError("orc_conv2d_nhwc failed")
+    return out
+
+
+def im2col_nhwc(X: np.ndarray, geom: np.ndarray) -> np.ndarray:
+    """The im2col matrix of an NHWC tensor (raw uint16 or float32/uint32 bits):
+    (n*Ho*Wo) x (kh*kw*c_in), same element type as X."""
+    lib = _load()
+    g = np.ascontiguousarray(geom, dtype=np.int64)
+    ho, wo = conv2d_output_size(g)
+    n, kh, kw, ci = int(g[0]), int(g[5]), int(g[6]), int(g[3])
+    X = np.ascontiguousarray(X)
+    out = np.empty((n * ho * wo, kh * kw * ci), dtype=X.dtype)
+    if lib.orc_im2col_nhwc(X.itemsize, X.ctypes.data, g.ctypes.data, out.ctypes.data,
+                           max(kh * kw * ci, 1)) != 0:
+        raise RuntimeError("orc_im2col_nhwc failed")
     return out

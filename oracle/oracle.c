@@ -401,3 +401,101 @@ int orc_epilogue(int out_dtype, const double *prod, int64_t M, int64_t N, double
         }
     return 0;
 }
+
+/* ------------------------------------------------- convolution (direct) */
+
+/* "深度学习加速核心：GEMM优化从分块到TensorCore的实战解析" section 1.1: a
+ * convolution is a GEMM once every output position's receptive field is laid
+ * out as one row of a large matrix (im2col).  The oracle computes the
+ * convolution itself, by its definition, not through that matrix:
+ *   Y[n][oh][ow][co] = sum over kh < KH, kw < KW, ci < C_in of
+ *                      X[n][oh*sh - ph + kh*dh][ow*sw - pw + kw*dw][ci] * Wt[kh][kw][ci][co]
+ * with X read as 0 outside the H x W image (zero padding).  Layouts (the pages
+ * fix none; channels-last is the plain reading for a GEMM whose rows are output
+ * positions): X is NHWC, Wt is KH x KW x C_in x C_out ("HWIO"), Y is NHWC,
+ * all dense.  Output size: Ho = (H + 2 ph - dh (KH-1) - 1) / sh + 1 (floor),
+ * likewise Wo.  geom = {n, h, w, c_in, c_out, kh, kw, sh, sw, ph, pw, dh, dw}.
+ * The sum runs over (kh, kw, ci) in that nesting, ascending, in fp64.
+ * dtype: ORC_F16, ORC_BF16 or ORC_F32 for X and Wt.  out: n*Ho*Wo*C_out. */
+static int conv_geometry(const int64_t *g, int64_t *ho, int64_t *wo)
+{
+    for (int i = 0; i < 13; i++)
+        if (g[i] < 0) return -1;
+    if (g[5] < 1 || g[6] < 1 || g[7] < 1 || g[8] < 1 || g[11] < 1 || g[12] < 1) return -1;
+    const int64_t eh = g[1] + 2 * g[9] - g[11] * (g[5] - 1) - 1;
+    const int64_t ew = g[2] + 2 * g[10] - g[12] * (g[6] - 1) - 1;
+    *ho = eh < 0 ? 0 : eh / g[7] + 1;
+    *wo = ew < 0 ? 0 : ew / g[8] + 1;
+    return 0;
+}
+
+int orc_conv2d_output_size(const int64_t *geom, int64_t *ho, int64_t *wo)
+{
+    return conv_geometry(geom, ho, wo);
+}
+
+int orc_conv2d_nhwc(int dtype, const void *X, const void *Wt, const int64_t *geom, double *out)
+{
+    int64_t ho, wo;
+    if (conv_geometry(geom, &ho, &wo) != 0) return -1;
+    if (dtype != ORC_F16 && dtype != ORC_BF16 && dtype != ORC_F32) return -1;
+    const int64_t N = geom[0], H = geom[1], W = geom[2], CI = geom[3], CO = geom[4];
+    const int64_t KH = geom[5], KW = geom[6], SH = geom[7], SW = geom[8];
+    const int64_t PH = geom[9], PW = geom[10], DH = geom[11], DW = geom[12];
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t oh = 0; oh < ho; oh++)
+            for (int64_t ow = 0; ow < wo; ow++)
+                for (int64_t co = 0; co < CO; co++) {
+                    double acc = 0.0;
+                    for (int64_t kh = 0; kh < KH; kh++) {
+                        const int64_t ih = oh * SH - PH + kh * DH;
+                        for (int64_t kw = 0; kw < KW; kw++) {
+                            const int64_t iw = ow * SW - PW + kw * DW;
+                            for (int64_t ci = 0; ci < CI; ci++) {
+                                double x = 0.0;
+                                if (ih >= 0 && ih < H && iw >= 0 && iw < W)
+                                    x = operand_at(dtype, X, CI, (n * H + ih) * W + iw, ci, NULL, 0);
+                                const double wv =
+                                    operand_at(dtype, Wt, CO, (kh * KW + kw) * CI + ci, co, NULL, 0);
+                                acc = acc + x * wv;
+                            }
+                        }
+                    }
+                    out[((n * ho + oh) * wo + ow) * CO + co] = acc;
+                }
+    return 0;
+}
+
+/* The im2col matrix itself (raw element bits, esize 2 or 4 bytes): row
+ * (n, oh, ow), column (kh, kw, ci), i.e.
+ *   col[((n*Ho + oh)*Wo + ow) * ldcol + (kh*KW + kw)*C_in + ci]
+ *     = X[n][oh*sh - ph + kh*dh][ow*sw - pw + kw*dw][ci], or 0 outside the image.
+ * The convolution is then col (M x K) times Wt seen as (KH*KW*C_in) x C_out. */
+int orc_im2col_nhwc(int esize, const void *X, const int64_t *geom, void *col, int64_t ldcol)
+{
+    int64_t ho, wo;
+    if (conv_geometry(geom, &ho, &wo) != 0 || (esize != 2 && esize != 4)) return -1;
+    const int64_t N = geom[0], H = geom[1], W = geom[2], CI = geom[3];
+    const int64_t KH = geom[5], KW = geom[6], SH = geom[7], SW = geom[8];
+    const int64_t PH = geom[9], PW = geom[10], DH = geom[11], DW = geom[12];
+    if (ldcol < KH * KW * CI) return -1;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t oh = 0; oh < ho; oh++)
+            for (int64_t ow = 0; ow < wo; ow++) {
+                const int64_t row = (n * ho + oh) * wo + ow;
+                for (int64_t kh = 0; kh < KH; kh++)
+                    for (int64_t kw = 0; kw < KW; kw++) {
+                        const int64_t ih = oh * SH - PH + kh * DH, iw = ow * SW - PW + kw * DW;
+                        const int inside = ih >= 0 && ih < H && iw >= 0 && iw < W;
+                        for (int64_t ci = 0; ci < CI; ci++) {
+                            const int64_t dst = row * ldcol + (kh * KW + kw) * CI + ci;
+                            const int64_t src = ((n * H + ih) * W + iw) * CI + ci;
+                            if (esize == 2)
+                                ((uint16_t *)col)[dst] = inside ? ((const uint16_t *)X)[src] : 0;
+                            else
+                                ((uint32_t *)col)[dst] = inside ? ((const uint32_t *)X)[src] : 0;
+                        }
+                    }
+            }
+    return 0;
+}

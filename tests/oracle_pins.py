@@ -15,7 +15,9 @@ Independent sources used here:
   power-of-two block patterns and the independent input recipe in gemm_inputs;
 * for the fused epilogue: hand-derived closed forms on all-ones products with a
   per-column bias, a row- and column-dependent prior C in a NaN-padded buffer,
-  relu thresholds and a NaN-filled prior that beta = 0 must leave unread.
+  relu thresholds and a NaN-filled prior that beta = 0 must leave unread;
+* for the convolution and im2col: torch's float64 conv2d and unfold, delta and
+  shift kernels, tap counts of an all-ones input, and the 1x1 case = the GEMM.
 """
 from __future__ import annotations
 
@@ -503,8 +505,107 @@ def pin_epilogue(orc) -> list:
     return fails
 
 
+# ------------------------------------------------------------ convolution
+
+CONV_CASES = [
+    # n, h, w, c_in, c_out, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w
+    dict(n=2, h=7, w=6, c_in=3, c_out=5, kh=3, kw=3, pad_h=1, pad_w=1),
+    dict(n=1, h=9, w=11, c_in=4, c_out=2, kh=3, kw=2, stride_h=2, stride_w=3, pad_h=2, pad_w=0),
+    dict(n=3, h=8, w=8, c_in=2, c_out=3, kh=2, kw=3, dil_h=2, dil_w=3, pad_h=1, pad_w=2),
+    dict(n=1, h=5, w=4, c_in=6, c_out=4, kh=1, kw=1),
+    dict(n=2, h=10, w=7, c_in=3, c_out=2, kh=7, kw=5, stride_h=2, stride_w=2, pad_h=3, pad_w=2),
+]
+
+
+def _torch_conv(xv, wv, g):
+    """torch's float64 CPU conv2d on decoded NHWC / HWIO values (the library
+    routine the oracle's convolution must agree with)."""
+    n, h, w, ci, co, kh, kw, sh, sw, ph, pw, dh, dw = (int(v) for v in g)
+    x = torch.from_numpy(xv.reshape(n, h, w, ci)).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(wv.reshape(kh, kw, ci, co)).permute(3, 2, 0, 1)
+    y = torch.nn.functional.conv2d(x, wt, stride=(sh, sw), padding=(ph, pw), dilation=(dh, dw))
+    return y.permute(0, 2, 3, 1).numpy()
+
+
+def pin_conv(orc) -> list:
+    """The direct convolution against torch's conv2d (float64, CPU) on random
+    operands of every type over strides, paddings and dilations; closed forms:
+    a centred delta kernel returns the input, a corner delta kernel shifts it
+    by the padding, all-ones counts the taps inside the image, and a 1x1
+    convolution is exactly the GEMM of the pixels by the weights."""
+    fails = []
+    for ci_, case in enumerate(CONV_CASES):
+        g = orc.conv_geom(**case)
+        n, h, w, ci, co, kh, kw = (int(v) for v in g[:7])
+        for dtype in ("f16", "bf16", "f32"):
+            X = random_operand(n * h * w, ci, dtype, 300 + ci_)[0]
+            W = random_operand(kh * kw * ci, co, dtype, 400 + ci_)[0]
+            got = orc.conv2d_nhwc(dtype, X, W, g)
+            want = _torch_conv(lib_decode(X, dtype), lib_decode(W, dtype), g)
+            if got.shape != want.shape or not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+                fails.append(f"conv {dtype} {case}: differs from torch conv2d")
+    # closed forms (f32 operands; all values exact)
+    n, h, w, c = 2, 5, 6, 3
+    X = random_operand(n * h * w, c, "f32", 500)[0]
+    xv = X.reshape(n, h, w, c).astype(np.float64)
+    delta = np.zeros((3, 3, c, c), np.float32)
+    delta[1, 1] = np.eye(c)
+    y = orc.conv2d_nhwc("f32", X, delta, orc.conv_geom(n=n, h=h, w=w, c_in=c, c_out=c, kh=3,
+                                                       kw=3, pad_h=1, pad_w=1))
+    if not np.array_equal(y, xv):
+        fails.append("conv: centred delta kernel does not return the input")
+    corner = np.zeros((3, 3, c, c), np.float32)
+    corner[0, 0] = np.eye(c)
+    y = orc.conv2d_nhwc("f32", X, corner, orc.conv_geom(n=n, h=h, w=w, c_in=c, c_out=c, kh=3,
+                                                        kw=3, pad_h=1, pad_w=1))
+    shifted = np.zeros_like(xv)
+    shifted[:, 1:, 1:, :] = xv[:, :-1, :-1, :]          # Y[oh][ow] = X[oh-1][ow-1]
+    if not np.array_equal(y, shifted):
+        fails.append("conv: corner delta kernel is not a shift by the padding")
+    ones = orc.conv2d_nhwc("f32", np.ones((n * h * w, c), np.float32),
+                           np.ones((3, 3, c, 2), np.float32),
+                           orc.conv_geom(n=n, h=h, w=w, c_in=c, c_out=2, kh=3, kw=3, pad_h=1,
+                                         pad_w=1))
+    rows_in = np.array([2] + [3] * (h - 2) + [2])       # taps inside along each axis
+    cols_in = np.array([2] + [3] * (w - 2) + [2])
+    want = (rows_in[:, None] * cols_in[None, :] * c).astype(np.float64)
+    if not all(np.array_equal(ones[b, :, :, o], want) for b in range(n) for o in range(2)):
+        fails.append("conv: all-ones does not count the taps inside the image")
+    W1 = random_operand(c, 4, "f32", 501)[0]
+    y = orc.conv2d_nhwc("f32", X, W1, orc.conv_geom(n=n, h=h, w=w, c_in=c, c_out=4, kh=1, kw=1))
+    if not np.array_equal(y.reshape(n * h * w, 4), orc.gemm("f32", X, W1, n * h * w, 4, c)):
+        fails.append("conv: 1x1 convolution differs from the GEMM")
+    return fails
+
+
+def pin_im2col(orc) -> list:
+    """The im2col matrix against torch's unfold (pure data movement, so exact),
+    reordered from unfold's (channel, kh, kw) columns to (kh, kw, channel), and
+    the 1x1 / stride 1 / no padding case, where it is the input itself."""
+    fails = []
+    for ci_, case in enumerate(CONV_CASES):
+        g = orc.conv_geom(**case)
+        n, h, w, ci, co, kh, kw, sh, sw, ph, pw, dh, dw = (int(v) for v in g)
+        for dtype in ("bf16", "f32"):
+            X = random_operand(n * h * w, ci, dtype, 600 + ci_)[0]
+            got = orc.im2col_nhwc(X, g)
+            x = torch.from_numpy(lib_decode(X, dtype).reshape(n, h, w, ci)).permute(0, 3, 1, 2)
+            u = torch.nn.functional.unfold(x, (kh, kw), dilation=(dh, dw), padding=(ph, pw),
+                                           stride=(sh, sw))            # (n, ci*kh*kw, L)
+            L = u.shape[2]
+            u = u.reshape(n, ci, kh, kw, L).permute(0, 4, 2, 3, 1).reshape(n * L, kh * kw * ci)
+            if got.shape != tuple(u.shape) or not np.array_equal(lib_decode(got, dtype), u.numpy()):
+                fails.append(f"im2col {dtype} {case}: differs from torch unfold")
+    X = random_operand(30, 5, "bf16", 610)[0]
+    if not np.array_equal(orc.im2col_nhwc(X, orc.conv_geom(n=2, h=3, w=5, c_in=5, c_out=1,
+                                                           kh=1, kw=1)), X):
+        fails.append("im2col: 1x1 case is not the input")
+    return fails
+
+
 ALL_PINS = (pin_decoders, pin_closed_forms, pin_bruteforce, pin_scale_blocks, pin_entries,
-            pin_tolerance_checker, pin_fp8_encode, pin_quantize_fp8, pin_epilogue)
+            pin_tolerance_checker, pin_fp8_encode, pin_quantize_fp8, pin_epilogue,
+            pin_conv, pin_im2col)
 
 
 def run_all(orc) -> list:

@@ -50,6 +50,14 @@ def test_epilogue(orc):
     assert pins.pin_epilogue(orc) == []
 
 
+def test_conv(orc):
+    assert pins.pin_conv(orc) == []
+
+
+def test_im2col(orc):
+    assert pins.pin_im2col(orc) == []
+
+
 def test_thread_count_does_not_change_result(orc):
     import gemm_inputs as gi
     A = gi.uniform_h16(67, 45, 1, "bf16")
@@ -121,6 +129,20 @@ MUTANTS = {
                 memcpy(&bbits, &bias[j], 4);
                 v = v + orc_f32_to_f64(bbits);
             }"""),
+    # convolution and im2col
+    "conv_dilation_ignored": ("const int64_t ih = oh * SH - PH + kh * DH;",
+                              "const int64_t ih = oh * SH - PH + kh;"),
+    "conv_stride_ignored": ("const int64_t iw = ow * SW - PW + kw * DW;",
+                            "const int64_t iw = ow - PW + kw * DW;"),
+    "conv_padding_sign": ("const int64_t ih = oh * SH - PH + kh * DH;",
+                          "const int64_t ih = oh * SH + PH + kh * DH;"),
+    "conv_weight_taps_swapped": ("Wt, CO, (kh * KW + kw) * CI + ci", "Wt, CO, (kw * KH + kh) * CI + ci"),
+    "conv_no_zero_padding": ("if (ih >= 0 && ih < H && iw >= 0 && iw < W)\n",
+                             "if (ih >= 0 && iw >= 0 && (n * H + ih) * W + iw < N * H * W)\n"),
+    "conv_output_size_floor": ("*ho = eh < 0 ? 0 : eh / g[7] + 1;", "*ho = eh < 0 ? 0 : (eh + g[7] - 1) / g[7] + 1;"),
+    "im2col_channel_major": ("row * ldcol + (kh * KW + kw) * CI + ci;",
+                             "row * ldcol + (ci * KH + kh) * KW + kw;"),
+    "im2col_no_zero_fill": ("inside ? ((const uint16_t *)X)[src] : 0", "((const uint16_t *)X)[src < 0 ? 0 : src]"),
 }
 
 _RUNNER = r"""
