@@ -7,7 +7,8 @@ A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
 4096^3, the ragged bf16 shapes, fp32 4096^3, fp8 block-scaled 8192^3, fp16
 256^3, the 4096^3 bf16 product with a fused bias + relu epilogue and with a
 fused residual add, the MFMA-only ceiling of the headline kernel, the seven
-rungs of the optimisation ladder on fp16 4096^3, and the FP8 block quantiser on
+rungs of the optimisation ladder on fp16 4096^3, two 3x3 convolution layers
+through im2col + GEMM and the im2col pack alone, and the FP8 block quantiser on
 the fp8 workload's 8192 x 8192 operand) are measured in the same run and listed
 under "workloads".
 
@@ -283,6 +284,71 @@ class LadderWorkload(Workload):
         return r
 
 
+class ConvWorkload(Workload):
+    """A 3x3 convolution layer (NHWC, HWIO weights, padding 1, bias + relu) through
+    gemm_conv2d_nhwc: the im2col pack into a preallocated workspace, then the
+    GEMM (n*ho*wo) x (9*c_in) x c_out.  TFLOP/s counts the convolution's
+    2 * n*ho*wo * 9*c_in * c_out flops; with `pack_only` the line times the
+    im2col kernel alone and reports its GB/s (input read once, matrix written)."""
+
+    def __init__(self, key, name, n, hw, c_in, c_out, wid, pack_only=False):
+        M = n * hw * hw
+        super().__init__(key, name, "bf16", M, c_out, 9 * c_in, wid)
+        self.n, self.hw, self.c_in, self.c_out, self.pack_only = n, hw, c_in, c_out, pack_only
+
+    def setup(self):
+        import numpy as np
+        import torch
+
+        import dense_gemm_13_amd as dg
+        import gemm_inputs as gi
+        dev = torch.device("cuda:0")
+        n, hw, ci, co = self.n, self.hw, self.c_in, self.c_out
+        as_bf16 = lambda b, shape: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16) \
+            .reshape(shape).to(dev)
+        self.A = as_bf16(gi.uniform_h16(n * hw * hw, ci, 1000 + self.wid, "bf16"), (n, hw, hw, ci))
+        self.B = as_bf16(gi.uniform_h16(9 * ci, co, 2000 + self.wid, "bf16"), (3, 3, ci, co))
+        self.bias = torch.from_numpy(gi.uniform_f32(1, co, 7000 + self.wid)[0]).to(dev)
+        self.C = torch.empty((n, hw, hw, co), dtype=torch.bfloat16, device=dev)
+        shape = dg.Conv2dShape(n, hw, hw, ci, co, 3, 3, 1, 1, 1, 1, 1, 1)
+        self.shape = shape
+        need = dg.lib.gemm_conv2d_workspace_bytes(dg.DTYPES["bf16"], ctypes.byref(shape))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        s = ctypes.c_void_p(self.stream.cuda_stream)
+        x, w, y, ws, b = (self.A.data_ptr(), self.B.data_ptr(), self.C.data_ptr(),
+                          self.ws.data_ptr(), self.bias.data_ptr())
+        sp = ctypes.byref(shape)
+        relu = dg.ACTIVATIONS["relu"]
+        if self.pack_only:
+            fn = dg.lib.gemm_im2col_nhwc
+            self.call = lambda: fn(dg.DTYPES["bf16"], x, ws, 9 * ci, sp, s)
+        else:
+            fn = dg.lib.gemm_conv2d_nhwc
+            self.call = lambda: fn(dg.DTYPES["bf16"], x, w, y, ws, need, sp, b, relu, s)
+        torch.cuda.synchronize()
+
+    def report(self, region, wall, mean, median, cold) -> dict:
+        r = super().report(region, wall, mean, median, cold)
+        n, hw, ci, co = self.n, self.hw, self.c_in, self.c_out
+        r.update({"conv": f"{n}x{hw}x{hw}x{ci} -> {co}, 3x3, pad 1, stride 1, bias + relu",
+                  "gemm": f"{self.M} x {co} x {9 * ci}"})
+        pack_bytes = 2 * n * hw * hw * ci + 2 * self.M * 9 * ci
+        if self.pack_only:
+            r["alg_gbs"] = pack_bytes / mean / 1e9
+            r["pct_hbm_peak"] = 100.0 * r["alg_gbs"] / HBM_PEAK_GBS
+            for k in ("tflops", "pct_peak", "cold_tflops"):
+                r.pop(k, None)
+        else:
+            r["alg_gbs"] = (2 * n * hw * hw * (ci + co) + 2 * 9 * ci * co + 4 * co) / mean / 1e9
+        return r
+
+    def summary(self, r) -> str:
+        if self.pack_only:
+            return f"{r['alg_gbs']:.0f} GB/s, {r['mean_launch_us']:.1f} us/launch"
+        return super().summary(r)
+
+
 class EpilogueWorkload(Workload):
     """A GEMM through its fused-epilogue entry point: a fully connected layer
     C = relu(A*B + bias) (alpha 1, beta 0, one fp32 bias per column), or with
@@ -344,6 +410,12 @@ WORKLOADS = [
                               "MFMA, one LDS stage", "MFMA + double buffer",
                               "MFMA + double buffer + swizzle", "library kernel"))
 ] + [
+    ConvWorkload("conv_56x64", "bf16 3x3 conv 32x56x56x64 -> 64 (im2col + GEMM, bias + relu)",
+                 32, 56, 64, 64, 8),
+    ConvWorkload("conv_14x256", "bf16 3x3 conv 32x14x14x256 -> 256 (im2col + GEMM, bias + relu)",
+                 32, 14, 256, 256, 9),
+    ConvWorkload("im2col_56x64", "bf16 im2col pack, 32x56x56x64, 3x3, pad 1", 32, 56, 64, 64, 8,
+                 pack_only=True),
     QuantWorkload("quant_8192", "FP8 E4M3 64x64 block quantiser, 8192x8192 fp32 N(0,1)",
                   8192, 8192, 64, "e4m3", 1005),
 ]

@@ -14,6 +14,9 @@ Entry points (same names as the C ABI in include/libgemm.h):
         beta=0.0, bias=None, activation="none", stream=None)
     gemm_fp8_blockscaled_epilogue(A, B, scale_a, scale_b, C=None, alpha=1.0, beta=0.0,
         bias=None, activation="none", stream=None)
+    gemm_conv2d_nhwc(X, Wt, stride=1, padding=0, dilation=1, bias=None, activation="none",
+        Y=None, workspace=None, stream=None)   (NHWC input, HWIO weights: im2col + GEMM)
+    gemm_im2col_nhwc(X, kernel, stride=1, padding=0, dilation=1, col=None, stream=None)
     gemm_h16_ladder(rung, A, B, C=None, stream=None)      (measurement only)
     gemm_h16_mfma_ceiling(A, B, C=None, stream=None)      (measurement only)
 The *_epilogue calls write act(alpha * A@B + beta * C + bias[column]) (fp32,
@@ -36,11 +39,20 @@ LIB_PATH = os.path.join(_HERE, "libgemm.so")
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM_ERR_LD",
                 -4: "GEMM_ERR_ALIGN", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_DEVICE",
-                -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG"}
+                -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG", -9: "GEMM_ERR_WORKSPACE"}
 ENTRY_POINTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled",
                 "gemm_f16_epilogue", "gemm_bf16_epilogue", "gemm_f32_epilogue",
                 "gemm_fp8_blockscaled_epilogue", "gemm_quantize_fp8", "gemm_h16_ladder",
-                "gemm_h16_mfma_ceiling", "gemm_status_string", "gemm_version")
+                "gemm_h16_mfma_ceiling", "gemm_conv2d_nhwc", "gemm_conv2d_workspace_bytes",
+                "gemm_im2col_nhwc", "gemm_status_string", "gemm_version")
+DTYPES = {"f16": 0, "bf16": 1, "f32": 2}      # enum gemm_dtype
+
+
+class Conv2dShape(ctypes.Structure):
+    """struct gemm_conv2d_shape."""
+    _fields_ = [(name, ctypes.c_int64) for name in
+                ("n", "h", "w", "c_in", "c_out", "kh", "kw", "stride_h", "stride_w", "pad_h",
+                 "pad_w", "dil_h", "dil_w")]
 LADDER_RUNGS = {"naive": 0, "lds_tiled": 1, "register_tiled": 2, "mfma": 3,
                 "mfma_double_buffer": 4, "mfma_swizzle": 5, "library": 6}   # enum gemm_ladder_rung
 ACTIVATIONS = {"none": 0, "relu": 1}          # enum gemm_activation
@@ -86,6 +98,13 @@ def _load():
     h.gemm_h16_ladder.restype = ctypes.c_int
     h.gemm_h16_mfma_ceiling.argtypes = [ci, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
     h.gemm_h16_mfma_ceiling.restype = ctypes.c_int
+    sp = ctypes.POINTER(Conv2dShape)
+    h.gemm_conv2d_nhwc.argtypes = [ci, vp, vp, vp, vp, i64, sp, vp, ci, vp]
+    h.gemm_conv2d_nhwc.restype = ctypes.c_int
+    h.gemm_conv2d_workspace_bytes.argtypes = [ci, sp]
+    h.gemm_conv2d_workspace_bytes.restype = ctypes.c_int64
+    h.gemm_im2col_nhwc.argtypes = [ci, vp, vp, i64, sp, vp]
+    h.gemm_im2col_nhwc.restype = ctypes.c_int
     h.gemm_status_string.argtypes = [ctypes.c_int]
     h.gemm_status_string.restype = ctypes.c_char_p
     h.gemm_version.argtypes = []
@@ -283,6 +302,90 @@ def gemm_h16_mfma_ceiling(A, B, C=None, stream=None):
     return C
 
 
+def _pair(v):
+    return (int(v), int(v)) if isinstance(v, int) else (int(v[0]), int(v[1]))
+
+
+def conv2d_shape(X, Wt, stride=1, padding=0, dilation=1) -> Conv2dShape:
+    """struct gemm_conv2d_shape of an NHWC input and HWIO weights."""
+    if X.dim() != 4 or Wt.dim() != 4:
+        raise ValueError("conv2d: X must be NHWC (4-D) and Wt HWIO (4-D)")
+    n, h, w, c_in = X.shape
+    kh, kw, c_in2, c_out = Wt.shape
+    if c_in2 != c_in:
+        raise ValueError(f"conv2d: input channels differ ({c_in} vs {c_in2})")
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride), _pair(padding), _pair(dilation)
+    return Conv2dShape(n, h, w, c_in, c_out, kh, kw, sh, sw, ph, pw, dh, dw)
+
+
+def _conv_dtype(name, *tensors):
+    torch = _torch()
+    names = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+    dt = names.get(tensors[0].dtype)
+    if dt is None or any(t.dtype != tensors[0].dtype for t in tensors):
+        raise TypeError(f"{name}: tensors must all be float16, bfloat16 or float32")
+    for t in tensors:
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: tensors must be contiguous")
+    return dt
+
+
+def conv2d_output_hw(shape: Conv2dShape):
+    eh = shape.h + 2 * shape.pad_h - shape.dil_h * (shape.kh - 1) - 1
+    ew = shape.w + 2 * shape.pad_w - shape.dil_w * (shape.kw - 1) - 1
+    return (0 if eh < 0 else eh // shape.stride_h + 1), (0 if ew < 0 else ew // shape.stride_w + 1)
+
+
+def gemm_conv2d_nhwc(X, Wt, stride=1, padding=0, dilation=1, bias=None, activation="none",
+                     Y=None, workspace=None, stream=None):
+    """Y = act(conv2d(X, Wt) + bias) with X NHWC, Wt HWIO (kh, kw, c_in, c_out),
+    Y NHWC, through im2col + GEMM.  The im2col workspace is allocated when not
+    given (a uint8 device tensor of gemm_conv2d_workspace_bytes bytes)."""
+    torch = _torch()
+    dt = _conv_dtype("gemm_conv2d_nhwc", X, Wt)
+    shape = conv2d_shape(X, Wt, stride, padding, dilation)
+    ho, wo = conv2d_output_hw(shape)
+    need = lib.gemm_conv2d_workspace_bytes(DTYPES[dt], ctypes.byref(shape))
+    _check(need if need < 0 else 0, "gemm_conv2d_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    if Y is None:
+        Y = torch.empty((shape.n, ho, wo, shape.c_out), dtype=X.dtype, device=X.device)
+    if Y.dtype != X.dtype or tuple(Y.shape) != (shape.n, ho, wo, shape.c_out) or \
+            not Y.is_contiguous():
+        raise ValueError(f"gemm_conv2d_nhwc: Y must be contiguous {X.dtype} "
+                         f"{(shape.n, ho, wo, shape.c_out)}")
+    _, _, bptr, act = _epilogue_args("gemm_conv2d_nhwc", Y, shape.c_out, 1.0, 0.0, bias,
+                                     activation, X.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.gemm_conv2d_nhwc(DTYPES[dt], X.data_ptr(), Wt.data_ptr(), Y.data_ptr(), ws_ptr,
+                                ws_bytes, ctypes.byref(shape), bptr, act,
+                                _stream_handle(stream, X.device)), "gemm_conv2d_nhwc")
+    return Y
+
+
+def gemm_im2col_nhwc(X, kernel, stride=1, padding=0, dilation=1, col=None, stream=None):
+    """The im2col matrix of an NHWC tensor: (n*ho*wo) x (kh*kw*c_in), row
+    (n, oh, ow), column (kh, kw, ci); zeros where a tap falls in the padding."""
+    torch = _torch()
+    dt = _conv_dtype("gemm_im2col_nhwc", X)
+    kh, kw = _pair(kernel)
+    n, h, w, c_in = X.shape
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride), _pair(padding), _pair(dilation)
+    shape = Conv2dShape(n, h, w, c_in, 1, kh, kw, sh, sw, ph, pw, dh, dw)
+    ho, wo = conv2d_output_hw(shape)
+    rows, cols = n * ho * wo, kh * kw * c_in
+    if col is None:
+        col = torch.empty((rows, cols), dtype=X.dtype, device=X.device)
+    if col.dtype != X.dtype or tuple(col.shape) != (rows, cols):
+        raise ValueError(f"gemm_im2col_nhwc: col must be {X.dtype} of shape ({rows}, {cols})")
+    _check(lib.gemm_im2col_nhwc(DTYPES[dt], X.data_ptr(), col.data_ptr(), _ld(col),
+                                ctypes.byref(shape), _stream_handle(stream, X.device)),
+           "gemm_im2col_nhwc")
+    return col
+
+
 def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None):
     """Block-scaled FP8 quantisation of a 2-D float32 or bfloat16 tensor.
 
@@ -317,5 +420,6 @@ def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
 
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "gemm_f16_epilogue",
            "gemm_bf16_epilogue", "gemm_f32_epilogue", "gemm_fp8_blockscaled_epilogue",
-           "gemm_quantize_fp8", "gemm_h16_ladder", "gemm_h16_mfma_ceiling", "status_string",
+           "gemm_quantize_fp8", "gemm_h16_ladder", "gemm_h16_mfma_ceiling", "gemm_conv2d_nhwc",
+           "gemm_im2col_nhwc", "Conv2dShape", "status_string",
            "GemmError", "lib", "LIB_PATH"]

@@ -384,6 +384,123 @@ extern "C" int gemm_h16_mfma_ceiling(int is_bf16, const void *A, const void *B, 
     return to_status(mfma_ceiling_launch(is_bf16, p));
 }
 
+namespace {
+
+// Checks of a convolution call's type and geometry; fills the kernel-side shape,
+// the output size and the element size.
+int conv_check(int dtype, const gemm_conv2d_shape *sp, ConvShape *cs, int64_t *ho, int64_t *wo,
+               int64_t *esize)
+{
+    if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16 && dtype != GEMM_DTYPE_F32)
+        return GEMM_ERR_ARG;
+    if (sp == nullptr) return GEMM_ERR_NULL;
+    const gemm_conv2d_shape &s = *sp;
+    const int64_t f[13] = {s.n, s.h, s.w, s.c_in, s.c_out, s.kh, s.kw, s.stride_h, s.stride_w,
+                           s.pad_h, s.pad_w, s.dil_h, s.dil_w};
+    for (int64_t v : f)
+        if (v < 0) return GEMM_ERR_DIM;
+    if (s.kh < 1 || s.kw < 1 || s.stride_h < 1 || s.stride_w < 1 || s.dil_h < 1 || s.dil_w < 1)
+        return GEMM_ERR_DIM;
+    // spatial sizes small enough that every input coordinate fits in int
+    constexpr int64_t SPATIAL = 1 << 15;
+    for (int i = 1; i < 13; ++i)
+        if (i != 3 && i != 4 && f[i] > SPATIAL) return GEMM_ERR_DIM;
+    if (s.n > DIM_LIMIT || s.c_in > DIM_LIMIT || s.c_out > DIM_LIMIT) return GEMM_ERR_DIM;
+    const int64_t eh = s.h + 2 * s.pad_h - s.dil_h * (s.kh - 1) - 1;
+    const int64_t ew = s.w + 2 * s.pad_w - s.dil_w * (s.kw - 1) - 1;
+    *ho = eh < 0 ? 0 : eh / s.stride_h + 1;
+    *wo = ew < 0 ? 0 : ew / s.stride_w + 1;
+    if (s.n * *ho * *wo > DIM_LIMIT || s.kh * s.kw * s.c_in > DIM_LIMIT ||
+        s.n * s.h * s.w > ((int64_t)1 << 40) / (s.c_in > 0 ? s.c_in : 1))
+        return GEMM_ERR_DIM;
+    *cs = ConvShape{(int)s.n, (int)s.h, (int)s.w, (int)s.c_in, (int)s.c_out, (int)s.kh, (int)s.kw,
+                    (int)s.stride_h, (int)s.stride_w, (int)s.pad_h, (int)s.pad_w, (int)s.dil_h,
+                    (int)s.dil_w};
+    *esize = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    return GEMM_OK;
+}
+
+// A 1 x 1 convolution with unit stride and no padding needs no im2col matrix:
+// the NHWC input already is it.
+bool conv_direct(const ConvShape &s)
+{
+    return s.kh == 1 && s.kw == 1 && s.stride_h == 1 && s.stride_w == 1 && s.pad_h == 0 &&
+           s.pad_w == 0;
+}
+
+}  // namespace
+
+extern "C" int64_t gemm_conv2d_workspace_bytes(int dtype, const gemm_conv2d_shape *shape)
+{
+    ConvShape s;
+    int64_t ho, wo, esize;
+    const int st = conv_check(dtype, shape, &s, &ho, &wo, &esize);
+    if (st != GEMM_OK) return st;
+    if (conv_direct(s)) return 0;
+    return (int64_t)s.n * ho * wo * s.kh * s.kw * s.c_in * esize;
+}
+
+extern "C" int gemm_im2col_nhwc(int dtype, const void *X, void *col, int64_t ldcol,
+                                const gemm_conv2d_shape *shape, hipStream_t stream)
+{
+    ConvShape s;
+    int64_t ho, wo, esize;
+    int st = conv_check(dtype, shape, &s, &ho, &wo, &esize);
+    if (st != GEMM_OK) return st;
+    const int64_t M = (int64_t)s.n * ho * wo, K = (int64_t)s.kh * s.kw * s.c_in;
+    if (ldcol < K || ldcol > (int64_t)1 << 40) return GEMM_ERR_LD;
+    if (M == 0 || K == 0) return GEMM_OK;
+    if (X == nullptr || col == nullptr) return GEMM_ERR_NULL;
+    if ((uintptr_t)X % esize || (uintptr_t)col % esize) return GEMM_ERR_ALIGN;
+    if (overlaps(col, span_bytes(M, K, ldcol, esize), X,
+                 (int64_t)s.n * s.h * s.w * s.c_in * esize))
+        return GEMM_ERR_ALIAS;
+    if ((st = check_device()) != GEMM_OK) return st;
+    return to_status(im2col_launch((int)esize, X, col, ldcol, s, (int)ho, (int)wo, stream));
+}
+
+extern "C" int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *Y, void *workspace,
+                                int64_t workspace_bytes, const gemm_conv2d_shape *shape,
+                                const float *bias, int activation, hipStream_t stream)
+{
+    if (activation != GEMM_ACT_NONE && activation != GEMM_ACT_RELU) return GEMM_ERR_ARG;
+    ConvShape s;
+    int64_t ho, wo, esize;
+    int st = conv_check(dtype, shape, &s, &ho, &wo, &esize);
+    if (st != GEMM_OK) return st;
+    const int64_t M = (int64_t)s.n * ho * wo, K = (int64_t)s.kh * s.kw * s.c_in, N = s.c_out;
+    if (M == 0 || N == 0) return GEMM_OK;
+    const bool direct = conv_direct(s);
+    const int64_t need = direct || K == 0 ? 0 : M * K * esize;
+    if (Y == nullptr || (K > 0 && (X == nullptr || Wt == nullptr))) return GEMM_ERR_NULL;
+    if ((uintptr_t)Y % esize || (K > 0 && ((uintptr_t)X % esize || (uintptr_t)Wt % esize)))
+        return GEMM_ERR_ALIGN;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GEMM_ERR_WORKSPACE;
+    if (need > 0 && (uintptr_t)workspace % esize) return GEMM_ERR_ALIGN;
+    const int64_t yb = M * N * esize, xb = (int64_t)s.n * s.h * s.w * s.c_in * esize;
+    const int64_t wb = K * N * esize;
+    if (K > 0 && (overlaps(Y, yb, X, xb) || overlaps(Y, yb, Wt, wb))) return GEMM_ERR_ALIAS;
+    if (need > 0 && (overlaps(workspace, need, X, xb) || overlaps(workspace, need, Wt, wb) ||
+                     overlaps(workspace, need, Y, yb)))
+        return GEMM_ERR_ALIAS;
+    if ((st = check_bias(bias, Y, M, N, N, esize)) != GEMM_OK) return st;
+    if ((st = check_device()) != GEMM_OK) return st;
+    Epilogue epi{1.f, 0.f, bias, activation == GEMM_ACT_RELU ? 1 : 0};
+    const Epilogue *pe = bias || activation == GEMM_ACT_RELU ? &epi : nullptr;
+    const int out = dtype == GEMM_DTYPE_F32 ? OUT_F32 : dtype == GEMM_DTYPE_BF16 ? OUT_BF16 : OUT_F16;
+    if (K == 0) return to_status(empty_sum_launch(Y, (int)M, (int)N, N, out, pe, stream));
+    const void *A = X;
+    if (!direct) {
+        st = to_status(im2col_launch((int)esize, X, workspace, K, s, (int)ho, (int)wo, stream));
+        if (st != GEMM_OK) return st;
+        A = workspace;
+    }
+    if (dtype == GEMM_DTYPE_F32)
+        return f32_entry(static_cast<const float *>(A), static_cast<const float *>(Wt),
+                         static_cast<float *>(Y), M, N, K, K, N, N, pe, stream);
+    return h16_entry(dtype == GEMM_DTYPE_BF16, A, Wt, Y, M, N, K, K, N, N, pe, stream);
+}
+
 extern "C" int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols,
                                  int64_t ldx, int block, int fmt, uint8_t *Q, int64_t ldq,
                                  float *scales, hipStream_t stream)
@@ -420,6 +537,7 @@ extern "C" const char *gemm_status_string(int status)
     case GEMM_ERR_ALIAS: return "an output overlaps an input (or the two quantiser outputs overlap)";
     case GEMM_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_ERR_WORKSPACE: return "workspace missing or smaller than the call needs";
     case GEMM_ERR_ARG:
         return "unsupported option (input type, block size, FP8 format, activation, or a "
                "non-finite alpha or beta)";

@@ -80,6 +80,15 @@ struct QuantProblem {
     hipStream_t stream;
 };
 hipError_t quant_fp8_launch(const QuantProblem &p);
+// Convolution geometry after argument checking (every field fits in int; the
+// products that index memory are formed in 64 bits).
+struct ConvShape {
+    int n, h, w, c_in, c_out, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+};
+// The im2col matrix of an NHWC tensor X (element size esize 2 or 4) into col,
+// (n*ho*wo) rows of kh*kw*c_in elements at leading dimension ldcol.
+hipError_t im2col_launch(int esize, const void *X, void *col, int64_t ldcol, const ConvShape &s,
+                         int ho, int wo, hipStream_t stream);
 // K == 0: every sum is empty.  Sets the M x N window of C (out: 0 fp16, 1 bf16,
 // 2 fp32; leading dimension ldc) to zero, or with an epilogue to
 // act(beta * c_prior + bias[column]).

@@ -50,8 +50,12 @@ enum gemm_status {
     GEMM_ERR_ALIAS = -5,   /* an output overlaps an input (or another output) */
     GEMM_ERR_DEVICE = -6,  /* the current device is not a gfx950 GPU, or it cannot be queried */
     GEMM_ERR_LAUNCH = -7,  /* the kernel launch was rejected by the runtime */
-    GEMM_ERR_ARG = -8      /* an option (input type, block size, FP8 format, activation, alpha/beta) is not supported */
+    GEMM_ERR_ARG = -8,     /* an option (input type, block size, FP8 format, activation, alpha/beta) is not supported */
+    GEMM_ERR_WORKSPACE = -9 /* a caller-provided workspace is missing or too small */
 };
+
+/* Element types of the convolution entry points. */
+enum gemm_dtype { GEMM_DTYPE_F16 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F32 = 2 };
 
 /* FP8 formats (OCP): E4M3 ("E4M3FN": bias 7, largest finite 448, no infinities)
  * and E5M2 (bias 15, largest finite 57344). */
@@ -199,6 +203,60 @@ int gemm_h16_ladder(int rung, int is_bf16, const void *A, const void *B, void *C
 int gemm_h16_mfma_ceiling(int is_bf16, const void *A, const void *B, void *C, int64_t M,
                           int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                           hipStream_t stream);
+
+/* Geometry of a 2-D convolution (all elements, not bytes):
+ *   input  X : n x h x w x c_in            (NHWC, dense)
+ *   weights Wt: kh x kw x c_in x c_out     ("HWIO", dense)
+ *   output Y : n x ho x wo x c_out         (NHWC, dense)
+ * with ho = floor((h + 2 pad_h - dil_h (kh - 1) - 1) / stride_h) + 1 and wo
+ * likewise (0 when the dilated kernel does not fit).  kh, kw, strides and
+ * dilations >= 1; paddings >= 0 (zeros); h, w, kh, kw, strides, paddings and
+ * dilations at most 32768; n*ho*wo and kh*kw*c_in at most 2^31 - 1. */
+typedef struct gemm_conv2d_shape {
+    int64_t n, h, w, c_in, c_out, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+} gemm_conv2d_shape;
+
+/* Convolution as a GEMM through im2col, "深度学习加速核心：GEMM优化从分块到
+ * TensorCore的实战解析" section 1.1 (each output position's receptive field laid
+ * out as one row of a large matrix turns the convolution into a GEMM, for the
+ * extra memory that matrix takes):
+ *   Y[n][oh][ow][co] = round( act( sum_{kh, kw, ci} X[n][ih][iw][ci] * Wt[kh][kw][ci][co]
+ *                                  + bias[co] ) ),
+ *   ih = oh*stride_h - pad_h + kh*dil_h,  iw = ow*stride_w - pad_w + kw*dil_w,
+ * X read as 0 outside the image.  The im2col matrix (n*ho*wo rows of
+ * kh*kw*c_in elements, row (n, oh, ow), column (kh, kw, ci)) is built in the
+ * caller's workspace by gemm_im2col_nhwc's kernel and multiplied by Wt, seen as
+ * the (kh*kw*c_in) x c_out row-major matrix it already is, by the GEMM of the
+ * same type (fp32 accumulation, one rounding), with bias and activation fused
+ * as in gemm_*_epilogue (bias: NULL or c_out device fp32 values, one per output
+ * channel).  A 1 x 1 convolution with unit strides and no padding uses X
+ * directly and needs no workspace.  dtype: GEMM_DTYPE_F16, _BF16 or _F32 for
+ * X, Wt and Y alike.  The layouts are a reading: the pages fix none.
+ * Work is enqueued on `stream` (im2col, then the GEMM); the workspace is
+ * caller-owned device memory of at least gemm_conv2d_workspace_bytes() bytes
+ * that must stay untouched until that work is done.  n*ho*wo == 0 or
+ * c_out == 0: nothing to do.  c_in == 0: Y = act(bias).
+ * Errors: GEMM_ERR_ARG (dtype, activation), GEMM_ERR_NULL (shape or a needed
+ * pointer), GEMM_ERR_DIM (geometry), GEMM_ERR_ALIGN (pointers not aligned to the
+ * element size, bias to 4 bytes), GEMM_ERR_WORKSPACE, GEMM_ERR_ALIAS (Y, the
+ * workspace and the inputs must not overlap), then those of the GEMM. */
+int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *Y, void *workspace,
+                     int64_t workspace_bytes, const gemm_conv2d_shape *shape, const float *bias,
+                     int activation, hipStream_t stream);
+
+/* Bytes of workspace gemm_conv2d_nhwc needs for this dtype and geometry (the
+ * im2col matrix, n*ho*wo * kh*kw*c_in elements; 0 for the direct 1 x 1 case),
+ * or a negative gemm_status for a bad dtype or geometry.  Host only. */
+int64_t gemm_conv2d_workspace_bytes(int dtype, const gemm_conv2d_shape *shape);
+
+/* The im2col matrix alone: with KW = shape->kw,
+ *   col[((n*ho + oh)*wo + ow) * ldcol + (kh*KW + kw)*c_in + ci] = X[n][ih][iw][ci]
+ * (ih, iw as above), or 0 where the tap falls outside the image.
+ * Pure data movement, bit for bit.  ldcol >= kh*kw*c_in (else GEMM_ERR_LD);
+ * col must not overlap X; bytes of col past each row's kh*kw*c_in elements are
+ * not written.  Errors otherwise as gemm_conv2d_nhwc. */
+int gemm_im2col_nhwc(int dtype, const void *X, void *col, int64_t ldcol,
+                     const gemm_conv2d_shape *shape, hipStream_t stream);
 
 /* Static, NUL-terminated description of a gemm_status value. */
 const char *gemm_status_string(int status);

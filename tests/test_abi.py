@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = dg.status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert dg.status_string(-99) == "unknown status"
@@ -56,6 +56,14 @@ def test_enum_values_match_header():
                                         for k, v in dg.ACTIVATIONS.items()}
     assert _enum("gemm_ladder_rung") == {"GEMM_LADDER_" + k.upper(): v
                                          for k, v in dg.LADDER_RUNGS.items()}
+    assert _enum("gemm_dtype") == {"GEMM_DTYPE_" + k.upper(): v for k, v in dg.DTYPES.items()}
+
+
+def test_conv_shape_struct_matches_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"struct gemm_conv2d_shape\s*\{(.*?)\}", text, flags=re.S).group(1)
+    names = re.findall(r"(\w+)\s*[,;]", body.replace("int64_t", ""))
+    assert names == [f[0] for f in dg.Conv2dShape._fields_]
 
 
 # Fake, never-dereferenced device addresses: 4 KiB aligned and far apart.
@@ -169,6 +177,48 @@ def test_ladder_and_ceiling_argument_errors():
     assert Q(K=48) == -2
     assert Q(a=A + 2) == -4
     assert Q(M=0) == 0
+
+
+def test_conv_argument_errors():
+    import ctypes
+    S = lambda **kw: dg.Conv2dShape(**{**dict(n=2, h=8, w=8, c_in=16, c_out=32, kh=3, kw=3,
+                                               stride_h=1, stride_w=1, pad_h=1, pad_w=1,
+                                               dil_h=1, dil_w=1), **kw})
+    need = lib.gemm_conv2d_workspace_bytes(1, ctypes.byref(S()))
+    assert need == 2 * 8 * 8 * 9 * 16 * 2
+    assert lib.gemm_conv2d_workspace_bytes(2, ctypes.byref(S())) == 2 * need
+    assert lib.gemm_conv2d_workspace_bytes(1, ctypes.byref(S(kh=1, kw=1, pad_h=0, pad_w=0))) == 0
+    assert lib.gemm_conv2d_workspace_bytes(3, ctypes.byref(S())) == -8
+    assert lib.gemm_conv2d_workspace_bytes(1, None) == -1
+    for bad in (dict(kh=0), dict(stride_w=0), dict(dil_h=0), dict(pad_h=-1), dict(h=1 << 16),
+                dict(n=-1)):
+        assert lib.gemm_conv2d_workspace_bytes(1, ctypes.byref(S(**bad))) == -2, bad
+    X, W, Y, WS = A, B, C, SA
+    conv = lambda s=S(), x=X, w=W, y=Y, ws=WS, wsb=need, dtype=1, bias=None, act=0: \
+        lib.gemm_conv2d_nhwc(dtype, x, w, y, ws, wsb, ctypes.byref(s), bias, act, None)
+    assert conv(act=2) == -8
+    assert conv(dtype=5) == -8
+    assert conv(y=0) == -1
+    assert conv(x=0) == -1
+    assert conv(y=Y + 1) == -4
+    assert conv(ws=0) == -9
+    assert conv(wsb=need - 1) == -9
+    assert conv(y=X + 64) == -5                   # output over the input
+    assert conv(ws=Y) == -5                       # workspace over the output
+    assert conv(bias=BIAS + 2) == -4
+    assert conv(s=S(h=1, pad_h=0)) == 0           # kernel taller than the image: no output
+    assert conv(s=S(c_out=0)) == 0
+    # the direct 1x1 case needs no workspace: it passes every argument check and
+    # reaches the device check (only where no GPU could run it on these fake pointers)
+    import torch
+    if not torch.cuda.is_available():
+        assert conv(s=S(kh=1, kw=1, pad_h=0, pad_w=0), ws=0, wsb=0) == -6
+    im2col = lambda s=S(), x=X, col=WS, ld=9 * 16: \
+        lib.gemm_im2col_nhwc(1, x, col, ld, ctypes.byref(s), None)
+    assert im2col(ld=9 * 16 - 1) == -3
+    assert im2col(col=0) == -1
+    assert im2col(col=X + 2) == -5
+    assert im2col(s=S(n=0)) == 0
 
 
 def test_quantize_argument_errors():
