@@ -190,17 +190,36 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                     (lds_i32x2_t *)(bs + b_off_r[j] + 8 * q * QBN));
             bfr[j] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
         }
+        // Software-pipelined promotion: the MFMA of tile t + 1 is issued before
+        // the 16 FMAs that promote tile t, into the other of two partial
+        // register sets, so the vector ALU works on one tile while the matrix
+        // core works on the next (with one set, each tile's FMAs would wait for
+        // its own MFMA, and the next MFMA for those FMAs).
+        // E4M3 for both operands (format 0); block scales 127 = 2^0.
+        constexpr int NT = QFM * QFN;
+        const auto mma = [&](int t) {
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bfr[t / QFM], af[t % QFM], f32x16{}, 0, 0, 0, 127, 0, 127);
+        };
+        const auto promote = [&](const f32x16 &p, int t) {
+            const int i = t % QFM, j = t / QFM;
+            const float s = i < 2 ? s0 : s1;
 #pragma unroll
-        for (int j = 0; j < QFN; ++j)
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], s, acc[i][j][e]);
+        };
+        f32x16 part[2];
+        part[0] = mma(0);
 #pragma unroll
-            for (int i = 0; i < QFM; ++i) {
-                // E4M3 for both operands (format 0); block scales 127 = 2^0
-                const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bfr[j], af[i], f32x16{}, 0, 0, 0, 127, 0, 127);
-                const float s = i < 2 ? s0 : s1;
+        for (int t = 1; t < NT; ++t) {
+            part[t & 1] = mma(t);
+            promote(part[(t - 1) & 1], t - 1);
+        }
+        promote(part[(NT - 1) & 1], NT - 1);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], s, acc[i][j][e]);
-            }
+        for (int t = 0; t < NT; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // sixteen VALU
+        }
     };
 
     const int ktiles = K / QBK;                          // a multiple of QSTAGES
