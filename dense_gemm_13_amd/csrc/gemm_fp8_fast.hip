@@ -15,7 +15,12 @@
 // one FMA per element by sa * sb of that block.  The promotion runs on the
 // vector ALU, so the accumulators live in VGPRs: 8 waves (two per SIMD), each
 // with a 128 x 64 sub-tile (128 accumulator VGPRs); one wave's MFMAs overlap the
-// other's promotion.
+// other's promotion.  The promotion costs as many vector-ALU cycles as the MFMAs
+// take on the matrix core (16 wave64 FMAs of 4 cycles per 64-cycle MFMA), so
+// the kernel is bound by how well the two overlap.  The block scales of each K
+// step travel into LDS with its operands, and one barrier per step (half-way
+// through its MFMAs) lets the next stage's fragments be read while the
+// current one is multiplied.
 //
 // B stays in LDS as rows of k (n contiguous, 256-byte rows) and the MFMA operand
 // "32 consecutive k of one column" comes from four ds_read_b64_tr_b8: within a
@@ -47,6 +52,11 @@ constexpr int QNBLK = QA_BLK + QB_BLK;
 
 template <int TAG>
 __shared__ __attribute__((aligned(1024))) uint8_t q_stage[16384];
+// The block scales of one stage (4 of A's scale rows, then 4 of B's scale
+// columns), 64 copies of each (one per lane of the wave that loads it), one
+// array per stage like the operand stages.
+template <int TAG>
+__shared__ __attribute__((aligned(256))) float q_scale[8 * 64];
 
 __device__ __forceinline__ uint8_t *q_ring(int idx)
 {
@@ -155,10 +165,25 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         b_off_r[j] = (32 * (g >> 1) + r8) * QBN + (((n >> 4) ^ qswz_b(r8)) << 4) + (n & 15);
     }
 
-    // Scale rows / column of this wave: A tiles 0,1 and 2,3 are in scale rows mb0 and mb0+1.
-    const int mb0 = (m0 + wm0) / 64, nb = (n0 + wn0) / 64;
-    const float *sa0 = scale_a + (int64_t)mb0 * kblocks, *sa1 = sa0 + kblocks;
-    const float *sbc = scale_b + nb;
+    // ---- block scales.  Every stage also carries the 8 scales of its K block
+    // that this tile needs: scale_a of the tile's 4 scale rows and scale_b of
+    // its 4 scale columns.  Wave w fetches one of them (w < 4: row w of A's
+    // scales, else column w - 4 of B's) with a 4-byte LDS-direct load in which
+    // every lane reads the same address (no branch), so the scales travel and
+    // are waited for exactly like the operands.
+    const float *sc_src = wave < 4 ? scale_a + (int64_t)(m0 / 64 + wave) * kblocks
+                                   : scale_b + n0 / 64 + (wave - 4);
+    const int64_t sc_step = wave < 4 ? 1 : nblocks;
+    // This wave's scale row pair (A tiles 0,1 / 2,3) and scale column, in the slot.
+    const int sc_row = wm0 / 64, sc_col = 4 + wn0 / 64;
+
+    auto issue_all = [&](auto S, int kt) {
+        issue(q_stage<S>, q_stage<QSTAGES + S>, kt);
+        __builtin_amdgcn_global_load_lds(sc_src + kt * sc_step,
+                                         (lds_void8_t *)&q_scale<S>[64 * wave], 4, 0, 0);
+    };
+    constexpr int QLOADS = QNBLK + 1;                    // loads per wave per stage
+    const int ktiles = K / QBK;                          // a multiple of QSTAGES
 
     f32x16 acc[QFM][QFN];
 #pragma unroll
@@ -166,72 +191,131 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
         for (int j = 0; j < QFN; ++j) acc[i][j] = f32x16{};
 
-    auto step = [&](const uint8_t *as, const uint8_t *bs, uint8_t *nas, uint8_t *nbs, int kt,
-                    int next_kt) {
-        q_wait_vmcnt<(QSTAGES - 2) * QNBLK>();
-        q_barrier();
-        issue(nas, nbs, next_kt);
-        const float sb = sbc[(int64_t)kt * nblocks];
-        const float s0 = sa0[kt] * sb, s1 = sa1[kt] * sb;
-        i32x8 af[QFM], bfr[QFN];
+    // Fragments of one stage: A tile i (ds_read_b128 x 2), B tile j (four
+    // transposing reads), and the two products sa * sb of the wave's scale rows.
+    i32x8 af[QFM], bfr[QFN];
+    const auto read_a = [&](const uint8_t *as, int i) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(as + a_off0[i]);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(as + a_off1[i]);
+        af[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                      (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    };
+    const auto read_b = [&](const uint8_t *bs, int j) {
+        i32x2 r[4];
 #pragma unroll
-        for (int i = 0; i < QFM; ++i) {
-            const u32x4 x0 = *reinterpret_cast<const u32x4 *>(as + a_off0[i]);
-            const u32x4 x1 = *reinterpret_cast<const u32x4 *>(as + a_off1[i]);
-            af[i] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        }
+        for (int q = 0; q < 4; ++q)
+            r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2_t *)(bs + b_off_r[j] + 8 * q * QBN));
+        bfr[j] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    };
+    // The raw scales of the next step are read at the end of a step and
+    // multiplied in the next step's first slot (not at once, which would wait
+    // for the reads just issued).
+    float rsa0, rsa1, rsb;
+    const auto read_scales = [&](const float *sl) {
+        rsb = sl[64 * sc_col];
+        rsa0 = sl[64 * sc_row];
+        rsa1 = sl[64 * (sc_row + 1)];
+    };
+    float cs0 = 0.f, cs1 = 0.f;                          // sa * sb of the current step
+
+    // One MFMA per 32 x 32 tile and K block (E4M3 operands, format 0; hardware
+    // block scales 127 = 2^0) into a fresh partial, promoted into the fp32
+    // accumulator with one FMA per element by that block's sa * sb.  The
+    // promotion of tile t runs after the MFMA of tile t + 1 has been issued
+    // (two partial register sets), so the vector ALU works on one tile while the
+    // matrix core works on the next and no FMA waits for the MFMA that feeds it.
+    // Tiles t = 0..3 use B tile 0, t = 4..7 B tile 1; tile t is A tile t % 4.
+    constexpr int NT = QFM * QFN;
+    f32x16 part[2];
+    const auto mma = [&](int t) {
+        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bfr[t / QFM], af[t % QFM], f32x16{}, 0, 0, 0, 127, 0, 127);
+    };
+    const auto promote = [&](int t, float s0, float s1) {
+        const int i = t % QFM, j = t / QFM;
+        const float s = i < 2 ? s0 : s1;
 #pragma unroll
-        for (int j = 0; j < QFN; ++j) {
-            i32x2 r[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (lds_i32x2_t *)(bs + b_off_r[j] + 8 * q * QBN));
-            bfr[j] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-        }
-        // Software-pipelined promotion: the MFMA of tile t + 1 is issued before
-        // the 16 FMAs that promote tile t, into the other of two partial
-        // register sets, so the vector ALU works on one tile while the matrix
-        // core works on the next (with one set, each tile's FMAs would wait for
-        // its own MFMA, and the next MFMA for those FMAs).
-        // E4M3 for both operands (format 0); block scales 127 = 2^0.
-        constexpr int NT = QFM * QFN;
-        const auto mma = [&](int t) {
-            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                bfr[t / QFM], af[t % QFM], f32x16{}, 0, 0, 0, 127, 0, 127);
-        };
-        const auto promote = [&](const f32x16 &p, int t) {
-            const int i = t % QFM, j = t / QFM;
-            const float s = i < 2 ? s0 : s1;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], s, acc[i][j][e]);
-        };
-        f32x16 part[2];
-        part[0] = mma(0);
-#pragma unroll
-        for (int t = 1; t < NT; ++t) {
-            part[t & 1] = mma(t);
-            promote(part[(t - 1) & 1], t - 1);
-        }
-        promote(part[(NT - 1) & 1], NT - 1);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // sixteen VALU
-        }
+        for (int e = 0; e < 16; ++e)
+            acc[i][j][e] = __builtin_fmaf(part[t & 1][e], s, acc[i][j][e]);
     };
 
-    const int ktiles = K / QBK;                          // a multiple of QSTAGES
-    q_unroll<QSTAGES - 1>([&](auto S) { issue(q_stage<S>, q_stage<QSTAGES + S>, S); });
-    for (int kt = 0; kt < ktiles; kt += QSTAGES) {
-        q_unroll<QSTAGES>([&](auto S) {
-            constexpr int NS = (S + QSTAGES - 1) % QSTAGES;
-            const int next = kt + S + QSTAGES - 1;
-            step(q_stage<S>, q_stage<QSTAGES + S>, q_stage<NS>, q_stage<QSTAGES + NS>, kt + S,
-                 next < ktiles ? next : ktiles - 1);
-        });
-    }
+    // K step s runs on stage S = s % QSTAGES with its fragments and scales
+    // already in registers:
+    //   * tiles 0..3 (B tile 0; the first slot also promotes the previous
+    //     step's last tile, with that step's scales);
+    //   * wait for this wave's loads of stage s + 1 and for its outstanding LDS
+    //     reads, barrier: stage s + 1 is complete, and every wave has read all
+    //     of stage s that it will read;
+    //   * issue the loads of K step s + QSTAGES into stage S; read B tile 0 of
+    //     stage s + 1;
+    //   * tiles 4..7 (B tile 1), reading A tile t - 4 of stage s + 1 after each
+    //     tile's MFMA (its last use of that A tile), then B tile 1 and the
+    //     scales of stage s + 1.
+    // A load has QSTAGES - 1 steps to land.  Slots are fenced so the compiler
+    // keeps this order.
+    float ps0 = 0.f, ps1 = 0.f;                          // scales of the previous step
+    const auto step = [&](auto S, int s) {
+        constexpr int N1 = (S + 1) % QSTAGES;
+#pragma unroll
+        for (int t = 0; t < NT / 2; ++t) {
+            mma(t);
+            if (t == 0) {
+                promote(NT - 1, ps0, ps1);
+                // Wave-uniform: held in scalar registers, so each promotion FMA
+                // reads two vector registers instead of three.
+                cs0 = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rsa0 * rsb)));
+                cs1 = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rsa1 * rsb)));
+            } else {
+                promote(t - 1, cs0, cs1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0)
+        q_wait_vmcnt<(QSTAGES - 2) * QLOADS>();
+        q_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int nxt = s + QSTAGES;
+        issue_all(S, nxt < ktiles ? nxt : ktiles - 1);
+        read_b(q_stage<QSTAGES + N1>, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = NT / 2; t < NT; ++t) {
+            mma(t);
+            promote(t - 1, cs0, cs1);
+            read_a(q_stage<N1>, t - NT / 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        read_b(q_stage<QSTAGES + N1>, 1);
+        ps0 = cs0;
+        ps1 = cs1;
+        read_scales(q_scale<N1>);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: K steps 0 .. QSTAGES-1 in flight, stage 0 published, its
+    // fragments and scales read.  The partial set the first slot promotes is
+    // zero (with zero scales).  Steps past the end re-load the last K block into
+    // stages nobody reads any more, and the last step's look-ahead reads a
+    // stage whose contents are not used.
+    q_unroll<QSTAGES>([&](auto S) { issue_all(S, (int)S); });
+    q_wait_vmcnt<(QSTAGES - 1) * QLOADS>();
+    q_barrier();
+#pragma unroll
+    for (int i = 0; i < QFM; ++i) read_a(q_stage<0>, i);
+#pragma unroll
+    for (int j = 0; j < QFN; ++j) read_b(q_stage<QSTAGES>, j);
+    read_scales(q_scale<0>);
+    part[(NT - 1) & 1] = f32x16{};
+    for (int kt = 0; kt < ktiles; kt += QSTAGES)
+        q_unroll<QSTAGES>([&](auto S) { step(S, kt + S); });
+    promote(NT - 1, ps0, ps1);
     q_wait_vmcnt<0>();
 
     // ---- epilogue through LDS: each wave's 128 x 64 bf16 sub-tile (16 KiB) goes
