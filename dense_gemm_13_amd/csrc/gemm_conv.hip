@@ -9,11 +9,14 @@
 // and with the weights in HWIO order (KH x KW x C_in x C_out) they already are
 // the GEMM's K x C_out operand, rows in the same (kh, kw, ci) order.
 //
-// The pack kernel is pure data movement and HBM/L2-bound: one thread per
-// 16-byte chunk (8 half-precision or 4 fp32 channels) when the channel count
-// and the pointers allow it, else one thread per element.  Consecutive threads
-// write consecutive chunks of a row (coalesced) and read consecutive channels
-// of one pixel.
+// The pack kernel is pure data movement and HBM/L2-bound.  A thread owns one
+// 16-byte chunk (8 half-precision or 4 fp32 channels; one element when the
+// channel count or the pointers do not allow 16 bytes) of one output position
+// and walks the kh x kw taps, so the position's coordinates are derived once
+// (three integer divisions, which the GPU does in software) and each tap costs a
+// few additions.  The threads of a workgroup cover consecutive chunks of
+// consecutive output rows: for every tap a wave reads whole runs of adjacent
+// input pixels and writes whole row segments of the matrix.
 #include <type_traits>
 
 #include "gemm_device.hpp"
@@ -23,34 +26,43 @@ namespace gemm {
 
 namespace {
 
-// VEC elements (of ESIZE bytes) per thread, 16 bytes when VEC * ESIZE == 16.
+// VEC elements (of ESIZE bytes) per chunk, 16 bytes when VEC * ESIZE == 16.
+// Workgroup b packs output rows [b * rows_per_block, (b + 1) * rows_per_block).
 template <int ESIZE, int VEC>
 __global__ void __launch_bounds__(256)
 im2col_kernel(const void *__restrict__ X, void *__restrict__ col, int64_t ldcol, ConvShape s,
-              int ho, int wo, int64_t total)
+              int ho, int wo, int rows, int rows_per_block)
 {
     using T = typename std::conditional<ESIZE == 2, uint16_t, uint32_t>::type;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= total) return;
-    const int cv = s.c_in / VEC;                      // vectors per pixel
-    const int64_t per_row = (int64_t)s.kh * s.kw * cv;
-    const int64_t m = t / per_row;
-    const int r = (int)(t - m * per_row);
-    const int tap = r / cv, c = (r - tap * cv) * VEC;
-    const int kh = tap / s.kw, kw = tap - kh * s.kw;
-    const int64_t img = m / ((int64_t)ho * wo);
-    const int pix = (int)(m - img * ho * wo);
-    const int oh = pix / wo, ow = pix - oh * wo;
-    const int ih = oh * s.stride_h - s.pad_h + kh * s.dil_h;
-    const int iw = ow * s.stride_w - s.pad_w + kw * s.dil_w;
-    const bool inside = ih >= 0 && ih < s.h && iw >= 0 && iw < s.w;
-    T *dst = static_cast<T *>(col) + m * ldcol + (int64_t)tap * s.c_in + c;
-    const T *src = static_cast<const T *>(X) + ((img * s.h + ih) * s.w + iw) * s.c_in + c;
-    if constexpr (VEC * ESIZE == 16) {
-        *reinterpret_cast<u32x4 *>(dst) =
-            inside ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0, 0, 0, 0};
-    } else {
-        *dst = inside ? *src : T(0);
+    const int cv = s.c_in / VEC;                      // chunks per pixel
+    const int per_block = rows_per_block * cv;
+    const int hw = ho * wo;
+    for (int q = threadIdx.x; q < per_block; q += blockDim.x) {
+        const int dm = q / cv;
+        const int m = blockIdx.x * rows_per_block + dm;
+        if (m >= rows) break;
+        const int c = (q - dm * cv) * VEC;
+        const int img = m / hw, pix = m - img * hw;
+        const int oh = pix / wo, ow = pix - oh * wo;
+        const int ih0 = oh * s.stride_h - s.pad_h, iw0 = ow * s.stride_w - s.pad_w;
+        const T *xim = static_cast<const T *>(X) + (int64_t)img * s.h * s.w * s.c_in + c;
+        T *dst = static_cast<T *>(col) + (int64_t)m * ldcol + c;
+        for (int kh = 0; kh < s.kh; ++kh) {
+            const int ih = ih0 + kh * s.dil_h;
+            const bool row_in = ih >= 0 && ih < s.h;
+            for (int kw = 0; kw < s.kw; ++kw, dst += s.c_in) {
+                const int iw = iw0 + kw * s.dil_w;
+                const bool inside = row_in && iw >= 0 && iw < s.w;
+                if constexpr (VEC * ESIZE == 16) {
+                    u32x4 v = u32x4{0, 0, 0, 0};
+                    if (inside)
+                        v = *reinterpret_cast<const u32x4 *>(xim + ((int64_t)ih * s.w + iw) * s.c_in);
+                    *reinterpret_cast<u32x4 *>(dst) = v;
+                } else {
+                    *dst = inside ? xim[((int64_t)ih * s.w + iw) * s.c_in] : T(0);
+                }
+            }
+        }
     }
 }
 
@@ -62,15 +74,17 @@ hipError_t im2col_typed(const void *X, void *col, int64_t ldcol, const ConvShape
     const bool vec = s.c_in % V == 0 && ((uintptr_t)X & 15) == 0 && ((uintptr_t)col & 15) == 0 &&
                      ldcol % V == 0;
     const int64_t rows = (int64_t)s.n * ho * wo;
-    const int64_t total = rows * s.kh * s.kw * (vec ? s.c_in / V : s.c_in);
-    const int64_t blocks = (total + 255) / 256;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (rows == 0 || s.c_in == 0) return hipSuccess;
+    if (rows > 0x7fffffff) return hipErrorInvalidValue;
+    const int cv = vec ? s.c_in / V : s.c_in;
+    const int rows_per_block = cv >= 256 ? 1 : 256 / cv;
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (vec)
         hipLaunchKernelGGL((im2col_kernel<ESIZE, V>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                           X, col, ldcol, s, ho, wo, total);
+                           X, col, ldcol, s, ho, wo, (int)rows, rows_per_block);
     else
         hipLaunchKernelGGL((im2col_kernel<ESIZE, 1>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                           X, col, ldcol, s, ho, wo, total);
+                           X, col, ldcol, s, ho, wo, (int)rows, rows_per_block);
     return hipGetLastError();
 }
 
