@@ -197,11 +197,23 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
         }
         return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
     }
-    // Small grids: when even 64 x 64 tiles leave most CUs idle, splitting K over
-    // the narrow kernel's waves is faster (256^3: 4.1 us against 5.0 us on
-    // 64 x 64 tiles and 10.9 us on one 256 x 256 tile).
+    // Small and medium grids: the register-staged kernels walk all of K in one
+    // workgroup per tile, so with few tiles and a long K splitting K over the
+    // narrow kernel's waves is faster.  Measured on MI355X (bf16): 256^3 4.1 us
+    // narrow against 5.0 us on 64 x 64 tiles; 1 x 4096 x 1000 6.1 against 11.2;
+    // 1000 x 512 x 4096 16.7 against 45.6; 300 x 4096 x 4096 40.9 against 50.8;
+    // with 64 x 64 tiles ahead from ~256 tiles at K ~ 1000 and ~512 at K = 4096.
     const int64_t small_tiles = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
-    if (small_tiles < 64 && p.K >= 256 && h16_narrow_general_eligible(p)) return narrow();
+    if (p.K >= 256 && h16_narrow_general_eligible(p) &&
+        (small_tiles < 64 || (p.K >= 512 && small_tiles <= 128) ||
+         (p.K >= 2048 && small_tiles <= 384)))
+        return narrow();
+    // Larger grids of unaligned rows with a long K: 256 x 256 tiles of the
+    // guarded kernel even when they fill only part of the chip (2048 x 1500 x
+    // 4096: 83.6 us against 141.6 on 64 x 64 tiles, whose B transposes through
+    // registers suffer most from rows that are not 16-byte aligned).
+    if (!p.aligned && p.K >= 2048 && p.M >= 256 && p.N >= 256 && h16_general_eligible(p))
+        return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
     return to_status(h16_launch(is_bf16, h16_pick_config(p.M, p.N, p.K), p));
 }
 

@@ -6,7 +6,10 @@
 //   * one workgroup per BM x BN tile of C; the grid is remapped XCD-aware;
 //   * K is walked in steps of 64; each step's A tile (BM x 64) and B tile
 //     (64 x BN) are fetched with 16-byte global loads, out-of-range elements read
-//     as zero;
+//     as zero.  Rows need no alignment beyond the element size: the hardware
+//     runs in unaligned-access mode, so 16-byte loads and 8-byte stores at
+//     2-byte-aligned addresses are legal; only chunks that straddle the edge of
+//     a row are read or written element by element;
 //   * LDS holds two stages (ping-pong): while the waves multiply stage t, the
 //     loads of stage t+1 are in flight in registers;
 //   * A sits in LDS as rows of k (as in memory).  The MFMA needs, in every lane,
@@ -55,8 +58,7 @@ __device__ __forceinline__ u32x4 load8_guarded(const uint16_t *p, bool row_ok, i
 // ring and the XOR swizzle, for the measured optimisation ladder: without DBUF
 // each K step loads, stores to LDS, synchronises and multiplies in turn; without
 // SWZ the 16-byte chunks sit in LDS in their natural order.
-template <bool IS_BF16, int BM, int BN, int WM, int WN, bool ALIGNED, bool EPI, bool DBUF = true,
-          bool SWZ = true>
+template <bool IS_BF16, int BM, int BN, int WM, int WN, bool EPI, bool DBUF = true, bool SWZ = true>
 __global__ void __launch_bounds__(WM * WN * 64)
 h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
@@ -105,7 +107,7 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             const int row = q >> 3, c = q & 7;
             const int gm = m0 + row, gk = k0 + c * 8;
             const uint16_t *src = A + (int64_t)gm * lda + gk;
-            if (ALIGNED && gm < M && gk + 8 <= K)
+            if (gm < M && gk + 8 <= K)
                 areg[it] = *reinterpret_cast<const u32x4 *>(src);
             else
                 areg[it] = load8_guarded(src, gm < M, K - gk);
@@ -119,7 +121,7 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             for (int r = 0; r < BR; ++r) {
                 const int gk = k0 + kb * BR + r;
                 const uint16_t *src = B + (int64_t)gk * ldb + gn;
-                if (ALIGNED && gk < K && gn + 8 <= N)
+                if (gk < K && gn + 8 <= N)
                     breg[it][r] = *reinterpret_cast<const u32x4 *>(src);
                 else
                     breg[it][r] = load8_guarded(src, gk < K, N - gn);
@@ -224,7 +226,7 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 if constexpr (EPI)
                     epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(epi, ev, crow, n, N - n);
                 const float v0 = ev[0], v1 = ev[1], v2 = ev[2], v3 = ev[3];
-                if (ALIGNED && n + 4 <= N) {
+                if (n + 4 <= N) {
                     *reinterpret_cast<u32x2 *>(crow + n) =
                         u32x2{pack2<IS_BF16>(v0, v1), pack2<IS_BF16>(v2, v3)};
                 } else {
@@ -251,14 +253,9 @@ hipError_t launch_cfg_epi(const Problem &p)
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
-    if (p.aligned)
-        hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, true, EPI>), grid, block, 0,
-                           p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m,
-                           tiles_n, group_m, epi);
-    else
-        hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, false, EPI>), grid, block, 0,
-                           p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m,
-                           tiles_n, group_m, epi);
+    hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, EPI>), grid, block, 0, p.stream,
+                       A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m,
+                       epi);
     return hipGetLastError();
 }
 
@@ -297,23 +294,14 @@ hipError_t ladder_typed(int rung, const Problem &p)
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const Epilogue none{1.f, 0.f, nullptr, 0};
-#define LADDER_LAUNCH(AL, DB, SW)                                                                  \
-    hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, AL, false, DB, SW>), grid, block, \
+#define LADDER_LAUNCH(DB, SW)                                                                      \
+    hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, false, DB, SW>), grid, block,     \
                        0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, \
                        group_m, none)
     switch (rung) {
-    case 3:
-        if (p.aligned) LADDER_LAUNCH(true, false, false);
-        else LADDER_LAUNCH(false, false, false);
-        break;
-    case 4:
-        if (p.aligned) LADDER_LAUNCH(true, true, false);
-        else LADDER_LAUNCH(false, true, false);
-        break;
-    case 5:
-        if (p.aligned) LADDER_LAUNCH(true, true, true);
-        else LADDER_LAUNCH(false, true, true);
-        break;
+    case 3: LADDER_LAUNCH(false, false); break;
+    case 4: LADDER_LAUNCH(true, false); break;
+    case 5: LADDER_LAUNCH(true, true); break;
     default: return hipErrorInvalidValue;
     }
 #undef LADDER_LAUNCH
@@ -334,18 +322,19 @@ hipError_t h16_ladder_launch(int rung, bool is_bf16, const Problem &p)
 // 64 x 64 tiles against 75 us on 256 x 256 tiles, three quarters of them empty).
 int h16_pick_config(int M, int N, int K)
 {
+    // Among the register-staged kernels (the large-tile kernels take big grids
+    // before this is asked): 256 x 256 when it fills half the chip with little
+    // padding; 128 x 128 only from two tiles per CU on; else 64 x 64, which
+    // measured faster than 128 x 128 up to ~256 tiles of 128 x 128 and faster
+    // than 32 x 64 tiles on every shape tried (e.g. 2048 x 1500 x 1000: 32.5 us
+    // on 64 x 64, 48.3 on 128 x 128; 300 x 1500 x 256: 7.9 against 11.3 on
+    // 32 x 64).
     (void)K;
-    static const int bm[] = {256, 128, 64, 32}, bn[] = {256, 128, 64, 64};
-    int best = H16_32x64_W2;
-    int64_t best_tiles = -1;
-    for (int c = 0; c < 4; ++c) {
-        const int64_t tm = (M + bm[c] - 1) / bm[c], tn = (N + bn[c] - 1) / bn[c];
-        const int64_t tiles = tm * tn;
-        const bool lean = 4 * tiles * bm[c] * bn[c] <= 5 * (int64_t)M * N;
-        if (lean && tiles >= 128) return c;
-        if (tiles > best_tiles) best = c, best_tiles = tiles;
-    }
-    return best;
+    const auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const auto lean = [&](int bm, int bn) { return 4 * tiles(bm, bn) * bm * bn <= 5 * (int64_t)M * N; };
+    if (lean(256, 256) && tiles(256, 256) >= 128) return H16_256x256_W8;
+    if (lean(128, 128) && tiles(128, 128) >= 512) return H16_128x128_W4;
+    return H16_64x64_W4;
 }
 
 hipError_t h16_launch(bool is_bf16, int config, const Problem &p)

@@ -317,9 +317,14 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             uint32_t w[4] = {0, 0, 0, 0};
             if (gm < M) {
                 const uint16_t *src = A + (int64_t)gm * lda + gk;
+                if (gk + 8 <= K) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                    w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (gk + e < K) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                    for (int e = 0; e < 8; ++e)
+                        if (gk + e < K) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                }
             }
             *reinterpret_cast<u32x4 *>(as + r * BK + ((c ^ swz_a<BK>(r)) << 3)) =
                 u32x4{w[0], w[1], w[2], w[3]};
@@ -331,9 +336,14 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             uint32_t w[4] = {0, 0, 0, 0};
             if (gk < K) {
                 const uint16_t *src = B + (int64_t)gk * ldb + gn;
+                if (gn + 8 <= N) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                    w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                    for (int e = 0; e < 8; ++e)
+                        if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                }
             }
             *reinterpret_cast<u32x4 *>(bs + r * FBN + ((c ^ swz_b(r)) << 3)) =
                 u32x4{w[0], w[1], w[2], w[3]};
