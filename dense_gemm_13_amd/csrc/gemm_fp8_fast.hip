@@ -1,5 +1,6 @@
-// FP8 (OCP E4M3) block-scaled GEMM, large-tile path for gfx950: whole 256 x 256
-// tiles, K a multiple of 256, 16-byte aligned A/B/C rows.
+// FP8 (OCP E4M3) block-scaled GEMM, large-tile path for gfx950: 256 x 256
+// tiles; whole tiles with K a multiple of 256 and 16-byte aligned rows, or (the
+// guarded instantiation) any shape with N >= 16 and K > 64.
 //
 //   C[i][j] = bf16( sum_kb  sa(i/64, kb) * sb(kb, j/64) * sum_{k in block kb} qa(i,k) qb(k,j) )
 //
@@ -97,15 +98,31 @@ __device__ __forceinline__ void q_unroll(F &&f)
     q_unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// GEN = false: whole 256 x 256 tiles, K a multiple of 256, 16-byte aligned
+// rows.  GEN = true: any M, N >= 16, K > 64 and any leading dimensions (the
+// hardware runs in unaligned-access mode, so 16-byte loads at any address are
+// legal), as the guarded half-precision kernel does it:
+//   * the last K block (possibly partial) is step 0, loaded through registers
+//     with zero fill past K, M and N together with its scales; steps 1, 2, ...
+//     load blocks 0, 1, ... LDS-direct, all of them whole blocks that never
+//     touch B's last row;
+//   * A rows past M are clamped to row M-1 and B column chunks starting past N
+//     to the chunk at N-16 (their products only reach C entries that are not
+//     stored; a chunk straddling N reads a few bytes past N inside a row that is
+//     not B's last), scale rows and columns past the grids to the last ones;
+//   * after the whole turns of the ring the remaining steps run once, guarded;
+//   * C stores, and the epilogue's reads of bias and prior C, are masked to the
+//     M x N window.
 // EPI: the fused epilogue is applied to the fp32 accumulators before they are
 // rounded; the lane that reads an entry's prior C does not store it, but the
 // store depends through LDS on the value that read produced.
-template <bool EPI>
+template <bool GEN, bool EPI>
 __global__ void __launch_bounds__(QNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
-                uint16_t *__restrict__ C, int K, int64_t lda, int64_t ldb, int64_t ldc,
-                const float *__restrict__ scale_a, const float *__restrict__ scale_b,
-                int kblocks, int nblocks, int tiles_m, int tiles_n, int group_m, Epilogue epi)
+                uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
+                int64_t ldc, const float *__restrict__ scale_a, const float *__restrict__ scale_b,
+                int mblocks, int kblocks, int nblocks, int tiles_m, int tiles_n, int group_m,
+                Epilogue epi)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,15 +142,19 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
     for (int j = 0; j < QA_BLK; ++j) {
         const int row = 16 * (wave * QA_BLK + j) + (lane >> 2);
-        a_off[j] = (uint32_t)(row * lda + 16 * ((lane & 3) ^ qswz_a(row)));
+        const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
+        a_off[j] = (uint32_t)(lrow * lda + 16 * ((lane & 3) ^ qswz_a(row)));
     }
+    // (GEN: the column, n0 included, is part of the per-lane offset.)
 #pragma unroll
     for (int j = 0; j < QB_BLK; ++j) {
         const int row = 4 * (wave * QB_BLK + j) + (lane >> 4);
-        b_off[j] = (uint32_t)(row * ldb + 16 * ((lane & 15) ^ qswz_b(row)));
+        int col = 16 * ((lane & 15) ^ qswz_b(row));
+        if (GEN) col = n0 + col >= N ? N - 16 : n0 + col;
+        b_off[j] = (uint32_t)(row * ldb + col);
     }
     const uint8_t *a_base = A + (int64_t)m0 * lda;
-    const uint8_t *b_base = B + n0;
+    const uint8_t *b_base = GEN ? B : B + n0;
     const int64_t b_step = (int64_t)QBK * ldb;
     auto issue = [&](uint8_t *as, uint8_t *bs, int kt) {
         const uint8_t *ab = a_base + kt * QBK;
@@ -171,19 +192,22 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // scales, else column w - 4 of B's) with a 4-byte LDS-direct load in which
     // every lane reads the same address (no branch), so the scales travel and
     // are waited for exactly like the operands.
-    const float *sc_src = wave < 4 ? scale_a + (int64_t)(m0 / 64 + wave) * kblocks
-                                   : scale_b + n0 / 64 + (wave - 4);
+    const int sc_blk = wave < 4 ? m0 / 64 + wave : n0 / 64 + (wave - 4);
+    const float *sc_src = wave < 4 ? scale_a + (int64_t)(sc_blk < mblocks ? sc_blk : mblocks - 1) * kblocks
+                                   : scale_b + (sc_blk < nblocks ? sc_blk : nblocks - 1);
     const int64_t sc_step = wave < 4 ? 1 : nblocks;
     // This wave's scale row pair (A tiles 0,1 / 2,3) and scale column, in the slot.
     const int sc_row = wm0 / 64, sc_col = 4 + wn0 / 64;
 
-    auto issue_all = [&](auto S, int kt) {
-        issue(q_stage<S>, q_stage<QSTAGES + S>, kt);
-        __builtin_amdgcn_global_load_lds(sc_src + kt * sc_step,
+    // K step s loads K block s (GEN: block s - 1; step 0 is the last block).
+    auto issue_all = [&](auto S, int s) {
+        const int kb = GEN ? s - 1 : s;
+        issue(q_stage<S>, q_stage<QSTAGES + S>, kb);
+        __builtin_amdgcn_global_load_lds(sc_src + kb * sc_step,
                                          (lds_void8_t *)&q_scale<S>[64 * wave], 4, 0, 0);
     };
     constexpr int QLOADS = QNBLK + 1;                    // loads per wave per stage
-    const int ktiles = K / QBK;                          // a multiple of QSTAGES
+    const int ktiles = (K + QBK - 1) / QBK;              // !GEN: K / QBK, a multiple of QSTAGES
 
     f32x16 acc[QFM][QFN];
 #pragma unroll
@@ -301,11 +325,59 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     // Prologue: K steps 0 .. QSTAGES-1 in flight, stage 0 published, its
     // fragments and scales read.  The partial set the first slot promotes is
-    // zero (with zero scales).  Steps past the end re-load the last K block into
-    // stages nobody reads any more, and the last step's look-ahead reads a
-    // stage whose contents are not used.
-    q_unroll<QSTAGES>([&](auto S) { issue_all(S, (int)S); });
-    q_wait_vmcnt<(QSTAGES - 1) * QLOADS>();
+    // zero (with zero scales).  Steps past the end re-load the last K block
+    // moved LDS-direct into stages nobody reads any more, and the last step's
+    // look-ahead reads a stage whose contents are not used.
+    // GEN: step 0 is the last K block [QBK*(ktiles-1), K), through registers
+    // with zero fill, in the swizzled layout the LDS-direct loads produce, with
+    // its scales (written before any LDS-direct load is issued).
+    if constexpr (GEN) {
+        const int k0 = QBK * (ktiles - 1);
+        uint8_t *as = q_stage<0>, *bs = q_stage<QSTAGES>;
+        for (int q = tid; q < QBM * QBK / 16; q += QNW * 64) {
+            const int r = q >> 2, c = q & 3;
+            const int gm = m0 + r, gk = k0 + 16 * c;
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (gm < M) {
+                const uint8_t *src = A + (int64_t)gm * lda + gk;
+                if (gk + 16 <= K) {
+                    v = *reinterpret_cast<const u32x4 *>(src);
+                } else {
+                    uint32_t w[4] = {0, 0, 0, 0};
+                    for (int e = 0; e < 16; ++e)
+                        if (gk + e < K) w[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+                    v = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+            *reinterpret_cast<u32x4 *>(as + r * QBK + ((c ^ qswz_a(r)) << 4)) = v;
+        }
+        for (int q = tid; q < QBK * QBN / 16; q += QNW * 64) {
+            const int r = q >> 4, c = q & 15;
+            const int gk = k0 + r, gn = n0 + 16 * c;
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (gk < K) {
+                const uint8_t *src = B + (int64_t)gk * ldb + gn;
+                if (gn + 16 <= N) {
+                    v = *reinterpret_cast<const u32x4 *>(src);
+                } else {
+                    uint32_t w[4] = {0, 0, 0, 0};
+                    for (int e = 0; e < 16; ++e)
+                        if (gn + e < N) w[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+                    v = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+            *reinterpret_cast<u32x4 *>(bs + r * QBN + ((c ^ qswz_b(r)) << 4)) = v;
+        }
+        q_scale<0>[64 * wave + lane] = sc_src[(int64_t)(ktiles - 1) * sc_step];
+        q_unroll<QSTAGES - 1>([&](auto S) {
+            constexpr int S1 = S + 1;
+            issue_all(std::integral_constant<int, S1>{}, S1 < ktiles ? S1 : ktiles - 1);
+        });
+        __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): the LDS writes landed
+    } else {
+        q_unroll<QSTAGES>([&](auto S) { issue_all(S, (int)S); });
+        q_wait_vmcnt<(QSTAGES - 1) * QLOADS>();
+    }
     q_barrier();
 #pragma unroll
     for (int i = 0; i < QFM; ++i) read_a(q_stage<0>, i);
@@ -313,8 +385,19 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     for (int j = 0; j < QFN; ++j) read_b(q_stage<QSTAGES>, j);
     read_scales(q_scale<0>);
     part[(NT - 1) & 1] = f32x16{};
-    for (int kt = 0; kt < ktiles; kt += QSTAGES)
+    // Whole turns of the ring without conditions (a step skipped at run time
+    // would let the compiler merge the steps' code and lose track of which
+    // stage array each LDS read addresses).  GEN: the remaining ktiles % QSTAGES
+    // steps follow, once.
+    const int kwhole = GEN ? ktiles - ktiles % QSTAGES : ktiles;
+    for (int kt = 0; kt < kwhole; kt += QSTAGES)
         q_unroll<QSTAGES>([&](auto S) { step(S, kt + S); });
+    if constexpr (GEN) {
+        const int rem = ktiles - kwhole;
+        q_unroll<QSTAGES - 1>([&](auto S) {
+            if (S < rem) step(S, kwhole + S);
+        });
+    }
     promote(NT - 1, ps0, ps1);
     q_wait_vmcnt<0>();
 
@@ -330,8 +413,10 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
         for (int j = 0; j < QFN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                epilogue_bias<4>(epi, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4, ebias[j][q]);
+            for (int q = 0; q < 4; ++q) {
+                const int gn = n0 + wn0 + 32 * j + 8 * q + 4 * half;
+                epilogue_bias<4>(epi, gn, GEN ? N - gn : 4, ebias[j][q]);
+            }
     }
 #pragma unroll
     for (int i = 0; i < QFM; ++i) {
@@ -340,14 +425,17 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const int hsw = half ^ ((row >> 3) & 1);
         if constexpr (EPI) {
             // The prior C of the row's entries first, then the arithmetic.
-            const uint16_t *crow = C + (int64_t)(m0 + wm0 + row) * ldc;
+            const bool row_in = !GEN || m0 + wm0 + row < M;
+            const uint16_t *crow = C + (int64_t)(row_in ? m0 + wm0 + row : 0) * ldc;
             float prior[QFN][4][4];
 #pragma unroll
             for (int j = 0; j < QFN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    epilogue_prior<OUT_BF16, 4>(epi, crow, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4,
+                for (int q = 0; q < 4; ++q) {
+                    const int gn = n0 + wn0 + 32 * j + 8 * q + 4 * half;
+                    epilogue_prior<OUT_BF16, 4>(epi, crow, gn, !row_in ? 0 : GEN ? N - gn : 4,
                                                 prior[j][q]);
+                }
 #pragma unroll
             for (int j = 0; j < QFN; ++j)
 #pragma unroll
@@ -376,7 +464,21 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const int row = 8 * it + (lane >> 3);
         u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * QWTN + ((cl ^ (row & 7)) << 3));
         if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        *reinterpret_cast<u32x4 *>(cbase + (int64_t)row * ldc + 8 * cl) = v;
+        uint16_t *dst = cbase + (int64_t)row * ldc + 8 * cl;
+        if (!GEN) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+            const int gm = m0 + wm0 + row, gn = n0 + wn0 + 8 * cl;
+            if (gm < M) {
+                if (gn + 8 <= N) {
+                    *reinterpret_cast<u32x4 *>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (gn + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
     }
 }
 
@@ -390,24 +492,47 @@ bool fp8_fast_eligible(const Problem &p)
            p.lda < (1 << 23) && p.ldb < (1 << 24);
 }
 
-hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b)
+// The guarded instantiation: any M, N >= 16 (a clamped column chunk starts at
+// N - 16), two K blocks at least, and per-lane 32-bit byte offsets that fit (256
+// rows of A from the tile's first row; 64 rows of B plus the column).
+bool fp8_general_eligible(const Problem &p)
 {
-    if (!fp8_fast_eligible(p)) return hipErrorInvalidValue;
-    const int tiles_m = p.M / QBM, tiles_n = p.N / QBN;
+    return p.M >= 1 && p.N >= 16 && p.K > QBK && p.lda < (1 << 23) &&
+           (int64_t)QBK * p.ldb + p.N < ((int64_t)1 << 31);
+}
+
+template <bool GEN>
+static hipError_t fp8_fast_typed(const Problem &p, const float *scale_a, const float *scale_b)
+{
+    const int tiles_m = (p.M + QBM - 1) / QBM, tiles_n = (p.N + QBN - 1) / QBN;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
     const uint8_t *A = static_cast<const uint8_t *>(p.A), *B = static_cast<const uint8_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
+    const int mblocks = (p.M + 63) / 64, kblocks = (p.K + 63) / 64, nblocks = (p.N + 63) / 64;
+    const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (p.epi)
-        hipLaunchKernelGGL(fp8_fast_kernel<true>, dim3((unsigned)nwg), dim3(QNW * 64), 0, p.stream,
-                           A, B, C, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b, p.K / 64, p.N / 64,
-                           tiles_m, tiles_n, group_m, *p.epi);
+        hipLaunchKernelGGL((fp8_fast_kernel<GEN, true>), dim3((unsigned)nwg), dim3(QNW * 64), 0,
+                           p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b,
+                           mblocks, kblocks, nblocks, tiles_m, tiles_n, group_m, epi);
     else
-        hipLaunchKernelGGL(fp8_fast_kernel<false>, dim3((unsigned)nwg), dim3(QNW * 64), 0,
-                           p.stream, A, B, C, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b, p.K / 64,
-                           p.N / 64, tiles_m, tiles_n, group_m, Epilogue{1.f, 0.f, nullptr, 0});
+        hipLaunchKernelGGL((fp8_fast_kernel<GEN, false>), dim3((unsigned)nwg), dim3(QNW * 64), 0,
+                           p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b,
+                           mblocks, kblocks, nblocks, tiles_m, tiles_n, group_m, epi);
     return hipGetLastError();
+}
+
+hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b)
+{
+    if (!fp8_fast_eligible(p)) return hipErrorInvalidValue;
+    return fp8_fast_typed<false>(p, scale_a, scale_b);
+}
+
+hipError_t fp8_general_launch(const Problem &p, const float *scale_a, const float *scale_b)
+{
+    if (!fp8_general_eligible(p)) return hipErrorInvalidValue;
+    return fp8_fast_typed<true>(p, scale_a, scale_b);
 }
 
 }  // namespace gemm

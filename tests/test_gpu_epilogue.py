@@ -121,14 +121,18 @@ def test_f32_paths(small):
     check("f32", ops, M, N, K, 1.5, 0.25, True, "relu", 60 + small, "f32", **kw)
 
 
-@pytest.mark.parametrize("small", [False, True])
-def test_fp8_paths(small):
-    if small:
-        os.environ["LIBGEMM_FP8_SMALL"] = "1"
-    M, N, K = (512, 512, 512) if not small else (200, 136, 320)
-    kw = {} if not small else dict(ldc=139)
+@pytest.mark.parametrize("path", ["large", "small", "guarded"])
+def test_fp8_paths(path):
+    """The large-tile kernel, the register-staged kernels ('1') and the guarded
+    large-tile kernel ('2', ragged shape, unaligned leading dimensions)."""
+    if path != "large":
+        os.environ["LIBGEMM_FP8_SMALL"] = "1" if path == "small" else "2"
+    M, N, K = {"large": (512, 512, 512), "small": (200, 136, 320), "guarded": (300, 270, 200)}[path]
+    kw = {"large": {}, "small": dict(ldc=139),
+          "guarded": dict(lda=203, ldb=275, ldc=277, offset=1)}[path]
     ops = gi.operands("fp8", M, N, K, 61)
-    check("fp8", ops, M, N, K, 0.5, 1.0, True, "relu", 61 + small, "fp8", **kw)
+    seed = {"large": 61, "small": 62, "guarded": 63}[path]
+    check("fp8", ops, M, N, K, 0.5, 1.0, True, "relu", seed, "fp8 " + path, **kw)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "fp8"])

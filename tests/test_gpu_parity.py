@@ -31,9 +31,11 @@ NARROW_GEN = 7    # the same kernel, guarded: any M, N >= 8, K >= 1, any leading
 
 @pytest.fixture(autouse=True)
 def _clear_config_override():
-    os.environ.pop("LIBGEMM_H16_CONFIG", None)
+    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_FP8_SMALL"):
+        os.environ.pop(v, None)
     yield
-    os.environ.pop("LIBGEMM_H16_CONFIG", None)
+    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_FP8_SMALL"):
+        os.environ.pop(v, None)
 
 
 def _encode(x, dtype):
@@ -165,6 +167,39 @@ def test_fp8_full_ragged(shape):
 def test_fp8_large_tile_path(shape):
     """Whole 256x256 tiles and K % 256 == 0 take the large-tile fp8 kernel."""
     _full_check("fp8", *shape, 6, "fp8_large")
+
+
+@pytest.mark.parametrize("shape,lds", [
+    ((300, 500, 320), None),                  # ragged M and N; 5 K blocks: one turn of the ring + 1
+    ((257, 300, 129), None),                  # one row past a tile; partial last K block
+    ((33, 17, 65), None),                     # partial tiles both ways, two K blocks, N barely >= 16
+    ((520, 270, 1000), (1003, 277, 281)),     # unaligned leading dimensions, offset pointers
+    ((256, 256, 448), None),                  # whole tiles, 7 K blocks: a guarded remainder of 3 steps
+    ((600, 700, 832), (840, 704, 712)),       # several tiles each way, 13 K blocks
+])
+def test_fp8_guarded_large_tile_path(shape, lds):
+    """The guarded large-tile fp8 kernel (testing override '2'): clamped rows and
+    column chunks, the partial last K block through registers, masked stores."""
+    os.environ["LIBGEMM_FP8_SMALL"] = "2"
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[fp8-guarded] {M}x{N}x{K} {kw}")
+    ops = gi.operands("fp8", M, N, K, 64)
+    _, got = run_gemm("fp8", ops, M, N, K, **kw)
+    ok, msg, _ = compare("fp8", got, reference("fp8", ops, M, N, K), "fp8-guarded")
+    assert ok, msg
+
+
+def test_fp8_guarded_permutation_exact():
+    M, K = 300, 320
+    os.environ["LIBGEMM_FP8_SMALL"] = "2"
+    say("[probe] fp8 guarded large-tile A*P")
+    ops, perm = _perm_case("fp8", M, K, 13)
+    _, got = run_gemm("fp8", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "fp8")
+    bad = np.argwhere(oracle.decode(got, "bf16") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
 
 
 @pytest.mark.parametrize("shape", [(128, 128, 64), (384, 256, 320), (1024, 640, 2048)])
