@@ -226,8 +226,21 @@ hipError_t launch_cfg(const Problem &p)
 
 hipError_t f32_launch(const Problem &p)
 {
-    const char *e = std::getenv("LIBGEMM_F32_SMALL");   // testing: force the general kernel
-    if (f32_fast_eligible(p) && !(e && e[0] == '1')) return f32_fast_launch(p);
+    // Testing override LIBGEMM_F32_SMALL: '1' forces the register-staged kernels
+    // below, '2' the guarded large-tile kernel and '3' the whole-tile large-tile
+    // kernel (each where it is eligible).
+    const char *e = std::getenv("LIBGEMM_F32_SMALL");
+    const int force = e && e[0] >= '1' && e[0] <= '3' ? e[0] - '0' : 0;
+    if (force == 3 && f32_fast_eligible(p)) return f32_fast_launch(p);
+    // The large-tile kernels (whole tiles, else guarded) once the grid has at
+    // least 128 tiles of 128 x 128; below that the register-staged kernels fill
+    // the chip better.  Measured: 4097 x 4095 x 4100 1321 us guarded against
+    // 2249 register-staged; 2000 x 3000 x 1000 144 against 227; but 1000^3 74
+    // against 43 and 256^3 (whole tiles) 21.6 against 10.5.
+    const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
+    if (force == 0 && tiles128 >= 128 && f32_fast_eligible(p)) return f32_fast_launch(p);
+    if ((force == 2 || (force == 0 && tiles128 >= 128)) && f32_general_eligible(p))
+        return f32_general_launch(p);
     const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
     if (big >= 128) return launch_cfg<128, 128, 2, 2>(p);
     return launch_cfg<64, 64, 2, 2>(p);

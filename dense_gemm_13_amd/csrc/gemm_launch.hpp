@@ -63,6 +63,8 @@ hipError_t mfma_ceiling_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p);
 bool f32_fast_eligible(const Problem &p);
 hipError_t f32_fast_launch(const Problem &p);
+bool f32_general_eligible(const Problem &p);
+hipError_t f32_general_launch(const Problem &p);
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
 bool fp8_fast_eligible(const Problem &p);
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);

@@ -111,14 +111,18 @@ def test_h16_paths(dtype, case):
     check(dtype, ops, M, N, K, 0.75, -0.5, True, act, case, f"config {config}", **kw)
 
 
-@pytest.mark.parametrize("small", [False, True])
-def test_f32_paths(small):
-    if small:
-        os.environ["LIBGEMM_F32_SMALL"] = "1"
-    M, N, K = (256, 384, 256) if not small else (200, 136, 77)
-    kw = {} if not small else dict(lda=80, ldb=139, ldc=141, offset=1)
+@pytest.mark.parametrize("path", ["large", "small", "guarded"])
+def test_f32_paths(path):
+    """The whole-tile large-tile kernel ('3'), the register-staged kernels ('1')
+    and the guarded large-tile kernel ('2', ragged shape, unaligned leading
+    dimensions)."""
+    os.environ["LIBGEMM_F32_SMALL"] = {"large": "3", "small": "1", "guarded": "2"}[path]
+    M, N, K = {"large": (256, 384, 256), "small": (200, 136, 77), "guarded": (300, 270, 200)}[path]
+    kw = {"large": {}, "small": dict(lda=80, ldb=139, ldc=141, offset=1),
+          "guarded": dict(lda=203, ldb=275, ldc=277, offset=1)}[path]
     ops = gi.operands("f32", M, N, K, 60)
-    check("f32", ops, M, N, K, 1.5, 0.25, True, "relu", 60 + small, "f32", **kw)
+    seed = {"large": 60, "small": 61, "guarded": 64}[path]
+    check("f32", ops, M, N, K, 1.5, 0.25, True, "relu", seed, "f32 " + path, **kw)
 
 
 @pytest.mark.parametrize("path", ["large", "small", "guarded"])

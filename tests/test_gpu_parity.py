@@ -31,10 +31,10 @@ NARROW_GEN = 7    # the same kernel, guarded: any M, N >= 8, K >= 1, any leading
 
 @pytest.fixture(autouse=True)
 def _clear_config_override():
-    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_FP8_SMALL"):
+    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_FP8_SMALL", "LIBGEMM_F32_SMALL"):
         os.environ.pop(v, None)
     yield
-    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_FP8_SMALL"):
+    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_FP8_SMALL", "LIBGEMM_F32_SMALL"):
         os.environ.pop(v, None)
 
 
@@ -202,14 +202,50 @@ def test_fp8_guarded_permutation_exact():
     assert bad.size == 0, f"first mismatch at {bad[0]}"
 
 
+@pytest.mark.parametrize("shape,lds", [
+    ((300, 500, 320), None),                  # ragged M and N; 10 K blocks
+    ((129, 130, 97), None),                   # one row / two columns past a tile; partial last K block
+    ((33, 5, 33), None),                      # partial tiles both ways, two K blocks, N barely >= 4
+    ((520, 270, 1000), (1003, 277, 281)),     # unaligned leading dimensions, offset pointers
+    ((256, 256, 96), None),                   # whole tiles, 3 K blocks: an odd count of steps
+])
+def test_f32_guarded_large_tile_path(shape, lds):
+    """The guarded large-tile fp32 kernel (testing override '2'): clamped rows and
+    column chunks, the partial last K block through registers, masked stores."""
+    os.environ["LIBGEMM_F32_SMALL"] = "2"
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[f32-guarded] {M}x{N}x{K} {kw}")
+    ops = gi.operands("f32", M, N, K, 65)
+    _, got = run_gemm("f32", ops, M, N, K, **kw)
+    ok, msg, _ = compare("f32", got, reference("f32", ops, M, N, K), "f32-guarded")
+    assert ok, msg
+
+
+def test_f32_guarded_permutation_exact():
+    M, K = 300, 160
+    os.environ["LIBGEMM_F32_SMALL"] = "2"
+    say("[probe] f32 guarded large-tile A*P")
+    ops, perm = _perm_case("f32", M, K, 15)
+    _, got = run_gemm("f32", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "f32")
+    bad = np.argwhere(oracle.decode(got, "f32") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 @pytest.mark.parametrize("shape", [(128, 128, 64), (384, 256, 320), (1024, 640, 2048)])
 def test_f32_large_tile_path(shape):
-    """Whole 128x128 tiles and K % 64 == 0 take the large-tile fp32 kernel."""
+    """Whole 128x128 tiles and K % 64 == 0: the large-tile fp32 kernel (forced
+    with the testing override '3': by default grids this small take the
+    register-staged kernels)."""
+    os.environ["LIBGEMM_F32_SMALL"] = "3"
     _full_check("f32", *shape, 7, "f32_large")
 
 
 def test_f32_large_tile_permutation_exact():
     M, K = 384, 512
+    os.environ["LIBGEMM_F32_SMALL"] = "3"
     say("[probe] f32 large-tile A*P")
     ops, perm = _perm_case("f32", M, K, 11)
     _, got = run_gemm("f32", ops, M, K, K)
