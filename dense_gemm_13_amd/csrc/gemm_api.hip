@@ -157,7 +157,9 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             (forced != H16_FAST_256x256 || h16_fast_eligible(p)) &&
             (forced != H16_GEN_256x256 || h16_general_eligible(p)) &&
             (forced != H16_NARROW_32x64 || h16_narrow_eligible(p)) &&
-            (forced != H16_NARROW_GEN || h16_narrow_general_eligible(p)))
+            (forced != H16_NARROW_GEN || h16_narrow_general_eligible(p)) &&
+            (forced != H16_NARROW64 || h16_narrow64_eligible(p)) &&
+            (forced != H16_NARROW64_GEN || h16_narrow_general_eligible(p)))
             return to_status(h16_launch(is_bf16, forced, p));
     }
     // The large-tile kernel, when its grid of 256 x 256 tiles fills at least half
@@ -170,7 +172,13 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     // (8192 x 64 x 4096: 21 us against 47 us on 64 x 64 tiles; with K = 576 the
     // split leaves each wave two blocks and 64 x 64 tiles are twice as fast).
     const int64_t narrow_tiles = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64);
+    // 64-row tiles when 32-row tiles would need a second round of workgroups
+    // (one per CU; 1000^3: 512 tiles of 32 x 64, 256 of 64 x 64).
     const auto narrow = [&]() {
+        const int64_t t32 = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64);
+        if (t32 > cus && p.M >= 64)
+            return to_status(h16_launch(
+                is_bf16, h16_narrow64_eligible(p) ? H16_NARROW64 : H16_NARROW64_GEN, p));
         return to_status(h16_launch(
             is_bf16, h16_narrow_eligible(p) ? H16_NARROW_32x64 : H16_NARROW_GEN, p));
     };
@@ -202,11 +210,22 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     // narrow kernel's waves is faster.  Measured on MI355X (bf16): 256^3 4.1 us
     // narrow against 5.0 us on 64 x 64 tiles; 1 x 4096 x 1000 6.1 against 11.2;
     // 1000 x 512 x 4096 16.7 against 45.6; 300 x 4096 x 4096 40.9 against 50.8;
-    // with 64 x 64 tiles ahead from ~256 tiles at K ~ 1000 and ~512 at K = 4096.
+    // 1000^3 (64-row narrow tiles, one round) 11.8 against 18.1; with 64 x 64
+    // tiles ahead at short K (1000 x 1000 x 250: 7.1 against 11.0) and beyond
+    // ~256 tiles at K ~ 1000 (2048 x 1024 x 1024: 14.3 against 18.7).
     const int64_t small_tiles = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
     if (p.K >= 256 && h16_narrow_general_eligible(p) &&
-        (small_tiles < 64 || (p.K >= 512 && small_tiles <= 128) ||
+        (small_tiles < 64 || (p.K >= 512 && small_tiles <= 256) ||
          (p.K >= 2048 && small_tiles <= 384)))
+        return narrow();
+    // Rows that are not 16-byte aligned slow the 64 x 64 tiles (their B
+    // transposes go through registers), so the narrow kernel's 64-row tiles stay
+    // ahead for up to three rounds of tiles: 1000 x 1500 x 1000 21.3 us against
+    // 27.6, 1500^3 43.4 against 53.5, 2048 x 1500 x 4096 71.3 against 83.4 on
+    // the guarded 256 x 256 tiles; not at K ~ 1000 with three rounds (2048 x 1500
+    // x 1000: 36.4 against 32.4).
+    if (!p.aligned && p.M >= 64 && h16_narrow_general_eligible(p) &&
+        ((p.K >= 768 && small_tiles <= 576) || (p.K >= 2048 && small_tiles <= 768)))
         return narrow();
     // Larger grids of unaligned rows with a long K: 256 x 256 tiles of the
     // guarded kernel even when they fill only part of the chip (2048 x 1500 x

@@ -27,6 +27,8 @@
 // register-tiled GEMM in "CUDA GEMM 优化实践笔记" (blocks of K accumulated
 // separately, then added), here inside one workgroup; operand movement and
 // fragment reads are those of the large-tile kernel (gemm_h16_fast.hip).
+#include <type_traits>
+
 #include "gemm_device.hpp"
 #include "gemm_launch.hpp"
 
@@ -38,14 +40,14 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_n_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_n_t;
 
-constexpr int NBM = 32, NBN = 64, NBK = 64;
+// Two shapes of the same kernel: 32 x 64 tiles with a 3-stage ring per wave
+// (144 KiB of LDS), and 64 x 64 tiles with a 2-stage ring (128 KiB) for grids
+// that would need a second round of 32-row tiles (one workgroup per CU either
+// way): 1000^3 has 512 tiles of 32 x 64 but 256 of 64 x 64.
+constexpr int NBN = 64, NBK = 64;
 constexpr int NNW = 4;                                   // waves, each its own K blocks
-constexpr int NSTAGES = 3;
-constexpr int NA_WAVE = NBM * NBK;                       // halves of A per wave and stage (4 KiB)
 constexpr int NB_WAVE = NBK * NBN;                       // halves of B per wave and stage (8 KiB)
-constexpr int NA_BLK = NA_WAVE * 2 / 1024;               // 1 KiB loads per wave and stage
-constexpr int NB_BLK = NB_WAVE * 2 / 1024;
-constexpr int NBLK_N = NA_BLK + NB_BLK;
+constexpr int NB_BLK = NB_WAVE * 2 / 1024;               // 1 KiB loads per wave and stage
 
 template <int TAG, int HALVES>
 __shared__ __attribute__((aligned(1024))) uint16_t nl_stage[HALVES];
@@ -65,19 +67,36 @@ __device__ __forceinline__ void n_wait()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-template <int S>
-__device__ __forceinline__ uint16_t *a_stage() { return nl_stage<S, NNW * NA_WAVE>; }
-template <int S>
-__device__ __forceinline__ uint16_t *b_stage() { return nl_stage<NSTAGES + S, NNW * NB_WAVE>; }
+// One 16-byte global -> LDS load per lane (lane t's bytes land at lds + 16t).
+// (A function of its own: with arguments that depend on the kernel's template
+// parameters, the builtin called directly in the kernel's lambdas leaves the
+// host-side instantiation of the kernel invalid and its launch stub undefined.)
+__device__ __forceinline__ void n_dma16(const void *src, uint16_t *lds)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void_n_t *)lds, 16, 0, 0);
+}
+
+// This workgroup's A and B arrays of stage S (A stages first, then B).
+template <int S, int TBM>
+__device__ __forceinline__ uint16_t *a_stage() { return nl_stage<S, NNW * TBM * NBK>; }
+template <int S, int STG>
+__device__ __forceinline__ uint16_t *b_stage() { return nl_stage<STG + S, NNW * NB_WAVE>; }
 
 // EPI: the fused epilogue is applied to the reduced fp32 sums before rounding
 // (the thread that reads an entry's prior C is the one that stores it).
-template <bool IS_BF16, bool GEN, bool EPI>
+// TBM: tile rows (32 or 64); STG: LDS stages per wave (3 or 2).
+template <bool IS_BF16, bool GEN, bool EPI, int TBM, int STG>
 __global__ void __launch_bounds__(NNW * 64)
 h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                   uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
                   int64_t ldc, int tiles_n, Epilogue epi)
 {
+    static_assert((TBM == 32 && STG == 3) || (TBM == 64 && STG == 2), "narrow shapes");
+    constexpr int NBM = TBM;
+    constexpr int NA_WAVE = NBM * NBK;                   // halves of A per wave and stage
+    constexpr int NA_BLK = NA_WAVE * 2 / 1024;           // 1 KiB loads per wave and stage
+    constexpr int NBLK_N = NA_BLK + NB_BLK;
+    constexpr int FM = NBM / 32;                         // 32-row MFMA tiles
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,16 +143,21 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
         const char *bb = b_base + (int64_t)kb * NBK * ldb * 2;
 #pragma unroll
         for (int j = 0; j < NA_BLK; ++j)
-            __builtin_amdgcn_global_load_lds(ab + a_off[j], (lds_void_n_t *)(as + wave * NA_WAVE + 512 * j), 16, 0, 0);
+            n_dma16(ab + a_off[j], as + wave * NA_WAVE + 512 * j);
 #pragma unroll
         for (int j = 0; j < NB_BLK; ++j)
-            __builtin_amdgcn_global_load_lds(bb + b_off_g[j], (lds_void_n_t *)(bs + wave * NB_WAVE + 512 * j), 16, 0, 0);
+            n_dma16(bb + b_off_g[j], bs + wave * NB_WAVE + 512 * j);
     };
 
     // Fragments (in halves, relative to this wave's part of a stage): A as in
     // the large-tile kernel with 128-byte rows; B from two transposing reads
     // per 32-column tile and 16-wide K sub-step.
-    const int a_row = l32 * NBK, a_sw = swz8(l32);
+    int a_row[FM], a_sw[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        a_row[i] = (32 * i + l32) * NBK;
+        a_sw[i] = swz8(32 * i + l32);
+    }
     const int g = lane >> 4, w16 = lane & 15, r4 = w16 >> 2, c4 = w16 & 3;
     int b_off[2];
 #pragma unroll
@@ -143,14 +167,18 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
     }
     const int b_krow = 8 * (g >> 1) + r4;
 
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    f32x16 acc[FM][2];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[i][0] = acc[i][1] = f32x16{};
     auto compute = [&](const uint16_t *as, const uint16_t *bs) {
         as += wave * NA_WAVE;
         bs += wave * NB_WAVE;
-        u32x4 af[NBK / 16], bf[NBK / 16][2];
+        u32x4 af[NBK / 16][FM], bf[NBK / 16][2];
 #pragma unroll
         for (int s = 0; s < NBK / 16; ++s) {
-            af[s] = *reinterpret_cast<const u32x4 *>(as + a_row + (((2 * s + half) ^ a_sw) << 3));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[s][i] = *reinterpret_cast<const u32x4 *>(as + a_row[i] + (((2 * s + half) ^ a_sw[i]) << 3));
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const uint16_t *p0 = bs + (16 * s + b_krow) * NBN + b_off[j];
@@ -163,25 +191,29 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
 #pragma unroll
         for (int s = 0; s < NBK / 16; ++s)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[j] = mfma32x32x16<IS_BF16>(bf[s][j], af[s], acc[j]);
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma32x32x16<IS_BF16>(bf[s][j], af[s][i], acc[i][j]);
     };
 
-    // Step t: this wave's loads of stage t % NSTAGES have landed once at most
-    // one later step's loads are outstanding; the stage refilled now (step
-    // t + NSTAGES - 1) was read by step t - 1, whose LDS reads have returned.
+    // Step t: this wave's loads of stage t % STG have landed once at most
+    // STG - 2 later steps' loads are outstanding; the stage refilled now (step
+    // t + STG - 1) was read by step t - 1, whose LDS reads have returned.
     // Steps past nsteps re-load the last block into stages nobody reads and
     // skip the MFMAs.
     if (nsteps > 0) {
-        issue(a_stage<0>(), b_stage<0>(), 0);
-        issue(a_stage<1>(), b_stage<1>(), 1);
+        issue(a_stage<0, TBM>(), b_stage<0, STG>(), 0);
+        if constexpr (STG == 3) issue(a_stage<1, TBM>(), b_stage<1, STG>(), 1);
     }
     // GEN: the last K block through registers, zero-filled past M, N and K, in
-    // the layout the LDS-direct loads produce, into this wave's part of stage 2
-    // (refilled only once the loop's first step has waited for these reads).
+    // the layout the LDS-direct loads produce, into this wave's part of the
+    // last stage (refilled only once the loop's first step has waited for
+    // these reads).
     if (GEN && wave == kdma % NNW) {
         const int k0 = NBK * kdma;
-        uint16_t *as = a_stage<2>() + wave * NA_WAVE;
-        uint16_t *bs = b_stage<2>() + wave * NB_WAVE;
+        uint16_t *as = a_stage<STG - 1, TBM>() + wave * NA_WAVE;
+        uint16_t *bs = b_stage<STG - 1, STG>() + wave * NB_WAVE;
 #pragma unroll
         for (int q = lane; q < NBM * NBK / 8; q += 64) {
             const int r = q >> 3, c = q & 7;
@@ -219,83 +251,107 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
             *reinterpret_cast<u32x4 *>(bs + r * NBN + ((c ^ swz_nb(r)) << 3)) = u32x4{w[0], w[1], w[2], w[3]};
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): the LDS writes landed
-        compute(a_stage<2>(), b_stage<2>());
+        compute(a_stage<STG - 1, TBM>(), b_stage<STG - 1, STG>());
     }
-    for (int t = 0; t < nsteps; t += NSTAGES) {
-        n_wait<NBLK_N>();
-        issue(a_stage<2>(), b_stage<2>(), t + 2);
-        compute(a_stage<0>(), b_stage<0>());
-        n_wait<NBLK_N>();
-        issue(a_stage<0>(), b_stage<0>(), t + 3);
-        if (t + 1 < nsteps) compute(a_stage<1>(), b_stage<1>());
-        n_wait<NBLK_N>();
-        issue(a_stage<1>(), b_stage<1>(), t + 4);
-        if (t + 2 < nsteps) compute(a_stage<2>(), b_stage<2>());
+    if constexpr (STG == 3) {
+        for (int t = 0; t < nsteps; t += 3) {
+            n_wait<NBLK_N>();
+            issue(a_stage<2, TBM>(), b_stage<2, STG>(), t + 2);
+            compute(a_stage<0, TBM>(), b_stage<0, STG>());
+            n_wait<NBLK_N>();
+            issue(a_stage<0, TBM>(), b_stage<0, STG>(), t + 3);
+            if (t + 1 < nsteps) compute(a_stage<1, TBM>(), b_stage<1, STG>());
+            n_wait<NBLK_N>();
+            issue(a_stage<1, TBM>(), b_stage<1, STG>(), t + 4);
+            if (t + 2 < nsteps) compute(a_stage<2, TBM>(), b_stage<2, STG>());
+        }
+    } else {
+        for (int t = 0; t < nsteps; t += 2) {
+            n_wait<0>();
+            issue(a_stage<1, TBM>(), b_stage<1, STG>(), t + 1);
+            compute(a_stage<0, TBM>(), b_stage<0, STG>());
+            n_wait<0>();
+            issue(a_stage<0, TBM>(), b_stage<0, STG>(), t + 2);
+            if (t + 1 < nsteps) compute(a_stage<1, TBM>(), b_stage<1, STG>());
+        }
     }
     n_wait<0>();
 
-    // Partial tiles into LDS (this wave's own 8 KiB of B stage 0 as 32 rows of
-    // 64 floats; 16-byte chunk index XOR row, so the 32 rows one store touches
-    // spread over the banks).  Lane l holds row l%32, columns 32j + 8q +
-    // 4*(l/32) .. +3.
-    float *red = reinterpret_cast<float *>(b_stage<0>());
-    {
-        float *mine = red + wave * (NBM * NBN);
+    // Partial tiles into LDS: 32-row tile i of every wave goes to B stage i
+    // (this wave's own 8 KiB of it as 32 rows of 64 floats; 16-byte chunk index
+    // XOR row, so the 32 rows one store touches spread over the banks).  Lane l
+    // holds row l%32 of the tile, columns 32j + 8q + 4*(l/32) .. +3.  Each stage
+    // array holds exactly the four waves' 32 x 64 fp32 partials.
+    const auto store_partial = [&](auto I) {
+        float *mine = reinterpret_cast<float *>(b_stage<I, STG>()) + wave * (32 * NBN);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int chunk = (8 * j + 2 * q + half) ^ (l32 & 15);
                 *reinterpret_cast<f32x4 *>(mine + l32 * NBN + 4 * chunk) =
-                    f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    f32x4{acc[I][j][4 * q], acc[I][j][4 * q + 1], acc[I][j][4 * q + 2],
+                          acc[I][j][4 * q + 3]};
             }
-    }
+    };
+    store_partial(std::integral_constant<int, 0>{});
+    if constexpr (FM == 2) store_partial(std::integral_constant<int, 1>{});
     __syncthreads();
-    // Thread t sums row t/8, columns 8(t%8) .. +7 over the four partials.
-    const int row = tid >> 3, c8 = tid & 7;
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // Thread t sums row t/8 of each 32-row tile, columns 8(t%8) .. +7, over the
+    // four partials, then applies the epilogue, rounds and stores.
+    const int rr = tid >> 3, c8 = tid & 7;
+    const auto finish = [&](auto I) {
+        const int row = 32 * I + rr;
+        const float *red = reinterpret_cast<const float *>(b_stage<I, STG>());
+        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < NNW; ++w) {
-        const float *part = red + w * (NBM * NBN) + row * NBN;
+        for (int w = 0; w < NNW; ++w) {
+            const float *part = red + w * (32 * NBN) + rr * NBN;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(part + 4 * ((2 * c8 + h) ^ (row & 15)));
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(part + 4 * ((2 * c8 + h) ^ (rr & 15)));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * h + e] += v[e];
+                for (int e = 0; e < 4; ++e) s[4 * h + e] += v[e];
+            }
         }
-    }
-    if constexpr (EPI) {
-        if (!GEN || m0 + row < M)
-            epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 8>(epi, s, C + (int64_t)(m0 + row) * ldc,
-                                                          n0 + 8 * c8, GEN ? N - n0 - 8 * c8 : 8);
-    }
-    const u32x4 out{pack2<IS_BF16>(s[0], s[1]), pack2<IS_BF16>(s[2], s[3]),
-                    pack2<IS_BF16>(s[4], s[5]), pack2<IS_BF16>(s[6], s[7])};
-    uint16_t *dst = C + (int64_t)(m0 + row) * ldc + n0 + 8 * c8;
-    if (!GEN) {
-        *reinterpret_cast<u32x4 *>(dst) = out;
-    } else if (m0 + row < M) {
-        const int gn = n0 + 8 * c8;
-        if (gn + 8 <= N) {
+        if constexpr (EPI) {
+            if (!GEN || m0 + row < M)
+                epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 8>(epi, s, C + (int64_t)(m0 + row) * ldc,
+                                                              n0 + 8 * c8, GEN ? N - n0 - 8 * c8 : 8);
+        }
+        const u32x4 out{pack2<IS_BF16>(s[0], s[1]), pack2<IS_BF16>(s[2], s[3]),
+                        pack2<IS_BF16>(s[4], s[5]), pack2<IS_BF16>(s[6], s[7])};
+        uint16_t *dst = C + (int64_t)(m0 + row) * ldc + n0 + 8 * c8;
+        if (!GEN) {
             *reinterpret_cast<u32x4 *>(dst) = out;
-        } else {
+        } else if (m0 + row < M) {
+            const int gn = n0 + 8 * c8;
+            if (gn + 8 <= N) {
+                *reinterpret_cast<u32x4 *>(dst) = out;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (gn + e < N) dst[e] = (uint16_t)(out[e >> 1] >> (16 * (e & 1)));
+                for (int e = 0; e < 8; ++e)
+                    if (gn + e < N) dst[e] = (uint16_t)(out[e >> 1] >> (16 * (e & 1)));
+            }
         }
-    }
+    };
+    finish(std::integral_constant<int, 0>{});
+    if constexpr (FM == 2) finish(std::integral_constant<int, 1>{});
 }
+
 
 }  // namespace
 
-// Whole 32 x 64 tiles, K in whole 64-wide blocks with at least one per wave,
-// 16-byte aligned rows, and per-lane 32-bit offsets that fit (32 rows of A, 64
-// rows of B past a base).
-bool h16_narrow_eligible(const Problem &p)
+// Whole tiles (32 or 64 rows x 64), K in whole 64-wide blocks with at least one
+// per wave, 16-byte aligned rows, and per-lane 32-bit offsets that fit (64 rows
+// of A, 64 rows of B past a base).
+static bool narrow_whole(const Problem &p, int tbm)
 {
-    return p.aligned && p.M % NBM == 0 && p.N % NBN == 0 && p.K % NBK == 0 && p.K >= NBK * NNW &&
+    return p.aligned && p.M % tbm == 0 && p.N % NBN == 0 && p.K % NBK == 0 && p.K >= NBK * NNW &&
            p.lda < (1 << 24) && p.ldb < (1 << 23);
 }
+bool h16_narrow_eligible(const Problem &p) { return narrow_whole(p, 32); }
+bool h16_narrow64_eligible(const Problem &p) { return narrow_whole(p, 64); }
 
 // The guarded instantiation: any M, N >= 8 (a clamped column chunk starts at
 // N-8), any K >= 1, any leading dimensions with 32-bit per-lane offsets.
@@ -305,37 +361,60 @@ bool h16_narrow_general_eligible(const Problem &p)
            (int64_t)NBK * p.ldb + p.N < ((int64_t)1 << 31);
 }
 
-template <bool GEN, bool EPI>
+template <bool GEN, bool EPI, int TBM>
 static hipError_t narrow_launch(bool is_bf16, const Problem &p)
 {
+    constexpr int STG = TBM == 32 ? 3 : 2;
     const int tiles_n = (p.N + NBN - 1) / NBN;
-    const int64_t nwg = (int64_t)((p.M + NBM - 1) / NBM) * tiles_n;
+    const int64_t nwg = (int64_t)((p.M + TBM - 1) / TBM) * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (is_bf16)
-        hipLaunchKernelGGL((h16_narrow_kernel<true, GEN, EPI>), dim3((unsigned)nwg),
+        hipLaunchKernelGGL((h16_narrow_kernel<true, GEN, EPI, TBM, STG>), dim3((unsigned)nwg),
                            dim3(NNW * 64), 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb,
                            p.ldc, tiles_n, epi);
     else
-        hipLaunchKernelGGL((h16_narrow_kernel<false, GEN, EPI>), dim3((unsigned)nwg),
+        hipLaunchKernelGGL((h16_narrow_kernel<false, GEN, EPI, TBM, STG>), dim3((unsigned)nwg),
                            dim3(NNW * 64), 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb,
                            p.ldc, tiles_n, epi);
     return hipGetLastError();
 }
 
+template <int TBM>
+static hipError_t narrow_dispatch(bool is_bf16, bool gen, const Problem &p)
+{
+    if (gen)
+        return p.epi ? narrow_launch<true, true, TBM>(is_bf16, p)
+                     : narrow_launch<true, false, TBM>(is_bf16, p);
+    return p.epi ? narrow_launch<false, true, TBM>(is_bf16, p)
+                 : narrow_launch<false, false, TBM>(is_bf16, p);
+}
+
 hipError_t h16_narrow_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_narrow_eligible(p)) return hipErrorInvalidValue;
-    return p.epi ? narrow_launch<false, true>(is_bf16, p) : narrow_launch<false, false>(is_bf16, p);
+    return narrow_dispatch<32>(is_bf16, false, p);
 }
 
 hipError_t h16_narrow_general_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_narrow_general_eligible(p)) return hipErrorInvalidValue;
-    return p.epi ? narrow_launch<true, true>(is_bf16, p) : narrow_launch<true, false>(is_bf16, p);
+    return narrow_dispatch<32>(is_bf16, true, p);
+}
+
+hipError_t h16_narrow64_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_narrow64_eligible(p)) return hipErrorInvalidValue;
+    return narrow_dispatch<64>(is_bf16, false, p);
+}
+
+hipError_t h16_narrow64_general_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_narrow_general_eligible(p)) return hipErrorInvalidValue;
+    return narrow_dispatch<64>(is_bf16, true, p);
 }
 
 }  // namespace gemm

@@ -40,7 +40,9 @@ enum H16Config {
     H16_GEN_256x256 = 5,  // same kernel, guarded: ragged M/N/K, any leading dimensions
     H16_NARROW_32x64 = 6, // whole 32x64 tiles, 4 waves splitting K (tall, narrow products)
     H16_NARROW_GEN = 7,   // same kernel, guarded: any M, N >= 8, K, leading dimensions
-    H16_NUM_CONFIGS = 8
+    H16_NARROW64 = 8,     // whole 64x64 tiles, 4 waves splitting K, 2 LDS stages per wave
+    H16_NARROW64_GEN = 9, // same kernel, guarded
+    H16_NUM_CONFIGS = 10
 };
 
 int h16_pick_config(int M, int N, int K);
@@ -53,6 +55,9 @@ bool h16_narrow_eligible(const Problem &p);
 hipError_t h16_narrow_launch(bool is_bf16, const Problem &p);
 bool h16_narrow_general_eligible(const Problem &p);
 hipError_t h16_narrow_general_launch(bool is_bf16, const Problem &p);
+bool h16_narrow64_eligible(const Problem &p);
+hipError_t h16_narrow64_launch(bool is_bf16, const Problem &p);
+hipError_t h16_narrow64_general_launch(bool is_bf16, const Problem &p);
 // The measured optimisation ladder (fp16 or bf16): rungs 0-2 on the vector
 // ALUs, rungs 3-5 the 128 x 128 MFMA kernel with its ring / swizzle switched,
 // and the MFMA-only ceiling of the large-tile kernel.

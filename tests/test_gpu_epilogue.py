@@ -18,7 +18,7 @@ from gpu_helpers import OUT_DTYPE, TOL, TORCH_DT, c_bits, reference, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-FAST, GENERAL, NARROW, NARROW_GEN = 4, 5, 6, 7
+FAST, GENERAL, NARROW, NARROW_GEN, NARROW64, NARROW64_GEN = 4, 5, 6, 7, 8, 9
 
 
 @pytest.fixture(autouse=True)
@@ -97,6 +97,8 @@ H16_CASES = [
     (GENERAL, (257, 9, 96), (101, 11, 13)),
     (NARROW, (256, 128, 512), None),
     (NARROW_GEN, (40, 100, 1000), (1001, 101, 103)),
+    (NARROW64, (128, 128, 512), None),
+    (NARROW64_GEN, (100, 150, 700), (701, 151, 153)),
 ]
 
 

@@ -22,11 +22,13 @@ from gpu_helpers import TOL, OUT_DTYPE, compare, reference, run_gemm, say, to_de
 
 pytestmark = pytest.mark.gpu
 
-H16_CONFIGS = (0, 1, 2, 3, 4, 5, 6, 7)
+H16_CONFIGS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9)
 FAST = 4          # whole 256x256 tiles, K % 128 == 0, aligned
 GENERAL = 5       # the same kernel, guarded: ragged M/N/K, any leading dimensions
 NARROW = 6        # whole 32x64 tiles, K % 64 == 0, K >= 256, aligned; waves split K
 NARROW_GEN = 7    # the same kernel, guarded: any M, N >= 8, K >= 1, any leading dimensions
+NARROW64 = 8      # whole 64x64 tiles, K % 64 == 0, K >= 256, aligned; waves split K, 2 stages
+NARROW64_GEN = 9  # the same kernel, guarded
 
 
 @pytest.fixture(autouse=True)
@@ -309,6 +311,42 @@ def test_narrow_path(dtype, shape):
     ops = gi.operands(dtype, M, N, K, 42)
     _, got = run_gemm(dtype, ops, M, N, K)
     ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "narrow")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [
+    (64, 64, 256),        # one tile, one K block per wave
+    (192, 128, 320),      # 5 K blocks: wave 0 takes two, the others one
+    (128, 192, 448),      # 7 blocks: 2,2,2,1 per wave (the last step of a pair skipped)
+    (320, 256, 1088),     # 17 blocks, several row strips (rotated K walks)
+])
+def test_narrow64_path(dtype, shape):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(NARROW64)
+    M, N, K = shape
+    say(f"[narrow64] {dtype} {M}x{N}x{K}")
+    ops = gi.operands(dtype, M, N, K, 46)
+    _, got = run_gemm(dtype, ops, M, N, K)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "narrow64")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 8, 1), None),                     # one row, eight columns, one k
+    ((65, 65, 65), None),                  # a row and a column past a tile, partial K block
+    ((1000, 1000, 1000), None),            # the 1000^3 workload's shape
+    ((100, 300, 1000), (1001, 301, 303)),  # unaligned leading dimensions, offset pointers
+    ((64, 70, 129), None),                 # 3 K blocks: two waves without LDS-direct blocks
+])
+def test_narrow64_general_path_edges(dtype, shape, lds):
+    os.environ["LIBGEMM_H16_CONFIG"] = str(NARROW64_GEN)
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[narrow64-general] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 47)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "narrow64-general")
     assert ok, msg
 
 
