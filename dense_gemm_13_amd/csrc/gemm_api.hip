@@ -272,12 +272,13 @@ int f32_entry(const float *A, const float *B, float *C, int64_t M, int64_t N, in
     int st = check_args(A, B, C, M, N, K, lda, ldb, ldc, 4, 4, &work);
     if (st != GEMM_OK || !work) return st;
     if (epi && (st = check_bias(epi->bias, C, M, N, ldc, 4)) != GEMM_OK) return st;
-    if ((st = check_device()) != GEMM_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != GEMM_OK) return st;
     if (K == 0) return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, OUT_F32, epi, stream));
     Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, epi};
     p.aligned = aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
                 ldc % 4 == 0;
-    return to_status(f32_launch(p));
+    return to_status(f32_launch(p, cus));
 }
 
 int fp8_entry(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N, int64_t K,

@@ -224,23 +224,47 @@ hipError_t launch_cfg(const Problem &p)
 
 }  // namespace
 
-hipError_t f32_launch(const Problem &p)
+hipError_t f32_launch(const Problem &p, int cus)
 {
     // Testing override LIBGEMM_F32_SMALL: '1' forces the register-staged kernels
-    // below, '2' the guarded large-tile kernel and '3' the whole-tile large-tile
-    // kernel (each where it is eligible).
+    // below, '2' the guarded large-tile kernel, '3' the whole-tile large-tile
+    // kernel, '4' / '5' the K-split kernel with 32-row tiles (whole-tile where
+    // eligible / guarded) and '6' / '7' the same with 64-row tiles (each where it
+    // is eligible).
     const char *e = std::getenv("LIBGEMM_F32_SMALL");
-    const int force = e && e[0] >= '1' && e[0] <= '3' ? e[0] - '0' : 0;
+    const int force = e && e[0] >= '1' && e[0] <= '7' ? e[0] - '0' : 0;
     if (force == 3 && f32_fast_eligible(p)) return f32_fast_launch(p);
-    // The large-tile kernels (whole tiles, else guarded) once the grid has at
-    // least 128 tiles of 128 x 128; below that the register-staged kernels fill
-    // the chip better.  Measured: 4097 x 4095 x 4100 1321 us guarded against
-    // 2249 register-staged; 2000 x 3000 x 1000 144 against 227; but 1000^3 74
-    // against 43 and 256^3 (whole tiles) 21.6 against 10.5.
-    const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
-    if (force == 0 && tiles128 >= 128 && f32_fast_eligible(p)) return f32_fast_launch(p);
-    if ((force == 2 || (force == 0 && tiles128 >= 128)) && f32_general_eligible(p))
-        return f32_general_launch(p);
+    if (force >= 4 && f32_narrow_general_eligible(p))
+        return f32_narrow_launch(p, force >= 6 ? 64 : 32, force == 5 || force == 7);
+    if (force == 2 && f32_general_eligible(p)) return f32_general_launch(p);
+    if (force == 0) {
+        // Measured on MI355X (us; large-tile / K-split / register-staged):
+        //  * from 256 tiles of 128 x 128, or 128 with K < 512, the large-tile
+        //    kernels (whole tiles, else guarded): 1000 x 4096 x 4096 291 / 316 /
+        //    360, 2048 x 1500 x 256 25.3 / 34.1 / 31.6;
+        //  * other grids with K >= 512, and small grids (< 96 tiles) with K >=
+        //    128, the K-split kernel: 2048 x 1500 x 4096 295 / 246 / 499,
+        //    8192 x 64 x 4096 289 / 50 / 133, 300 x 1500 x 4096 289 / 48 / 195;
+        //  * 96 to 127 tiles with K < 512, the register-staged kernels:
+        //    300 x 4096 x 256 23.5 / 20.3 / 15.8;
+        //  * products at most 64 columns wide never take 128-column tiles, half
+        //    of which would be padding.
+        const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
+        const bool large = p.N > 64 && (tiles128 >= 256 || (tiles128 >= 128 && p.K < 512));
+        if (large && f32_fast_eligible(p)) return f32_fast_launch(p);
+        if (large && f32_general_eligible(p)) return f32_general_launch(p);
+        const bool ksplit = p.K >= 512 || (p.K >= 128 && tiles128 < 96);
+        if (!large && ksplit && f32_narrow_general_eligible(p)) {
+            // 64-row tiles do twice the work per workgroup: take them when that
+            // costs no more rounds of one workgroup per CU (1000^3: 28 against 33
+            // us; 300 x 4096 x 4096: 159 against 137 the other way).
+            const int64_t cu = cus > 0 ? cus : 256;
+            const int64_t t32 = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64);
+            const int64_t t64 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+            const bool rows64 = p.M >= 64 && 2 * ((t64 + cu - 1) / cu) <= (t32 + cu - 1) / cu;
+            return f32_narrow_launch(p, rows64 ? 64 : 32, false);
+        }
+    }
     const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
     if (big >= 128) return launch_cfg<128, 128, 2, 2>(p);
     return launch_cfg<64, 64, 2, 2>(p);

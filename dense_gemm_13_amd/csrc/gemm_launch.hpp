@@ -65,11 +65,13 @@ hipError_t ladder_valu_launch(int rung, bool is_bf16, const Problem &p);
 hipError_t h16_ladder_launch(int rung, bool is_bf16, const Problem &p);
 bool mfma_ceiling_eligible(const Problem &p);
 hipError_t mfma_ceiling_launch(bool is_bf16, const Problem &p);
-hipError_t f32_launch(const Problem &p);
+hipError_t f32_launch(const Problem &p, int cus);
 bool f32_fast_eligible(const Problem &p);
 hipError_t f32_fast_launch(const Problem &p);
 bool f32_general_eligible(const Problem &p);
 hipError_t f32_general_launch(const Problem &p);
+bool f32_narrow_general_eligible(const Problem &p);
+hipError_t f32_narrow_launch(const Problem &p, int tbm, bool force_general);
 hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
 bool fp8_fast_eligible(const Problem &p);
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);

@@ -113,17 +113,27 @@ def test_h16_paths(dtype, case):
     check(dtype, ops, M, N, K, 0.75, -0.5, True, act, case, f"config {config}", **kw)
 
 
-@pytest.mark.parametrize("path", ["large", "small", "guarded"])
+F32_PATHS = {   # override, shape, leading dimensions (None: packed), seed
+    "large": ("3", (256, 384, 256), None, 60),
+    "small": ("1", (200, 136, 77), (80, 139, 141), 61),
+    "guarded": ("2", (300, 270, 200), (203, 275, 277), 64),
+    "ksplit32": ("4", (96, 192, 320), None, 65),
+    "ksplit32_guarded": ("5", (100, 150, 333), (337, 151, 155), 66),
+    "ksplit64": ("6", (128, 128, 256), None, 67),
+    "ksplit64_guarded": ("7", (130, 70, 200), (203, 75, 77), 68),
+}
+
+
+@pytest.mark.parametrize("path", list(F32_PATHS))
 def test_f32_paths(path):
-    """The whole-tile large-tile kernel ('3'), the register-staged kernels ('1')
-    and the guarded large-tile kernel ('2', ragged shape, unaligned leading
-    dimensions)."""
-    os.environ["LIBGEMM_F32_SMALL"] = {"large": "3", "small": "1", "guarded": "2"}[path]
-    M, N, K = {"large": (256, 384, 256), "small": (200, 136, 77), "guarded": (300, 270, 200)}[path]
-    kw = {"large": {}, "small": dict(lda=80, ldb=139, ldc=141, offset=1),
-          "guarded": dict(lda=203, ldb=275, ldc=277, offset=1)}[path]
+    """The whole-tile large-tile kernel ('3'), the register-staged kernels ('1'),
+    the guarded large-tile kernel ('2') and the K-split kernel with 32-row ('4',
+    '5') and 64-row tiles ('6', '7'), whole-tile and guarded (ragged shapes,
+    unaligned leading dimensions)."""
+    force, (M, N, K), lds, seed = F32_PATHS[path]
+    os.environ["LIBGEMM_F32_SMALL"] = force
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
     ops = gi.operands("f32", M, N, K, 60)
-    seed = {"large": 60, "small": 61, "guarded": 64}[path]
     check("f32", ops, M, N, K, 1.5, 0.25, True, "relu", seed, "f32 " + path, **kw)
 
 

@@ -257,6 +257,67 @@ def test_f32_large_tile_permutation_exact():
     assert bad.size == 0, f"first mismatch at {bad[0]}"
 
 
+@pytest.mark.parametrize("force,shape", [
+    ("4", (32, 64, 128)),       # 32-row tiles: one tile, one K block per wave
+    ("4", (96, 128, 160)),      # 5 K blocks: wave 0 takes two, the others one
+    ("4", (160, 192, 416)),     # 13 blocks: a second trip through the 3-stage ring for wave 0
+    ("4", (2048, 64, 544)),     # 17 blocks, 64 row strips (rotated K walks)
+    ("6", (64, 64, 128)),       # 64-row tiles: one tile, one K block per wave
+    ("6", (192, 128, 160)),     # 5 K blocks
+    ("6", (128, 192, 224)),     # 7 blocks: 2,2,2,1 per wave (the last step of a pair skipped)
+    ("6", (320, 256, 544)),     # 17 blocks, several row strips
+])
+def test_f32_ksplit_path(force, shape):
+    """The fp32 K-split kernel on whole tiles (testing overrides '4': 32-row
+    tiles, '6': 64-row tiles)."""
+    os.environ["LIBGEMM_F32_SMALL"] = force
+    M, N, K = shape
+    say(f"[f32-ksplit {force}] {M}x{N}x{K}")
+    ops = gi.operands("f32", M, N, K, 48)
+    _, got = run_gemm("f32", ops, M, N, K)
+    ok, msg, _ = compare("f32", got, reference("f32", ops, M, N, K), "f32-ksplit")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("force", ["5", "7"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 4, 1), None),                     # one row, four columns, one k
+    ((5, 200, 32), None),                  # one K block: the register-loaded block only
+    ((33, 65, 33), None),                  # partial tiles both ways, partial K block
+    ((31, 64, 300), (303, 67, 71)),        # unaligned leading dimensions, offset pointers
+    ((64, 70, 65), None),                  # 3 K blocks: two waves without LDS-direct blocks
+    ((100, 300, 1000), (1001, 301, 303)),  # 32 blocks incl. the partial one
+    ((1000, 1000, 1000), None),            # the 1000^3 workload's shape
+])
+def test_f32_ksplit_general_edges(force, shape, lds):
+    """The guarded fp32 K-split kernel (testing overrides '5': 32-row tiles,
+    '7': 64-row tiles): clamped rows and column chunks, the last K block through
+    registers, masked stores."""
+    os.environ["LIBGEMM_F32_SMALL"] = force
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[f32-ksplit-general {force}] {M}x{N}x{K} {kw}")
+    ops = gi.operands("f32", M, N, K, 49)
+    _, got = run_gemm("f32", ops, M, N, K, **kw)
+    ok, msg, _ = compare("f32", got, reference("f32", ops, M, N, K), "f32-ksplit-general")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("force", ["4", "7"])
+def test_f32_ksplit_permutation_exact(force):
+    """A * P with P a permutation: every output is one product by 1 plus zeros,
+    so it is exact whatever the order of the K split."""
+    M, K = 320, 256
+    os.environ["LIBGEMM_F32_SMALL"] = force
+    say(f"[probe] f32 K-split {force} A*P")
+    ops, perm = _perm_case("f32", M, K, 16)
+    _, got = run_gemm("f32", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "f32")
+    bad = np.argwhere(oracle.decode(got, "f32") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 def test_fp8_large_tile_permutation_exact():
     M = K = 512
     say("[probe] fp8 large-tile A*P")
