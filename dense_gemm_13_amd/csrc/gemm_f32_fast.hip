@@ -1,17 +1,24 @@
-// fp32 SGEMM, large-tile path for gfx950: whole 128 x 128 tiles, K a multiple of
-// 64, 16-byte aligned rows.
+// fp32 SGEMM, large-tile path for gfx950: 128 x 128 tiles of C, 4 waves of
+// 64 x 64 (2 x 2 MFMA tiles of v_mfma_f32_32x32x2_f32).
 //
 // The register-tiled SGEMM of "CUDA GEMM 优化实践笔记" (block tile of C staged in
 // shared memory, K walked in BK steps, per-thread register tile) with the FMA
-// outer product replaced by v_mfma_f32_32x32x2_f32 on 64 x 64 wave tiles, and
-// the operands moved with global_load_lds_dwordx4 into two LDS stages (one array
-// per stage, indexed at compile time; the 16-byte chunk swizzle is applied on
-// the global side).  Two-level accumulation as in gemm_f32.hip: each 32-wide K
-// step is summed into a fresh partial and then added to the running total.
-// 64 KiB of LDS and at most 256 registers per lane (two waves per SIMD) let two
-// workgroups share a CU, so one workgroup's MFMAs cover the other's barriers.
+// outer product replaced by MFMAs on 64 x 64 wave tiles, and the operands moved
+// with global_load_lds_dwordx4 into a ring of 4 LDS stages of 16-wide K steps
+// (one array per stage, indexed at compile time; the 16-byte chunk swizzle is
+// applied on the global side).  Each step waits only for the loads of the
+// stage after it, and its workgroup barrier sits before its last sub-step:
+// that sub-step's MFMAs cover the reads of the next stage's first fragments and
+// the global loads of the step three ahead, and every sub-step multiplies while
+// the following one's fragments are read, so no LDS latency is exposed.
+// Two-level accumulation: each 64-wide K block (one turn of the ring) is summed
+// into a fresh partial that is then added to the running total (with b-wide
+// partials the rounding error of a K-term sum grows like b + K/b, least at b
+// near sqrt(K): 64 for K = 4096).  64 KiB of LDS and at
+// most 256 registers per lane (two waves per SIMD) let two workgroups share a
+// CU.
 //
-// LDS: A as rows of k (128 bytes per row, chunk XOR swz8(row)); B as rows of n
+// LDS: A as rows of k (64 bytes per row, chunk XOR swz_af(row)); B as rows of n
 // (512 bytes per row), read as single floats: 32 lanes cover 128 contiguous
 // bytes of row k while the other 32 read row k+4; rows with bit 2 set have
 // their chunks XOR-moved by 128 bytes so the two halves never share banks.
@@ -26,24 +33,53 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void32_t;
 
-constexpr int SBM = 128, SBN = 128, SBK = 32, SSTAGES = 2;
+constexpr int SBM = 128, SBN = 128, SBK = 16, SSTAGES = 4;
 constexpr int SWM = 2, SWN = 2, SNW = SWM * SWN;
 constexpr int SWTM = SBM / SWM, SWTN = SBN / SWN;       // 64 x 64 per wave
 constexpr int SFM = SWTM / 32, SFN = SWTN / 32;         // 2 x 2 MFMA tiles
-constexpr int SA_STAGE = SBM * SBK;                      // floats per stage (16 KiB)
+constexpr int SA_STAGE = SBM * SBK;                      // floats per stage (8 KiB)
 constexpr int SB_STAGE = SBK * SBN;
 constexpr int SA_BLK = SA_STAGE * 4 / 1024 / SNW;        // 1 KiB loads per wave per stage
 constexpr int SB_BLK = SB_STAGE * 4 / 1024 / SNW;
 
 template <int TAG>
-__shared__ __attribute__((aligned(1024))) float s_stage[4096];
+__shared__ __attribute__((aligned(1024))) float s_stage[2048];
 
+// A rows are 64 bytes (4 chunks).  A 16-byte read by 16 lanes covers 16
+// consecutive rows: moving the chunks of rows 4a .. 4a+3 by a puts all 16
+// reads on distinct banks.
+__host__ __device__ __forceinline__ int swz_af(int row) { return (row >> 2) & 3; }
 __host__ __device__ __forceinline__ int swz_bf(int k) { return ((k >> 2) & 1) << 3; }
 
 __device__ __forceinline__ void s_barrier_nf() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt vmcnt(N) (N < 64), leaving expcnt and lgkmcnt alone.
+template <int N>
+__device__ __forceinline__ void s_wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One 16-byte global -> LDS load per lane (lane t's bytes land at lds + 16t).
+__device__ __forceinline__ void s_dma16(const void *src, float *lds)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void32_t *)lds, 16, 0, 0);
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void s_unroll_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void s_unroll(F &&f)
+{
+    s_unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // GEN = false: whole 128 x 128 tiles, K a multiple of 64, 16-byte aligned rows.
-// GEN = true: any M, N >= 4, K > 32 and any leading dimensions (the hardware
+// GEN = true: any M, N >= 4, K > 16 and any leading dimensions (the hardware
 // runs in unaligned-access mode, so 16-byte loads and stores at 4-byte-aligned
 // addresses are legal):
 //   * the last K block (possibly partial) is step 0, loaded through registers
@@ -53,8 +89,8 @@ __device__ __forceinline__ void s_barrier_nf() { asm volatile("s_barrier" ::: "m
 //     to the chunk at N-4 (their products only reach C entries that are not
 //     stored; a chunk straddling N reads a few floats past N inside a row that
 //     is not B's last);
-//   * an odd number of K steps ends with one more step, and C stores (and the
-//     epilogue's reads) are masked to the M x N window.
+//   * whole turns of the ring are followed by the remaining steps, and C
+//     stores (and the epilogue's reads) are masked to the M x N window.
 // EPI: the fused epilogue is applied to the results by the lane that stores them.
 template <bool GEN, bool EPI>
 __global__ void __launch_bounds__(SNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -73,15 +109,15 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * SBM, n0 = tn * SBN;
 
-    // A block b: 8 rows of 128 bytes, lane -> row 8b + lane/8, slot lane%8
-    // (logical chunk slot ^ swz8(row)).  B block b: 2 rows of 512 bytes, lane ->
-    // row 2b + lane/32, slot lane%32 (logical chunk slot ^ swz_bf(row)).
+    // A block b: 16 rows of 64 bytes, lane -> row 16b + lane/4, slot lane%4
+    // (logical chunk slot ^ swz_af(row)).  B block b: 2 rows of 512 bytes, lane
+    // -> row 2b + lane/32, slot lane%32 (logical chunk slot ^ swz_bf(row)).
     uint32_t a_off[SA_BLK], b_off[SB_BLK];
 #pragma unroll
     for (int j = 0; j < SA_BLK; ++j) {
-        const int row = 8 * (wave * SA_BLK + j) + (lane >> 3);
+        const int row = 16 * (wave * SA_BLK + j) + (lane >> 2);
         const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
-        a_off[j] = (uint32_t)(lrow * lda + 4 * ((lane & 7) ^ swz8(row))) * 4u;
+        a_off[j] = (uint32_t)(lrow * lda + 4 * ((lane & 3) ^ swz_af(row))) * 4u;
     }
     // (GEN: the column, n0 included, is part of the per-lane offset.)
 #pragma unroll
@@ -100,11 +136,9 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         const char *ab = a_base + (int64_t)kt * SBK * 4;
         const char *bb = b_base + kt * b_step;
 #pragma unroll
-        for (int j = 0; j < SA_BLK; ++j)
-            __builtin_amdgcn_global_load_lds(ab + a_off[j], (lds_void32_t *)(as + (wave * SA_BLK + j) * 256), 16, 0, 0);
+        for (int j = 0; j < SA_BLK; ++j) s_dma16(ab + a_off[j], as + (wave * SA_BLK + j) * 256);
 #pragma unroll
-        for (int j = 0; j < SB_BLK; ++j)
-            __builtin_amdgcn_global_load_lds(bb + b_off[j], (lds_void32_t *)(bs + (wave * SB_BLK + j) * 256), 16, 0, 0);
+        for (int j = 0; j < SB_BLK; ++j) s_dma16(bb + b_off[j], bs + (wave * SB_BLK + j) * 256);
     };
 
     // Fragments (floats, relative to a stage).  Sub-step s covers k = 8s .. 8s+7;
@@ -114,71 +148,122 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     for (int i = 0; i < SFM; ++i) {
         const int row = wm0 + 32 * i + l32;
         a_off_r[i] = row * SBK;
-        a_swz[i] = swz8(row);
+        a_swz[i] = swz_af(row);
     }
     int b_col[SFN];
 #pragma unroll
     for (int j = 0; j < SFN; ++j) b_col[j] = wn0 + 32 * j + l32;
 
-    f32x16 total[SFM][SFN];
+    f32x16 total[SFM][SFN], part[SFM][SFN];
 #pragma unroll
     for (int i = 0; i < SFM; ++i)
 #pragma unroll
-        for (int j = 0; j < SFN; ++j) total[i][j] = f32x16{};
+        for (int j = 0; j < SFN; ++j) total[i][j] = part[i][j] = f32x16{};
 
-    auto compute = [&](const float *as, const float *bs) {
-        f32x16 part[SFM][SFN];
+    // Fragments of one 8-wide K sub-step: SFM A reads of 16 bytes and 4 B floats
+    // per column tile.
+    struct Frags {
+        f32x4 a[SFM];
+        float b[SFN][4];
+    };
+    auto load_frags = [&](Frags &f, const float *as, const float *bs, int s) {
+        const int c = 2 * s + half;
 #pragma unroll
         for (int i = 0; i < SFM; ++i)
+            f.a[i] = *reinterpret_cast<const f32x4 *>(as + a_off_r[i] + ((c ^ a_swz[i]) << 2));
 #pragma unroll
-            for (int j = 0; j < SFN; ++j) part[i][j] = f32x16{};
+        for (int e = 0; e < 4; ++e) {
+            const int k = 8 * s + 4 * half + e;
 #pragma unroll
-        for (int s = 0; s < SBK / 8; ++s) {
-            const int c = 2 * s + half;
-            f32x4 af[SFM];
-            float bv[SFN][4];
+            for (int j = 0; j < SFN; ++j) {
+                const int n = b_col[j];
+                f.b[j][e] = bs[k * SBN + (((n >> 2) ^ swz_bf(k)) << 2) + (n & 3)];
+            }
+        }
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < SFM; ++i)
-                af[i] = *reinterpret_cast<const f32x4 *>(as + a_off_r[i] + ((c ^ a_swz[i]) << 2));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = 8 * s + 4 * half + e;
-#pragma unroll
-                for (int j = 0; j < SFN; ++j) {
-                    const int n = b_col[j];
-                    bv[j][e] = bs[k * SBN + (((n >> 2) ^ swz_bf(k)) << 2) + (n & 3)];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int i = 0; i < SFM; ++i)
-#pragma unroll
-                    for (int j = 0; j < SFN; ++j)
-                        part[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[j][e], af[i][e],
-                                                                         part[i][j], 0, 0, 0);
-        }
+                for (int j = 0; j < SFN; ++j)
+                    part[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.b[j][e], f.a[i][e],
+                                                                     part[i][j], 0, 0, 0);
+    };
+    // The partial of a 64-wide K block into the total (after every fourth step).
+    auto close_part = [&]() {
 #pragma unroll
         for (int i = 0; i < SFM; ++i)
 #pragma unroll
-            for (int j = 0; j < SFN; ++j) total[i][j] += part[i][j];
+            for (int j = 0; j < SFN; ++j) {
+                total[i][j] += part[i][j];
+                part[i][j] = f32x16{};
+            }
     };
 
-    auto step = [&](float *as, float *bs, float *nas, float *nbs, int next_kt, bool dma) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0): this stage (own loads)
-        s_barrier_nf();                                  // ... everyone's; the other stage is free
-        if (dma) issue(nas, nbs, next_kt);
-        compute(as, bs);
+    // K step t runs on stage t % 4 with the fragments of its first sub-step
+    // already in registers: sub-step 0 multiplies while sub-step 1's fragments
+    // are read.  Then: wait for this wave's loads of stage t+1, barrier
+    // (everyone's loads of stage t+1 have landed, everyone has finished reading
+    // stage t-1), read stage t+1's first fragments and issue the loads of K step
+    // t+3 into stage t-1 while sub-step 1 multiplies.  A load has two steps to
+    // land.
+    constexpr int SUB = SBK / 8;                         // sub-steps per K step (2)
+    constexpr int NMF = 4 * SFM * SFN;                   // MFMAs per sub-step (16)
+    constexpr int DS = SFM + 2 * SFN;                    // LDS reads per sub-step (B pairs merged)
+    constexpr int NBLK = SA_BLK + SB_BLK;                // global->LDS loads per step
+    static_assert(SUB == 2, "one sub-step before the barrier");
+    static_assert(NMF >= DS + NBLK, "MFMAs to interleave with");
+    Frags cur, nxt;
+    auto step = [&](const float *as, const float *bs, const float *nas_read, const float *nbs_read,
+                    float *nas_dma, float *nbs_dma, int next_kt, bool close) {
+        load_frags(nxt, as, bs, 1);
+        mfmas(cur);
+        cur = nxt;
+#pragma unroll
+        for (int x = 0; x < DS; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - DS, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        s_wait_vmcnt<(SSTAGES - 3) * NBLK>();
+        s_barrier_nf();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(nxt, nas_read, nbs_read, 0);
+        issue(nas_dma, nbs_dma, next_kt);
+        mfmas(cur);
+        cur = nxt;
+#pragma unroll
+        for (int x = 0; x < DS; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < NBLK; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - DS - NBLK, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (close) close_part();
     };
 
-    const int ktiles = (K + SBK - 1) / SBK;              // !GEN: K / SBK, even
+    // Prologue: K steps 0 .. 2 in flight (GEN: step 0 through registers), stage
+    // 0 published, its first fragments read.  Indices past the end are clamped:
+    // the last steps re-fetch the final K step into stages nobody reads any
+    // more, and the last step's look-ahead reads a stage whose contents are not
+    // used (identical code in every step).  All loads are drained before the
+    // stores.
+    const int ktiles = (K + SBK - 1) / SBK;              // !GEN: K / SBK, a multiple of 4
     if constexpr (GEN) {
         // Step 0: the last K block [SBK*(ktiles-1), K) through registers, zero
         // filled, in the swizzled layout the LDS-direct loads produce.
         const int k0 = SBK * (ktiles - 1);
-        float *as = s_stage<0>, *bs = s_stage<2>;
+        float *as = s_stage<0>, *bs = s_stage<SSTAGES>;
         for (int q = tid; q < SBM * SBK / 4; q += SNW * 64) {
-            const int r = q >> 3, c = q & 7;
+            const int r = q >> 2, c = q & 3;
             const int gm = m0 + r, gk = k0 + 4 * c;
             f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
             if (gm < M) {
@@ -191,7 +276,7 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
                         if (gk + e < K) v[e] = src[e];
                 }
             }
-            *reinterpret_cast<f32x4 *>(as + r * SBK + ((c ^ swz8(r)) << 2)) = v;
+            *reinterpret_cast<f32x4 *>(as + r * SBK + ((c ^ swz_af(r)) << 2)) = v;
         }
         for (int q = tid; q < SBK * SBN / 4; q += SNW * 64) {
             const int r = q >> 5, c = q & 31;
@@ -209,17 +294,40 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
             }
             *reinterpret_cast<f32x4 *>(bs + r * SBN + ((c ^ swz_bf(r)) << 2)) = v;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): the LDS writes landed
-    } else {
-        issue(s_stage<0>, s_stage<2>, 0);
     }
-    // Pairs of steps over the two stages; GEN: an odd count ends with one more.
-    int kt = 0;
-    for (; kt + 1 < ktiles; kt += 2) {
-        step(s_stage<0>, s_stage<2>, s_stage<1>, s_stage<3>, kt + 1, true);
-        step(s_stage<1>, s_stage<3>, s_stage<0>, s_stage<2>, kt + 2, kt + 2 < ktiles);
+    // (GEN: steps past the last one re-load the last full block, K > SBK.)
+    s_unroll<SSTAGES - 1>([&](auto S) {
+        if (!GEN || S > 0)
+            issue(s_stage<S>, s_stage<SSTAGES + S>, !GEN || S < ktiles ? (int)S : ktiles - 1);
+    });
+    // GEN: stage 0 came through registers (its global loads were waited for
+    // before the LDS writes); the writes must land before the barrier.
+    if constexpr (GEN) __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0)
+    s_wait_vmcnt<(SSTAGES - 2) * NBLK>();
+    s_barrier_nf();
+    load_frags(cur, s_stage<0>, s_stage<SSTAGES>, 0);
+    // Whole turns of the ring without conditions (a step skipped at run time
+    // would let the compiler merge the steps' code and lose track of which
+    // stage array each LDS read addresses).  GEN: the remaining ktiles % 4
+    // steps follow, once, and their partial is added at the end.
+    auto ring_step = [&](auto S, int kt) {
+        constexpr int N1 = (S + 1) % SSTAGES;          // next stage (read ahead)
+        constexpr int NS = (S + SSTAGES - 1) % SSTAGES; // stage to refill
+        const int next = kt + S + SSTAGES - 1;
+        step(s_stage<S>, s_stage<SSTAGES + S>, s_stage<N1>, s_stage<SSTAGES + N1>, s_stage<NS>,
+             s_stage<SSTAGES + NS>, next < ktiles ? next : ktiles - 1, S == SSTAGES - 1);
+    };
+    const int kwhole = GEN ? ktiles - ktiles % SSTAGES : ktiles;
+    for (int kt = 0; kt < kwhole; kt += SSTAGES)
+        s_unroll<SSTAGES>([&](auto S) { ring_step(S, kt); });
+    if constexpr (GEN) {
+        const int rem = ktiles - kwhole;
+        s_unroll<SSTAGES - 1>([&](auto S) {
+            if (S < rem) ring_step(S, kwhole);
+        });
+        if (rem > 0) close_part();
     }
-    if (GEN && kt < ktiles) step(s_stage<0>, s_stage<2>, s_stage<1>, s_stage<3>, kt + 1, false);
+    s_wait_vmcnt<0>();
 
     // lane holds C[m][n..n+3], n = 8g + 4*half (+ tile offsets): one 16-byte store
 #pragma unroll
