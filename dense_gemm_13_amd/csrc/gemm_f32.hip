@@ -233,7 +233,7 @@ hipError_t f32_launch(const Problem &p, int cus)
     // is eligible).
     const char *e = std::getenv("LIBGEMM_F32_SMALL");
     const int force = e && e[0] >= '1' && e[0] <= '7' ? e[0] - '0' : 0;
-    if (force == 3 && f32_fast_eligible(p)) return f32_fast_launch(p);
+    if (force == 3 && f32_fast_eligible(p)) return f32_fast_launch(p, cus);
     if (force >= 4 && f32_narrow_general_eligible(p))
         return f32_narrow_launch(p, force >= 6 ? 64 : 32, force == 5 || force == 7);
     if (force == 2 && f32_general_eligible(p)) return f32_general_launch(p);
@@ -251,7 +251,7 @@ hipError_t f32_launch(const Problem &p, int cus)
         //    of which would be padding.
         const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
         const bool large = p.N > 64 && (tiles128 >= 256 || (tiles128 >= 128 && p.K < 512));
-        if (large && f32_fast_eligible(p)) return f32_fast_launch(p);
+        if (large && f32_fast_eligible(p)) return f32_fast_launch(p, cus);
         if (large && f32_general_eligible(p)) return f32_general_launch(p);
         const bool ksplit = p.K >= 512 || (p.K >= 128 && tiles128 < 96);
         if (!large && ksplit && f32_narrow_general_eligible(p)) {

@@ -105,9 +105,13 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     const int wn0 = (wave % SWN) * SWTN;
     const int l32 = lane & 31, half = lane >> 5;
 
+    // !GEN: a persistent workgroup walks the tiles blockIdx.x, blockIdx.x +
+    // gridDim.x, ... (gridDim.x a multiple of 8, so under the remap they are all
+    // tiles of this workgroup's XCD); GEN: one tile per workgroup.
+    const int ntiles = tiles_m * tiles_n;
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * SBM, n0 = tn * SBN;
+    tile_coords(blockIdx.x, ntiles, tiles_m, tiles_n, group_m, tm, tn);
+    int m0 = tm * SBM, n0 = tn * SBN;
 
     // A block b: 16 rows of 64 bytes, lane -> row 16b + lane/4, slot lane%4
     // (logical chunk slot ^ swz_af(row)).  B block b: 2 rows of 512 bytes, lane
@@ -127,14 +131,26 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         if (GEN) col = n0 + col >= N ? N - 4 : n0 + col;
         b_off[j] = (uint32_t)(row * ldb + col) * 4u;
     }
-    const char *a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
-    const char *b_base = reinterpret_cast<const char *>(GEN ? B : B + n0);
+    auto a_tile = [&](int tile_m) {
+        return reinterpret_cast<const char *>(A + (int64_t)tile_m * SBM * lda);
+    };
+    auto b_tile = [&](int tile_n) { return reinterpret_cast<const char *>(GEN ? B : B + tile_n * SBN); };
+    const char *a_cur = a_tile(tm), *b_cur = b_tile(tn);
+    // The next tile of this workgroup and its bases (!GEN).  Without one they
+    // stay the current tile's: loads past its last step then re-fetch that step
+    // into a stage nobody reads any more.
+    int next_tile = blockIdx.x + gridDim.x;
+    bool has_next = !GEN && next_tile < ntiles;
+    int ntm = tm, ntn = tn;
+    if (has_next) tile_coords(next_tile, ntiles, tiles_m, tiles_n, group_m, ntm, ntn);
+    const char *a_nxt = a_tile(ntm), *b_nxt = b_tile(ntn);
     const int64_t b_step = (int64_t)SBK * ldb * 4;
-    // K step s loads K block s (GEN: block s - 1; step 0 is the last block).
-    auto issue = [&](float *as, float *bs, int s) {
+    // K step s of the tile with bases abase, bbase loads its K block s (GEN:
+    // block s - 1; step 0 is the last block).
+    auto issue = [&](float *as, float *bs, const char *abase, const char *bbase, int s) {
         const int kt = GEN ? s - 1 : s;
-        const char *ab = a_base + (int64_t)kt * SBK * 4;
-        const char *bb = b_base + kt * b_step;
+        const char *ab = abase + (int64_t)kt * SBK * 4;
+        const char *bb = bbase + kt * b_step;
 #pragma unroll
         for (int j = 0; j < SA_BLK; ++j) s_dma16(ab + a_off[j], as + (wave * SA_BLK + j) * 256);
 #pragma unroll
@@ -216,8 +232,9 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     static_assert(SUB == 2, "one sub-step before the barrier");
     static_assert(NMF >= DS + NBLK, "MFMAs to interleave with");
     Frags cur, nxt;
-    auto step = [&](const float *as, const float *bs, const float *nas_read, const float *nbs_read,
-                    float *nas_dma, float *nbs_dma, int next_kt, bool close) {
+    auto step = [&](auto FIRST, const float *as, const float *bs, const float *nas_read,
+                    const float *nbs_read, float *nas_dma, float *nbs_dma, const char *abase,
+                    const char *bbase, int next_kt, bool close) {
         load_frags(nxt, as, bs, 1);
         mfmas(cur);
         cur = nxt;
@@ -228,11 +245,15 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         }
         __builtin_amdgcn_sched_group_barrier(0x008, NMF - DS, 0);
         __builtin_amdgcn_sched_barrier(0);
-        s_wait_vmcnt<(SSTAGES - 3) * NBLK>();
+        // (The first step of a tile after another one waits for everything: the
+        // previous tile's stores share the counter with the loads, and the two
+        // kinds need not complete in order.)
+        if constexpr (FIRST) s_wait_vmcnt<0>();
+        else s_wait_vmcnt<(SSTAGES - 3) * NBLK>();
         s_barrier_nf();
         __builtin_amdgcn_sched_barrier(0);
         load_frags(nxt, nas_read, nbs_read, 0);
-        issue(nas_dma, nbs_dma, next_kt);
+        issue(nas_dma, nbs_dma, abase, bbase, next_kt);
         mfmas(cur);
         cur = nxt;
 #pragma unroll
@@ -298,7 +319,8 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     // (GEN: steps past the last one re-load the last full block, K > SBK.)
     s_unroll<SSTAGES - 1>([&](auto S) {
         if (!GEN || S > 0)
-            issue(s_stage<S>, s_stage<SSTAGES + S>, !GEN || S < ktiles ? (int)S : ktiles - 1);
+            issue(s_stage<S>, s_stage<SSTAGES + S>, a_cur, b_cur,
+                  !GEN || S < ktiles ? (int)S : ktiles - 1);
     });
     // GEN: stage 0 came through registers (its global loads were waited for
     // before the LDS writes); the writes must land before the barrier.
@@ -308,50 +330,88 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     load_frags(cur, s_stage<0>, s_stage<SSTAGES>, 0);
     // Whole turns of the ring without conditions (a step skipped at run time
     // would let the compiler merge the steps' code and lose track of which
-    // stage array each LDS read addresses).  GEN: the remaining ktiles % 4
-    // steps follow, once, and their partial is added at the end.
-    auto ring_step = [&](auto S, int kt) {
+    // stage array each LDS read addresses).  Steps past the tile's last one
+    // load the next tile's first steps.  GEN: the remaining ktiles % 4 steps
+    // follow, once, and their partial is added at the end.
+    auto ring_step = [&](auto S, int kt, auto FIRST) {
         constexpr int N1 = (S + 1) % SSTAGES;          // next stage (read ahead)
         constexpr int NS = (S + SSTAGES - 1) % SSTAGES; // stage to refill
         const int next = kt + S + SSTAGES - 1;
-        step(s_stage<S>, s_stage<SSTAGES + S>, s_stage<N1>, s_stage<SSTAGES + N1>, s_stage<NS>,
-             s_stage<SSTAGES + NS>, next < ktiles ? next : ktiles - 1, S == SSTAGES - 1);
+        const bool wrap = next >= ktiles;
+        const int lkt = !wrap ? next : has_next ? next - ktiles : ktiles - 1;
+        step(FIRST, s_stage<S>, s_stage<SSTAGES + S>, s_stage<N1>, s_stage<SSTAGES + N1>,
+             s_stage<NS>, s_stage<SSTAGES + NS>, wrap ? a_nxt : a_cur, wrap ? b_nxt : b_cur, lkt,
+             S == SSTAGES - 1);
     };
-    const int kwhole = GEN ? ktiles - ktiles % SSTAGES : ktiles;
-    for (int kt = 0; kt < kwhole; kt += SSTAGES)
-        s_unroll<SSTAGES>([&](auto S) { ring_step(S, kt); });
-    if constexpr (GEN) {
-        const int rem = ktiles - kwhole;
-        s_unroll<SSTAGES - 1>([&](auto S) {
-            if (S < rem) ring_step(S, kwhole);
-        });
-        if (rem > 0) close_part();
-    }
-    s_wait_vmcnt<0>();
+    const std::integral_constant<bool, false> plain{};
 
     // lane holds C[m][n..n+3], n = 8g + 4*half (+ tile offsets): one 16-byte store
+    auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < SFM; ++i) {
-        const int gm = m0 + wm0 + 32 * i + l32;
-        if (GEN && gm >= M) continue;
-        float *const rowp = C + (int64_t)gm * ldc;
+        for (int i = 0; i < SFM; ++i) {
+            const int gm = m0 + wm0 + 32 * i + l32;
+            if (GEN && gm >= M) continue;
+            float *const rowp = C + (int64_t)gm * ldc;
 #pragma unroll
-        for (int j = 0; j < SFN; ++j)
+            for (int j = 0; j < SFN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int gn = n0 + wn0 + 4 * half + 32 * j + 8 * g;
-                const int cnt = GEN ? N - gn : 4;
-                float ev[4] = {total[i][j][4 * g], total[i][j][4 * g + 1], total[i][j][4 * g + 2],
-                               total[i][j][4 * g + 3]};
-                if constexpr (EPI) epilogue_row<OUT_F32, 4>(epi, ev, rowp, gn, cnt);
-                if (!GEN || cnt >= 4) {
-                    *reinterpret_cast<f32x4 *>(rowp + gn) = f32x4{ev[0], ev[1], ev[2], ev[3]};
-                } else {
+                for (int g = 0; g < 4; ++g) {
+                    const int gn = n0 + wn0 + 4 * half + 32 * j + 8 * g;
+                    const int cnt = GEN ? N - gn : 4;
+                    float ev[4] = {total[i][j][4 * g], total[i][j][4 * g + 1],
+                                   total[i][j][4 * g + 2], total[i][j][4 * g + 3]};
+                    if constexpr (EPI) epilogue_row<OUT_F32, 4>(epi, ev, rowp, gn, cnt);
+                    if (!GEN || cnt >= 4) {
+                        *reinterpret_cast<f32x4 *>(rowp + gn) = f32x4{ev[0], ev[1], ev[2], ev[3]};
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (e < cnt) rowp[gn + e] = ev[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (e < cnt) rowp[gn + e] = ev[e];
+                    }
                 }
+        }
+    };
+
+    if constexpr (GEN) {
+        const int kwhole = ktiles - ktiles % SSTAGES;
+        for (int kt = 0; kt < kwhole; kt += SSTAGES)
+            s_unroll<SSTAGES>([&](auto S) { ring_step(S, kt, plain); });
+        const int rem = ktiles - kwhole;
+        s_unroll<SSTAGES - 1>([&](auto S) {
+            if (S < rem) ring_step(S, kwhole, plain);
+        });
+        if (rem > 0) close_part();
+        s_wait_vmcnt<0>();
+        store_tile();
+    } else {
+        for (bool first = true;; first = false) {
+            // The first turn of a tile after another one starts with a full wait.
+            if (first) {
+                s_unroll<SSTAGES>([&](auto S) { ring_step(S, 0, plain); });
+            } else {
+                s_unroll<SSTAGES>([&](auto S) {
+                    ring_step(S, 0, std::integral_constant<bool, S == 0>{});
+                });
             }
+            for (int kt = SSTAGES; kt < ktiles; kt += SSTAGES)
+                s_unroll<SSTAGES>([&](auto S) { ring_step(S, kt, plain); });
+            store_tile();
+            if (!has_next) break;
+#pragma unroll
+            for (int i = 0; i < SFM; ++i)
+#pragma unroll
+                for (int j = 0; j < SFN; ++j) total[i][j] = f32x16{};
+            tm = ntm, tn = ntn;
+            m0 = tm * SBM, n0 = tn * SBN;
+            a_cur = a_nxt, b_cur = b_nxt;
+            next_tile += gridDim.x;
+            has_next = next_tile < ntiles;
+            if (has_next) {
+                tile_coords(next_tile, ntiles, tiles_m, tiles_n, group_m, ntm, ntn);
+                a_nxt = a_tile(ntm), b_nxt = b_tile(ntn);
+            }
+        }
+        s_wait_vmcnt<0>();
     }
 }
 
@@ -371,12 +431,16 @@ bool f32_general_eligible(const Problem &p)
            (int64_t)SBK * p.ldb + p.N < ((int64_t)1 << 30);
 }
 
+// GEN: one workgroup per tile; whole tiles: min(tiles, 2 per CU) persistent
+// workgroups (a multiple of 8 when it is the CU bound).
 template <bool GEN>
-static hipError_t f32_fast_typed(const Problem &p)
+static hipError_t f32_fast_typed(const Problem &p, int cus)
 {
     const int tiles_m = (p.M + SBM - 1) / SBM, tiles_n = (p.N + SBN - 1) / SBN;
-    const int64_t nwg = (int64_t)tiles_m * tiles_n;
-    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+    if (ntiles > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t slots = (int64_t)2 * (cus > 0 ? cus : 256) / 8 * 8;
+    const int64_t nwg = GEN || ntiles <= slots ? ntiles : slots;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
     const float *A = static_cast<const float *>(p.A), *B = static_cast<const float *>(p.B);
     float *C = static_cast<float *>(p.C);
@@ -392,16 +456,16 @@ static hipError_t f32_fast_typed(const Problem &p)
     return hipGetLastError();
 }
 
-hipError_t f32_fast_launch(const Problem &p)
+hipError_t f32_fast_launch(const Problem &p, int cus)
 {
     if (!f32_fast_eligible(p)) return hipErrorInvalidValue;
-    return f32_fast_typed<false>(p);
+    return f32_fast_typed<false>(p, cus);
 }
 
 hipError_t f32_general_launch(const Problem &p)
 {
     if (!f32_general_eligible(p)) return hipErrorInvalidValue;
-    return f32_fast_typed<true>(p);
+    return f32_fast_typed<true>(p, 0);
 }
 
 }  // namespace gemm

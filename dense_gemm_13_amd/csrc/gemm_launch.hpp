@@ -67,7 +67,7 @@ bool mfma_ceiling_eligible(const Problem &p);
 hipError_t mfma_ceiling_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p, int cus);
 bool f32_fast_eligible(const Problem &p);
-hipError_t f32_fast_launch(const Problem &p);
+hipError_t f32_fast_launch(const Problem &p, int cus);
 bool f32_general_eligible(const Problem &p);
 hipError_t f32_general_launch(const Problem &p);
 bool f32_narrow_general_eligible(const Problem &p);

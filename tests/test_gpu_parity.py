@@ -245,6 +245,27 @@ def test_f32_large_tile_path(shape):
     _full_check("f32", *shape, 7, "f32_large")
 
 
+@pytest.mark.parametrize("shape", [(3072, 3072, 64), (5120, 4096, 64), (4096, 4096, 192)])
+def test_f32_large_tile_persistent(shape):
+    """More tiles than two workgroups per CU (576, 1280 and 1024 tiles of
+    128 x 128): each persistent workgroup walks several tiles on one ring, the
+    next tile's first steps loading during the current tile's last ones."""
+    os.environ["LIBGEMM_F32_SMALL"] = "3"
+    _full_check("f32", *shape, 8, "f32_persistent")
+
+
+def test_f32_large_tile_persistent_permutation_exact():
+    M, K = 5120, 2048                       # 640 tiles: 128 workgroups take two
+    os.environ["LIBGEMM_F32_SMALL"] = "3"
+    say("[probe] f32 persistent large-tile A*P")
+    ops, perm = _perm_case("f32", M, K, 17)
+    _, got = run_gemm("f32", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "f32")
+    bad = np.argwhere(oracle.decode(got, "f32") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 def test_f32_large_tile_permutation_exact():
     M, K = 384, 512
     os.environ["LIBGEMM_F32_SMALL"] = "3"
