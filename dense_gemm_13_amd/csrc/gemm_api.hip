@@ -159,7 +159,8 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             (forced != H16_NARROW_32x64 || h16_narrow_eligible(p)) &&
             (forced != H16_NARROW_GEN || h16_narrow_general_eligible(p)) &&
             (forced != H16_NARROW64 || h16_narrow64_eligible(p)) &&
-            (forced != H16_NARROW64_GEN || h16_narrow_general_eligible(p)))
+            (forced != H16_NARROW64_GEN || h16_narrow_general_eligible(p)) &&
+            (forced != H16_ROWS || rows_eligible(p)))
             return to_status(h16_launch(is_bf16, forced, p));
     }
     // The large-tile kernel, when its grid of 256 x 256 tiles fills at least half

@@ -229,14 +229,19 @@ hipError_t f32_launch(const Problem &p, int cus)
     // Testing override LIBGEMM_F32_SMALL: '1' forces the register-staged kernels
     // below, '2' the guarded large-tile kernel, '3' the whole-tile large-tile
     // kernel, '4' / '5' the K-split kernel with 32-row tiles (whole-tile where
-    // eligible / guarded) and '6' / '7' the same with 64-row tiles (each where it
-    // is eligible).
+    // eligible / guarded), '6' / '7' the same with 64-row tiles and '8' the
+    // vector-ALU kernel for at most 4 rows (each where it is eligible).
     const char *e = std::getenv("LIBGEMM_F32_SMALL");
-    const int force = e && e[0] >= '1' && e[0] <= '7' ? e[0] - '0' : 0;
+    const int force = e && e[0] >= '1' && e[0] <= '8' ? e[0] - '0' : 0;
     if (force == 3 && f32_fast_eligible(p)) return f32_fast_launch(p, cus);
-    if (force >= 4 && f32_narrow_general_eligible(p))
+    if (force == 8 && rows_eligible(p)) return rows_launch(OUT_F32, p);
+    if (force >= 4 && force <= 7 && f32_narrow_general_eligible(p))
         return f32_narrow_launch(p, force >= 6 ? 64 : 32, force == 5 || force == 7);
     if (force == 2 && f32_general_eligible(p)) return f32_general_launch(p);
+    // At most 4 rows: the vector-ALU stream over B (1 x 4096 x 4096 16.8 us
+    // against 44.5 on the K-split kernel, 4 x 16384 x 4096 41.3 against 54.4,
+    // 1 x 64 x 16384 44.9 against 153).
+    if (force == 0 && rows_eligible(p)) return rows_launch(OUT_F32, p);
     if (force == 0) {
         // Measured on MI355X (us; large-tile / K-split / register-staged):
         //  * from 256 tiles of 128 x 128, or 128 with K < 512, the large-tile

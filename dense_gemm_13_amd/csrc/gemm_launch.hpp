@@ -42,7 +42,8 @@ enum H16Config {
     H16_NARROW_GEN = 7,   // same kernel, guarded: any M, N >= 8, K, leading dimensions
     H16_NARROW64 = 8,     // whole 64x64 tiles, 4 waves splitting K, 2 LDS stages per wave
     H16_NARROW64_GEN = 9, // same kernel, guarded
-    H16_NUM_CONFIGS = 10
+    H16_ROWS = 10,        // at most 4 rows: vector-ALU stream over B, 64 columns per workgroup
+    H16_NUM_CONFIGS = 11
 };
 
 int h16_pick_config(int M, int N, int K);
@@ -66,6 +67,9 @@ hipError_t h16_ladder_launch(int rung, bool is_bf16, const Problem &p);
 bool mfma_ceiling_eligible(const Problem &p);
 hipError_t mfma_ceiling_launch(bool is_bf16, const Problem &p);
 hipError_t f32_launch(const Problem &p, int cus);
+// At most 4 rows of A; out: the element type (OUT_F16, OUT_BF16 or OUT_F32).
+bool rows_eligible(const Problem &p);
+hipError_t rows_launch(int out, const Problem &p);
 bool f32_fast_eligible(const Problem &p);
 hipError_t f32_fast_launch(const Problem &p, int cus);
 bool f32_general_eligible(const Problem &p);

@@ -99,6 +99,7 @@ H16_CASES = [
     (NARROW_GEN, (40, 100, 1000), (1001, 101, 103)),
     (NARROW64, (128, 128, 512), None),
     (NARROW64_GEN, (100, 150, 700), (701, 151, 153)),
+    (10, (3, 200, 300), (301, 203, 205)),   # the vector-ALU kernel for at most 4 rows
 ]
 
 
@@ -121,15 +122,17 @@ F32_PATHS = {   # override, shape, leading dimensions (None: packed), seed
     "ksplit32_guarded": ("5", (100, 150, 333), (337, 151, 155), 66),
     "ksplit64": ("6", (128, 128, 256), None, 67),
     "ksplit64_guarded": ("7", (130, 70, 200), (203, 75, 77), 68),
+    "rows": ("8", (4, 150, 333), (337, 151, 155), 69),
 }
 
 
 @pytest.mark.parametrize("path", list(F32_PATHS))
 def test_f32_paths(path):
     """The whole-tile large-tile kernel ('3'), the register-staged kernels ('1'),
-    the guarded large-tile kernel ('2') and the K-split kernel with 32-row ('4',
-    '5') and 64-row tiles ('6', '7'), whole-tile and guarded (ragged shapes,
-    unaligned leading dimensions)."""
+    the guarded large-tile kernel ('2'), the K-split kernel with 32-row ('4',
+    '5') and 64-row tiles ('6', '7'), whole-tile and guarded, and the vector-ALU
+    kernel for at most 4 rows ('8') (ragged shapes, unaligned leading
+    dimensions)."""
     force, (M, N, K), lds, seed = F32_PATHS[path]
     os.environ["LIBGEMM_F32_SMALL"] = force
     kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)

@@ -136,3 +136,23 @@ def test_operand_past_2_31_entries_exact(dtype, config):
     _check_rows(C, lambda r0, r1: bank[rows[r0:r1]], sel, dtype,
                 f"large-A {dtype} config={config}", chunk=65536)
     del bank, B, C
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rows_operand_B_past_2_31_entries_exact(dtype):
+    """The vector-ALU kernel for at most 4 rows (forced) with a B of more than
+    2^31 entries (K = 2^20 rows of 2112 columns): C[i][j] = A[i][sel[j]]."""
+    M, K, N = 3, 1 << 20, 2112
+    os.environ["LIBGEMM_F32_SMALL" if dtype == "f32" else "LIBGEMM_H16_CONFIG"] = (
+        "8" if dtype == "f32" else "10")
+    say(f"[large-B rows] {dtype} M={M} N={N} K={K}: generating")
+    A = _device(gi.operands(dtype, M, 8, K, 504)["A"], dtype)
+    sel = torch.from_numpy(np.random.default_rng(505).integers(0, K, N)).cuda()
+    B = torch.zeros((K, N), dtype=TORCH_IN[dtype], device="cuda")
+    B[sel, torch.arange(N, device="cuda")] = 1
+    assert B.numel() > 2 ** 31
+    C = torch.full((M, N), float("nan"), dtype=TORCH_OUT[dtype], device="cuda")
+    say(f"[large-B rows] {dtype}: gpu")
+    _run(dtype, A, B, C, M, K)
+    _check_rows(C, lambda r0, r1: A[r0:r1], sel, dtype, f"large-B rows {dtype}")
+    del A, B, C

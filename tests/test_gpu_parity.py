@@ -339,6 +339,48 @@ def test_f32_ksplit_permutation_exact(force):
     assert bad.size == 0, f"first mismatch at {bad[0]}"
 
 
+ROWS_ENV = {"bf16": ("LIBGEMM_H16_CONFIG", "10"), "f16": ("LIBGEMM_H16_CONFIG", "10"),
+            "f32": ("LIBGEMM_F32_SMALL", "8")}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 1, 1), None),                      # one element
+    ((1, 64, 4100), None),                  # one workgroup; K not a multiple of the row groups
+    ((2, 100, 333), (337, 101, 103)),       # partial column chunk, unaligned ld, offset pointers
+    ((3, 4095, 517), None),                 # 64 workgroups, the last one ragged
+    ((4, 130, 2048), (2051, 131, 133)),     # four rows, unaligned leading dimensions
+    ((1, 4095, 4100), (4100, 4095, 4095)),  # the tail row of 4097 x 4095 x 4100
+])
+def test_rows_path(dtype, shape, lds):
+    """The vector-ALU kernel for at most 4 rows (testing overrides: half-precision
+    config 10, fp32 '8'): zeros past K and N, a chunk straddling N element by
+    element, sums across lanes and waves."""
+    var, val = ROWS_ENV[dtype]
+    os.environ[var] = val
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[rows] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 51)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "rows")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_rows_permutation_exact(dtype):
+    M, K = 4, 520
+    var, val = ROWS_ENV[dtype]
+    os.environ[var] = val
+    say(f"[probe] rows {dtype} A*P")
+    ops, perm = _perm_case(dtype, M, K, 18)
+    _, got = run_gemm(dtype, ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], dtype)
+    bad = np.argwhere(oracle.decode(got, OUT_DTYPE[dtype]) != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 def test_fp8_large_tile_permutation_exact():
     M = K = 512
     say("[probe] fp8 large-tile A*P")
