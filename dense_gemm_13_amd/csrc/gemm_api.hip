@@ -160,14 +160,19 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             (forced != H16_NARROW_GEN || h16_narrow_general_eligible(p)) &&
             (forced != H16_NARROW64 || h16_narrow64_eligible(p)) &&
             (forced != H16_NARROW64_GEN || h16_narrow_general_eligible(p)) &&
-            (forced != H16_ROWS || rows_eligible(p)))
+            (forced != H16_ROWS || rows_eligible(p)) &&
+            (forced != H16_FAST_128 || h16_fast128_eligible(p)) &&
+            (forced != H16_GEN_128 || h16_general_eligible(p)))
             return to_status(h16_launch(is_bf16, forced, p));
     }
-    // The large-tile kernel, when its grid of 256 x 256 tiles fills at least half
-    // the chip (one workgroup per CU).
+    // The large-tile kernel with 256 x 256 tiles, when their grid fills more than
+    // half the chip (one workgroup per CU); at half or less its 128 x 128 tiles
+    // (two workgroups per CU) are faster: 2048 x 4096 x 4096 (128 tiles) 72.2 us
+    // against 81.2, but 3072^3 (144 tiles) 65.8 against 73.2.
     const int64_t tiles_n = (p.N + 255) / 256;
     const int64_t big_tiles = (int64_t)((p.M + 255) / 256) * tiles_n;
-    if (big_tiles >= 128 && h16_fast_eligible(p))
+    const bool big = 2 * big_tiles > cus;
+    if (big && h16_fast_eligible(p))
         return to_status(h16_launch(is_bf16, H16_FAST_256x256, p));
     // Tall, narrow products with a long K: 32 x 64 tiles, K split over the waves
     // (8192 x 64 x 4096: 21 us against 47 us on 64 x 64 tiles; with K = 576 the
@@ -188,7 +193,7 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     // Large problems with ragged edges or unaligned rows: the guarded large-tile
     // kernel.  A few rows left below the whole 256-row tiles that would cost an
     // extra, mostly idle round of workgroups go to the narrow kernel instead.
-    if (p.M >= 256 && p.N >= 256 && big_tiles >= 128 && h16_general_eligible(p)) {
+    if (p.M >= 256 && p.N >= 256 && big && h16_general_eligible(p)) {
         const int tail = p.M % 256;
         const int64_t main_tiles = (int64_t)(p.M / 256) * tiles_n;
         if (tail > 0 && tail <= 64 && (main_tiles + cus - 1) / cus < (big_tiles + cus - 1) / cus) {
@@ -206,34 +211,31 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
         }
         return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
     }
-    // Small and medium grids: the register-staged kernels walk all of K in one
-    // workgroup per tile, so with few tiles and a long K splitting K over the
-    // narrow kernel's waves is faster.  Measured on MI355X (bf16): 256^3 4.1 us
-    // narrow against 5.0 us on 64 x 64 tiles; 1 x 4096 x 1000 6.1 against 11.2;
-    // 1000 x 512 x 4096 16.7 against 45.6; 300 x 4096 x 4096 40.9 against 50.8;
-    // 1000^3 (64-row narrow tiles, one round) 11.8 against 18.1; with 64 x 64
-    // tiles ahead at short K (1000 x 1000 x 250: 7.1 against 11.0) and beyond
-    // ~256 tiles at K ~ 1000 (2048 x 1024 x 1024: 14.3 against 18.7).
+    // Small grids: with few tiles and a long K, splitting K over the narrow
+    // kernel's waves beats walking all of K in one workgroup per tile.  Measured
+    // on MI355X (bf16): 256^3 4.1 us narrow against 5.0 on 64 x 64 tiles;
+    // 1 x 4096 x 1000 6.1 against 11.2.  Up to 256 tiles of 64 x 64 it also beats
+    // 128 x 128 tiles where its whole-tile form applies (1024^3 6.2 against 8.4,
+    // 512 x 2048 x 2048 9.1 against 13.3) or where 128 x 128 tiles would be fewer
+    // than 64 (3000 x 200 x 3000: 22.9 against 34.4); its guarded form otherwise
+    // ties or loses (2048 x 512 x 1000: 11.1 against 9.9).
     const int64_t small_tiles = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+    const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
+    const bool narrow_whole = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64) > cus && p.M >= 64
+                                  ? h16_narrow64_eligible(p)
+                                  : h16_narrow_eligible(p);
     if (p.K >= 256 && h16_narrow_general_eligible(p) &&
-        (small_tiles < 64 || (p.K >= 512 && small_tiles <= 256) ||
-         (p.K >= 2048 && small_tiles <= 384)))
+        (small_tiles < 64 ||
+         (p.K >= 512 && small_tiles <= 256 && (narrow_whole || tiles128 < 64))))
         return narrow();
-    // Rows that are not 16-byte aligned slow the 64 x 64 tiles (their B
-    // transposes go through registers), so the narrow kernel's 64-row tiles stay
-    // ahead for up to three rounds of tiles: 1000 x 1500 x 1000 21.3 us against
-    // 27.6, 1500^3 43.4 against 53.5, 2048 x 1500 x 4096 71.3 against 83.4 on
-    // the guarded 256 x 256 tiles; not at K ~ 1000 with three rounds (2048 x 1500
-    // x 1000: 36.4 against 32.4).
-    if (!p.aligned && p.M >= 64 && h16_narrow_general_eligible(p) &&
-        ((p.K >= 768 && small_tiles <= 576) || (p.K >= 2048 && small_tiles <= 768)))
-        return narrow();
-    // Larger grids of unaligned rows with a long K: 256 x 256 tiles of the
-    // guarded kernel even when they fill only part of the chip (2048 x 1500 x
-    // 4096: 83.6 us against 141.6 on 64 x 64 tiles, whose B transposes through
-    // registers suffer most from rows that are not 16-byte aligned).
-    if (!p.aligned && p.K >= 2048 && p.M >= 256 && p.N >= 256 && h16_general_eligible(p))
-        return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
+    // Medium grids: 128 x 128 tiles of the large-tile kernel (LDS-direct ring,
+    // two workgroups per CU; whole tiles where they fit, else guarded), ahead of
+    // the register-staged and narrow kernels there: 1500^3 22.4 us against 45.3
+    // (unaligned rows), 2048^3 22.9 against 40.2, 1000 x 4096 x 4096 41.5
+    // against 70.9, 2000 x 3000 x 1000 24.3 against 44.2.
+    if (p.M >= 128 && p.N >= 128 && h16_general_eligible(p))
+        return to_status(
+            h16_launch(is_bf16, h16_fast128_eligible(p) ? H16_FAST_128 : H16_GEN_128, p));
     return to_status(h16_launch(is_bf16, h16_pick_config(p.M, p.N, p.K), p));
 }
 

@@ -1,5 +1,6 @@
 // fp16 / bf16 GEMM, large-tile path for gfx950 (whole 256 x 256 tiles, K a
-// multiple of BK * STAGES, 16-byte aligned operands).
+// multiple of BK * STAGES, 16-byte aligned operands; 128 x 128 tiles of the same
+// design for medium grids, two workgroups per CU).
 //
 // Same product as gemm_h16.hip; what changes is how operands travel:
 //   * global -> LDS with global_load_lds_dwordx4: each lane's 16 bytes land at
@@ -13,7 +14,8 @@
 //     each of the 4 rows;
 //   * 4 waves (one per SIMD), each owning a 128 x 128 sub-tile as 4 x 4 MFMA
 //     32x32x16 tiles (256 fp32 accumulators per lane), which halves the LDS
-//     bytes read per MFMA compared with 64-column wave tiles;
+//     bytes read per MFMA compared with 64-column wave tiles (128 x 128 tiles:
+//     64 x 64 sub-tiles, and half the LDS, so two workgroups share a CU);
 //   * a ring of STAGES LDS stages, one separate array per stage and stage
 //     indices known at compile time, so the compiler can tell that loads into
 //     one stage do not alias reads of another and does not serialise them.  The
@@ -36,7 +38,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int FBM = 256, FBN = 256;
 constexpr int FAST_BK = 32, FAST_STAGES = 4;
 constexpr int FAST_WM = 2, FAST_WN = 2;                  // waves along M and N
 
@@ -92,7 +93,7 @@ __device__ __forceinline__ void unroll(F &&f)
     unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The 16 KiB ring array with index idx (stages of A first, then of B).
+// The ring array with index idx (stages of A first, then of B).
 template <int HALVES>
 __device__ __forceinline__ uint16_t *ring_array(int idx)
 {
@@ -108,7 +109,8 @@ __device__ __forceinline__ uint16_t *ring_array(int idx)
     }
 }
 
-// GEN = false: whole 256 x 256 tiles, K a multiple of BK * STAGES, 16-byte
+// TB: tile rows and columns (256 or 128).
+// GEN = false: whole TB x TB tiles, K a multiple of BK * STAGES, 16-byte
 // aligned operands.  GEN = true: any M, N >= 8, K > BK and any leading
 // dimensions (the hardware runs in unaligned-access mode, so 16-byte loads and
 // stores at 2-byte-aligned addresses are legal):
@@ -126,12 +128,14 @@ __device__ __forceinline__ uint16_t *ring_array(int idx)
 // rounded (each lane reads the bias and, for beta != 0, the prior C of the
 // entries it holds; it never stores them itself, but the store of an entry
 // depends through LDS on the value this read produced).
-template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI>
-__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI, int TB>
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
+    TB == 256 ? WM * WN / 4 : 2, TB == 256 ? WM * WN / 4 : 2)))
 h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
                 int64_t ldc, int tiles_m, int tiles_n, int group_m, Epilogue epi)
 {
+    constexpr int FBM = TB, FBN = TB;
     constexpr int FNW = WM * WN;
     constexpr int FWTM = FBM / WM, FWTN = FBN / WN;      // wave sub-tile
     constexpr int FFM = FWTM / 32, FFN = FWTN / 32;      // MFMA tiles per wave
@@ -167,13 +171,15 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
         a_off[j] = (uint32_t)(lrow * lda + 8 * ((lane % CPR) ^ swz_a<BK>(row))) * 2u;
     }
-    // B block b (2 rows of 512 bytes): lane -> row 2b + lane/32, slot lane%32.
-    // For GEN the column (including n0) is part of the per-lane offset.
+    // B block b (BRPK rows of FBN halves: 2 rows of 512 bytes, or 4 of 256):
+    // lane -> row BRPK*b + lane/BCPR, slot lane%BCPR.  For GEN the column
+    // (including n0) is part of the per-lane offset.
+    constexpr int BCPR = FBN / 8, BRPK = 64 / BCPR;
     uint32_t b_off_g[B_BLK];
 #pragma unroll
     for (int j = 0; j < B_BLK; ++j) {
-        const int row = 2 * (wave * B_BLK + j) + (lane >> 5);
-        int col = 8 * ((lane & 31) ^ swz_b(row));
+        const int row = BRPK * (wave * B_BLK + j) + lane / BCPR;
+        int col = 8 * ((lane % BCPR) ^ swz_b(row));
         if (GEN) col = n0 + col >= N ? N - 8 : n0 + col;
         b_off_g[j] = (uint32_t)(row * ldb + col) * 2u;
     }
@@ -287,13 +293,19 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+        if constexpr (FFM * FFN >= DS / 2 + NBLK) {
 #pragma unroll
-        for (int x = 0; x < NBLK; ++x) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            for (int x = 0; x < NBLK; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2 - NBLK, 0);
+        } else {
+            // (64 x 64 sub-tiles: too few MFMAs to pair each load with one.)
+            static_assert(FFM * FFN > DS / 2, "MFMAs to interleave with");
+            __builtin_amdgcn_sched_group_barrier(0x020, NBLK, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2, 0);
         }
-        static_assert(FFM * FFN >= DS / 2 + NBLK, "MFMAs to interleave with");
-        __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2 - NBLK, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -386,15 +398,15 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     wait_vmcnt<0>();
 
     // ---- epilogue through LDS (the ring is idle now): each wave converts its
-    // sub-tile to 16-bit and writes it to its own 16 KiB ring arrays, then stores
+    // sub-tile to 16-bit and writes it to its own ring arrays, then stores
     // whole row segments of the sub-tile with 16 bytes per lane.  Lane l holds
     // C[32i + l%32][32j + 8q + 4*(l/32) .. +3]: 8 bytes in 16-byte chunk 4j + q,
     // half l/32.  Chunks are XORed with the row modulo the chunks per row and the
     // half with the next row bit, so the rows one store touches spread over the
     // banks.
-    static_assert(A_STAGE == 8192 && B_STAGE == 8192 && 2 * STAGES == 8, "epilogue staging");
-    constexpr int ARR = FWTM * FWTN / 8192;              // ring arrays per wave
-    constexpr int ROWS_PER_ARR = 8192 / FWTN;
+    static_assert(A_STAGE == B_STAGE && 2 * STAGES == 8, "epilogue staging");
+    constexpr int ARR = FWTM * FWTN / A_STAGE;           // ring arrays per wave
+    constexpr int ROWS_PER_ARR = A_STAGE / FWTN;
     constexpr int CPRC = FWTN / 8;                       // 16-byte chunks per staged row
     constexpr int RPI = 1024 / (FWTN * 2);               // rows per 1 KiB store
     static_assert(ARR >= 1 && ARR * FNW <= 8, "staging space");
@@ -402,7 +414,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     barrier_no_fence();                                  // every wave is done with the ring
     uint16_t *st[ARR];
 #pragma unroll
-    for (int a = 0; a < ARR; ++a) st[a] = ring_array<8192>(wave * ARR + a);
+    for (int a = 0; a < ARR; ++a) st[a] = ring_array<A_STAGE>(wave * ARR + a);
     // EPI, whole tiles: the bias of this lane's columns, loaded once for all
     // its rows.
     [[maybe_unused]] float ebias[EPI && !GEN ? FFN : 1][4][4];
@@ -481,11 +493,13 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 // Whole tiles, a whole number of stage rings and 16-byte alignment: the
 // unguarded instantiation.  The per-lane 32-bit byte offsets (up to 256 rows of
 // A or BK rows of B past a base) must fit.
-bool h16_fast_eligible(const Problem &p)
+static bool fast_whole(const Problem &p, int tb)
 {
-    return p.aligned && p.M % FBM == 0 && p.N % FBN == 0 &&
+    return p.aligned && p.M % tb == 0 && p.N % tb == 0 &&
            p.K % (FAST_BK * FAST_STAGES) == 0 && p.lda < (1 << 22) && p.ldb < (1 << 22);
 }
+bool h16_fast_eligible(const Problem &p) { return fast_whole(p, 256); }
+bool h16_fast128_eligible(const Problem &p) { return fast_whole(p, 128); }
 
 // The guarded instantiation: any leading dimensions, N >= 8, two K steps at
 // least, and offsets that fit in 32 bits (A rows are addressed from the tile's
@@ -496,10 +510,10 @@ bool h16_general_eligible(const Problem &p)
            (int64_t)FAST_BK * p.ldb + p.N < (int64_t)1 << 30;
 }
 
-template <bool GEN, bool EPI>
+template <bool GEN, bool EPI, int TB>
 static hipError_t fast_launch(bool is_bf16, const Problem &p)
 {
-    const int tiles_m = (p.M + FBM - 1) / FBM, tiles_n = (p.N + FBN - 1) / FBN;
+    const int tiles_m = (p.M + TB - 1) / TB, tiles_n = (p.N + TB - 1) / TB;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
@@ -510,25 +524,47 @@ static hipError_t fast_launch(bool is_bf16, const Problem &p)
     const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (is_bf16)
         hipLaunchKernelGGL(
-            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI>), grid, block,
-            0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m, epi);
+            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TB>), grid,
+            block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
+            group_m, epi);
     else
         hipLaunchKernelGGL(
-            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI>), grid, block,
-            0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, group_m, epi);
+            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TB>), grid,
+            block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
+            group_m, epi);
     return hipGetLastError();
+}
+
+template <int TB>
+static hipError_t fast_dispatch(bool is_bf16, bool gen, const Problem &p)
+{
+    if (gen)
+        return p.epi ? fast_launch<true, true, TB>(is_bf16, p) : fast_launch<true, false, TB>(is_bf16, p);
+    return p.epi ? fast_launch<false, true, TB>(is_bf16, p) : fast_launch<false, false, TB>(is_bf16, p);
 }
 
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_fast_eligible(p)) return hipErrorInvalidValue;
-    return p.epi ? fast_launch<false, true>(is_bf16, p) : fast_launch<false, false>(is_bf16, p);
+    return fast_dispatch<256>(is_bf16, false, p);
 }
 
 hipError_t h16_general_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_general_eligible(p)) return hipErrorInvalidValue;
-    return p.epi ? fast_launch<true, true>(is_bf16, p) : fast_launch<true, false>(is_bf16, p);
+    return fast_dispatch<256>(is_bf16, true, p);
+}
+
+hipError_t h16_fast128_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_fast128_eligible(p)) return hipErrorInvalidValue;
+    return fast_dispatch<128>(is_bf16, false, p);
+}
+
+hipError_t h16_general128_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_general_eligible(p)) return hipErrorInvalidValue;
+    return fast_dispatch<128>(is_bf16, true, p);
 }
 
 }  // namespace gemm

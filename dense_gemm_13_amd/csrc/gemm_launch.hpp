@@ -43,7 +43,9 @@ enum H16Config {
     H16_NARROW64 = 8,     // whole 64x64 tiles, 4 waves splitting K, 2 LDS stages per wave
     H16_NARROW64_GEN = 9, // same kernel, guarded
     H16_ROWS = 10,        // at most 4 rows: vector-ALU stream over B, 64 columns per workgroup
-    H16_NUM_CONFIGS = 11
+    H16_FAST_128 = 11,    // whole 128x128 tiles of the large-tile kernel, two workgroups per CU
+    H16_GEN_128 = 12,     // same kernel, guarded
+    H16_NUM_CONFIGS = 13
 };
 
 int h16_pick_config(int M, int N, int K);
@@ -52,6 +54,9 @@ bool h16_fast_eligible(const Problem &p);
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p);
 bool h16_general_eligible(const Problem &p);
 hipError_t h16_general_launch(bool is_bf16, const Problem &p);
+bool h16_fast128_eligible(const Problem &p);
+hipError_t h16_fast128_launch(bool is_bf16, const Problem &p);
+hipError_t h16_general128_launch(bool is_bf16, const Problem &p);
 bool h16_narrow_eligible(const Problem &p);
 hipError_t h16_narrow_launch(bool is_bf16, const Problem &p);
 bool h16_narrow_general_eligible(const Problem &p);

@@ -100,6 +100,8 @@ H16_CASES = [
     (NARROW64, (128, 128, 512), None),
     (NARROW64_GEN, (100, 150, 700), (701, 151, 153)),
     (10, (3, 200, 300), (301, 203, 205)),   # the vector-ALU kernel for at most 4 rows
+    (11, (256, 384, 256), None),             # 128 x 128 tiles of the large-tile kernel
+    (12, (300, 264, 200), (203, 267, 269)),  # the same, guarded
 ]
 
 
