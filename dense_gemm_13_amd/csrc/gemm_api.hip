@@ -162,7 +162,9 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             (forced != H16_NARROW64_GEN || h16_narrow_general_eligible(p)) &&
             (forced != H16_ROWS || rows_eligible(p)) &&
             (forced != H16_FAST_128 || h16_fast128_eligible(p)) &&
-            (forced != H16_GEN_128 || h16_general_eligible(p)))
+            (forced != H16_GEN_128 || h16_general_eligible(p)) &&
+            (forced != H16_FAST_128x256 || h16_fast128x256_eligible(p)) &&
+            (forced != H16_GEN_128x256 || h16_general_eligible(p)))
             return to_status(h16_launch(is_bf16, forced, p));
     }
     // The large-tile kernel with 256 x 256 tiles, when their grid fills more than
@@ -233,9 +235,18 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     // the register-staged and narrow kernels there: 1500^3 22.4 us against 45.3
     // (unaligned rows), 2048^3 22.9 against 40.2, 1000 x 4096 x 4096 41.5
     // against 70.9, 2000 x 3000 x 1000 24.3 against 44.2.
-    if (p.M >= 128 && p.N >= 128 && h16_general_eligible(p))
+    // When 128 x 256 tiles (one workgroup per CU, 64 x 128 wave tiles) fill more
+    // than half the chip they are faster still: 2560^3 37.4 against 43.6,
+    // 4096 x 2048 x 4096 63.6 against 74.3; at half or less 128 x 128 tiles keep
+    // more CUs busy (2048^3: 22.6 against 27.6).
+    if (p.M >= 128 && p.N >= 128 && h16_general_eligible(p)) {
+        const int64_t tiles128x256 = (int64_t)((p.M + 127) / 128) * ((p.N + 255) / 256);
+        if (p.N >= 256 && 2 * tiles128x256 > cus)
+            return to_status(h16_launch(
+                is_bf16, h16_fast128x256_eligible(p) ? H16_FAST_128x256 : H16_GEN_128x256, p));
         return to_status(
             h16_launch(is_bf16, h16_fast128_eligible(p) ? H16_FAST_128 : H16_GEN_128, p));
+    }
     return to_status(h16_launch(is_bf16, h16_pick_config(p.M, p.N, p.K), p));
 }
 

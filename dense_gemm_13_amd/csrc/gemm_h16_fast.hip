@@ -109,7 +109,21 @@ __device__ __forceinline__ uint16_t *ring_array(int idx)
     }
 }
 
-// TB: tile rows and columns (256 or 128).
+// The B-stage ring array with index idx (B stages follow the STAGES A stages;
+// naming only these keeps the A stages of wider tiles at their own size).
+template <int HALVES, int STAGES>
+__device__ __forceinline__ uint16_t *b_ring_array(int idx)
+{
+    static_assert(STAGES == 4, "four B stages");
+    switch (idx) {
+    case 0: return lds_stage<STAGES + 0, HALVES>;
+    case 1: return lds_stage<STAGES + 1, HALVES>;
+    case 2: return lds_stage<STAGES + 2, HALVES>;
+    default: return lds_stage<STAGES + 3, HALVES>;
+    }
+}
+
+// TBM x TBN: tile rows and columns (256 x 256, 128 x 128 or 128 x 256).
 // GEN = false: whole TB x TB tiles, K a multiple of BK * STAGES, 16-byte
 // aligned operands.  GEN = true: any M, N >= 8, K > BK and any leading
 // dimensions (the hardware runs in unaligned-access mode, so 16-byte loads and
@@ -128,14 +142,14 @@ __device__ __forceinline__ uint16_t *ring_array(int idx)
 // rounded (each lane reads the bias and, for beta != 0, the prior C of the
 // entries it holds; it never stores them itself, but the store of an entry
 // depends through LDS on the value this read produced).
-template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI, int TB>
+template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI, int TBM, int TBN>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
-    TB == 256 ? WM * WN / 4 : 2, TB == 256 ? WM * WN / 4 : 2)))
+    TBM * TBN == 128 * 128 ? 2 : WM * WN / 4, TBM * TBN == 128 * 128 ? 2 : WM * WN / 4)))
 h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
                 int64_t ldc, int tiles_m, int tiles_n, int group_m, Epilogue epi)
 {
-    constexpr int FBM = TB, FBN = TB;
+    constexpr int FBM = TBM, FBN = TBN;
     constexpr int FNW = WM * WN;
     constexpr int FWTM = FBM / WM, FWTN = FBN / WN;      // wave sub-tile
     constexpr int FFM = FWTM / 32, FFN = FWTN / 32;      // MFMA tiles per wave
@@ -404,17 +418,25 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // half l/32.  Chunks are XORed with the row modulo the chunks per row and the
     // half with the next row bit, so the rows one store touches spread over the
     // banks.
-    static_assert(A_STAGE == B_STAGE && 2 * STAGES == 8, "epilogue staging");
-    constexpr int ARR = FWTM * FWTN / A_STAGE;           // ring arrays per wave
-    constexpr int ROWS_PER_ARR = A_STAGE / FWTN;
+    // Square tiles stage in the A and B arrays alike; wider tiles (B stages
+    // larger than A stages) in the B arrays only, one per wave.
+    constexpr int SQ = A_STAGE == B_STAGE;
+    constexpr int ARR_SZ = SQ ? A_STAGE : B_STAGE;       // halves per staging array
+    static_assert(2 * STAGES == 8 && (SQ || (B_STAGE > A_STAGE && FNW <= STAGES)),
+                  "epilogue staging");
+    constexpr int ARR = FWTM * FWTN / ARR_SZ;            // ring arrays per wave
+    constexpr int ROWS_PER_ARR = ARR_SZ / FWTN;
     constexpr int CPRC = FWTN / 8;                       // 16-byte chunks per staged row
     constexpr int RPI = 1024 / (FWTN * 2);               // rows per 1 KiB store
-    static_assert(ARR >= 1 && ARR * FNW <= 8, "staging space");
+    static_assert(ARR >= 1 && ARR * FNW <= (SQ ? 8 : STAGES), "staging space");
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): own LDS reads done
     barrier_no_fence();                                  // every wave is done with the ring
     uint16_t *st[ARR];
 #pragma unroll
-    for (int a = 0; a < ARR; ++a) st[a] = ring_array<A_STAGE>(wave * ARR + a);
+    for (int a = 0; a < ARR; ++a) {
+        if constexpr (SQ) st[a] = ring_array<ARR_SZ>(wave * ARR + a);
+        else st[a] = b_ring_array<ARR_SZ, STAGES>(wave * ARR + a);
+    }
     // EPI, whole tiles: the bias of this lane's columns, loaded once for all
     // its rows.
     [[maybe_unused]] float ebias[EPI && !GEN ? FFN : 1][4][4];
@@ -493,13 +515,14 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 // Whole tiles, a whole number of stage rings and 16-byte alignment: the
 // unguarded instantiation.  The per-lane 32-bit byte offsets (up to 256 rows of
 // A or BK rows of B past a base) must fit.
-static bool fast_whole(const Problem &p, int tb)
+static bool fast_whole(const Problem &p, int tbm, int tbn)
 {
-    return p.aligned && p.M % tb == 0 && p.N % tb == 0 &&
+    return p.aligned && p.M % tbm == 0 && p.N % tbn == 0 &&
            p.K % (FAST_BK * FAST_STAGES) == 0 && p.lda < (1 << 22) && p.ldb < (1 << 22);
 }
-bool h16_fast_eligible(const Problem &p) { return fast_whole(p, 256); }
-bool h16_fast128_eligible(const Problem &p) { return fast_whole(p, 128); }
+bool h16_fast_eligible(const Problem &p) { return fast_whole(p, 256, 256); }
+bool h16_fast128_eligible(const Problem &p) { return fast_whole(p, 128, 128); }
+bool h16_fast128x256_eligible(const Problem &p) { return fast_whole(p, 128, 256); }
 
 // The guarded instantiation: any leading dimensions, N >= 8, two K steps at
 // least, and offsets that fit in 32 bits (A rows are addressed from the tile's
@@ -510,10 +533,10 @@ bool h16_general_eligible(const Problem &p)
            (int64_t)FAST_BK * p.ldb + p.N < (int64_t)1 << 30;
 }
 
-template <bool GEN, bool EPI, int TB>
+template <bool GEN, bool EPI, int TBM, int TBN>
 static hipError_t fast_launch(bool is_bf16, const Problem &p)
 {
-    const int tiles_m = (p.M + TB - 1) / TB, tiles_n = (p.N + TB - 1) / TB;
+    const int tiles_m = (p.M + TBM - 1) / TBM, tiles_n = (p.N + TBN - 1) / TBN;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
@@ -524,47 +547,61 @@ static hipError_t fast_launch(bool is_bf16, const Problem &p)
     const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (is_bf16)
         hipLaunchKernelGGL(
-            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TB>), grid,
+            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TBM, TBN>), grid,
             block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
             group_m, epi);
     else
         hipLaunchKernelGGL(
-            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TB>), grid,
+            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TBM, TBN>), grid,
             block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
             group_m, epi);
     return hipGetLastError();
 }
 
-template <int TB>
+template <int TBM, int TBN>
 static hipError_t fast_dispatch(bool is_bf16, bool gen, const Problem &p)
 {
     if (gen)
-        return p.epi ? fast_launch<true, true, TB>(is_bf16, p) : fast_launch<true, false, TB>(is_bf16, p);
-    return p.epi ? fast_launch<false, true, TB>(is_bf16, p) : fast_launch<false, false, TB>(is_bf16, p);
+        return p.epi ? fast_launch<true, true, TBM, TBN>(is_bf16, p)
+                     : fast_launch<true, false, TBM, TBN>(is_bf16, p);
+    return p.epi ? fast_launch<false, true, TBM, TBN>(is_bf16, p)
+                 : fast_launch<false, false, TBM, TBN>(is_bf16, p);
 }
 
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_fast_eligible(p)) return hipErrorInvalidValue;
-    return fast_dispatch<256>(is_bf16, false, p);
+    return fast_dispatch<256, 256>(is_bf16, false, p);
 }
 
 hipError_t h16_general_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_general_eligible(p)) return hipErrorInvalidValue;
-    return fast_dispatch<256>(is_bf16, true, p);
+    return fast_dispatch<256, 256>(is_bf16, true, p);
 }
 
 hipError_t h16_fast128_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_fast128_eligible(p)) return hipErrorInvalidValue;
-    return fast_dispatch<128>(is_bf16, false, p);
+    return fast_dispatch<128, 128>(is_bf16, false, p);
 }
 
 hipError_t h16_general128_launch(bool is_bf16, const Problem &p)
 {
     if (!h16_general_eligible(p)) return hipErrorInvalidValue;
-    return fast_dispatch<128>(is_bf16, true, p);
+    return fast_dispatch<128, 128>(is_bf16, true, p);
+}
+
+hipError_t h16_fast128x256_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_fast128x256_eligible(p)) return hipErrorInvalidValue;
+    return fast_dispatch<128, 256>(is_bf16, false, p);
+}
+
+hipError_t h16_general128x256_launch(bool is_bf16, const Problem &p)
+{
+    if (!h16_general_eligible(p)) return hipErrorInvalidValue;
+    return fast_dispatch<128, 256>(is_bf16, true, p);
 }
 
 }  // namespace gemm

@@ -45,7 +45,9 @@ enum H16Config {
     H16_ROWS = 10,        // at most 4 rows: vector-ALU stream over B, 64 columns per workgroup
     H16_FAST_128 = 11,    // whole 128x128 tiles of the large-tile kernel, two workgroups per CU
     H16_GEN_128 = 12,     // same kernel, guarded
-    H16_NUM_CONFIGS = 13
+    H16_FAST_128x256 = 13, // whole 128x256 tiles of the large-tile kernel, one workgroup per CU
+    H16_GEN_128x256 = 14, // same kernel, guarded
+    H16_NUM_CONFIGS = 15
 };
 
 int h16_pick_config(int M, int N, int K);
@@ -57,6 +59,9 @@ hipError_t h16_general_launch(bool is_bf16, const Problem &p);
 bool h16_fast128_eligible(const Problem &p);
 hipError_t h16_fast128_launch(bool is_bf16, const Problem &p);
 hipError_t h16_general128_launch(bool is_bf16, const Problem &p);
+bool h16_fast128x256_eligible(const Problem &p);
+hipError_t h16_fast128x256_launch(bool is_bf16, const Problem &p);
+hipError_t h16_general128x256_launch(bool is_bf16, const Problem &p);
 bool h16_narrow_eligible(const Problem &p);
 hipError_t h16_narrow_launch(bool is_bf16, const Problem &p);
 bool h16_narrow_general_eligible(const Problem &p);

@@ -102,6 +102,8 @@ H16_CASES = [
     (10, (3, 200, 300), (301, 203, 205)),   # the vector-ALU kernel for at most 4 rows
     (11, (256, 384, 256), None),             # 128 x 128 tiles of the large-tile kernel
     (12, (300, 264, 200), (203, 267, 269)),  # the same, guarded
+    (13, (256, 512, 256), None),             # 128 x 256 tiles of the large-tile kernel
+    (14, (300, 520, 200), (203, 523, 525)),  # the same, guarded
 ]
 
 

@@ -22,7 +22,7 @@ from gpu_helpers import TOL, OUT_DTYPE, compare, reference, run_gemm, say, to_de
 
 pytestmark = pytest.mark.gpu
 
-H16_CONFIGS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12)
+H16_CONFIGS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 13, 14)
 FAST = 4          # whole 256x256 tiles, K % 128 == 0, aligned
 GENERAL = 5       # the same kernel, guarded: ragged M/N/K, any leading dimensions
 NARROW = 6        # whole 32x64 tiles, K % 64 == 0, K >= 256, aligned; waves split K
@@ -31,6 +31,8 @@ NARROW64 = 8      # whole 64x64 tiles, K % 64 == 0, K >= 256, aligned; waves spl
 NARROW64_GEN = 9  # the same kernel, guarded
 FAST128 = 11      # whole 128x128 tiles of the large-tile kernel, two workgroups per CU
 GEN128 = 12       # the same kernel, guarded
+FAST128x256 = 13  # whole 128x256 tiles of the large-tile kernel, one workgroup per CU
+GEN128x256 = 14   # the same kernel, guarded
 
 
 @pytest.fixture(autouse=True)
@@ -69,7 +71,7 @@ def _perm_case(dtype, M, K, seed):
 def test_permutation_probe_exact(dtype, config):
     if config is not None:
         os.environ["LIBGEMM_H16_CONFIG"] = str(config)
-    M, K = (512, 512) if config in (FAST, FAST128) else (320, 384)
+    M, K = (512, 512) if config in (FAST, FAST128, FAST128x256) else (320, 384)
     say(f"[probe] A*P {dtype} config={config} M={M} N=K={K}")
     ops, perm = _perm_case(dtype, M, K, 7)
     _, got = run_gemm(dtype, ops, M, K, K)
@@ -434,6 +436,40 @@ def test_fast128_whole_tiles(dtype, shape):
     ops = gi.operands(dtype, M, N, K, 44)
     _, got = run_gemm(dtype, ops, M, N, K)
     ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "fast128")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(128, 256, 128), (256, 512, 384), (512, 768, 1152),
+                                   (1024, 1024, 2048)])
+def test_fast128x256_whole_tiles(dtype, shape):
+    """128 x 256 tiles of the large-tile kernel (config 13): wave tiles of
+    64 x 128, the epilogue staged in the B stage arrays."""
+    os.environ["LIBGEMM_H16_CONFIG"] = str(FAST128x256)
+    M, N, K = shape
+    say(f"[fast128x256] {dtype} {M}x{N}x{K}")
+    ops = gi.operands(dtype, M, N, K, 46)
+    _, got = run_gemm(dtype, ops, M, N, K)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "fast128x256")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 8, 33), None),                      # one row, eight columns, a partial second K block
+    ((129, 257, 97), None),                  # a row and a column past a tile
+    ((300, 520, 203), (206, 521, 525)),      # unaligned leading dimensions, offset pointers
+    ((1000, 1000, 1000), None),              # the 1000^3 workload's shape
+])
+def test_general128x256_edges(dtype, shape, lds):
+    """The guarded 128 x 256 instantiation (config 14)."""
+    os.environ["LIBGEMM_H16_CONFIG"] = str(GEN128x256)
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[general128x256] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 47)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "general128x256")
     assert ok, msg
 
 
