@@ -311,12 +311,13 @@ int fp8_entry(const uint8_t *A, const uint8_t *B, void *C, int64_t M, int64_t N,
         if (overlaps(C, cb, scale_a, sab) || overlaps(C, cb, scale_b, sbb)) return GEMM_ERR_ALIAS;
     }
     if (epi && (st = check_bias(epi->bias, C, M, N, ldc, 2)) != GEMM_OK) return st;
-    if ((st = check_device()) != GEMM_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != GEMM_OK) return st;
     if (K == 0) return to_status(empty_sum_launch(C, (int)M, (int)N, ldc, OUT_BF16, epi, stream));
     Problem p{A, B, C, (int)M, (int)N, (int)K, lda, ldb, ldc, false, stream, epi};
     p.aligned = aligned16(A) && ((uintptr_t)B & 3) == 0 && aligned16(C) && lda % 16 == 0 &&
                 ldb % 4 == 0 && ldc % 8 == 0;
-    return to_status(fp8_launch(p, scale_a, scale_b));
+    return to_status(fp8_launch(p, scale_a, scale_b, cus));
 }
 
 }  // namespace

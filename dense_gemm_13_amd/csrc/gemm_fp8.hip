@@ -275,19 +275,38 @@ hipError_t launch_cfg(const Problem &p, const float *sa, const float *sb)
 
 }  // namespace
 
-hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b)
+hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b, int cus)
 {
     // Testing override LIBGEMM_FP8_SMALL: '1' forces the register-staged kernels
-    // below, '2' the guarded large-tile kernel (where it is eligible).
+    // below, '2' the guarded large-tile kernel, '3' / '4' the K-split kernel with
+    // 32-row tiles (whole-tile where eligible / guarded), '5' / '6' the same with
+    // 64-row tiles and '7' the whole-tile large-tile kernel (each where it is
+    // eligible).
     const char *e = std::getenv("LIBGEMM_FP8_SMALL");
-    const int force = e && (e[0] == '1' || e[0] == '2') ? e[0] - '0' : 0;
+    const int force = e && e[0] >= '1' && e[0] <= '7' ? e[0] - '0' : 0;
+    if (force == 7 && fp8_fast_eligible(p)) return fp8_fast_launch(p, scale_a, scale_b);
+    if (force >= 3 && force <= 6 && fp8_narrow_general_eligible(p))
+        return fp8_narrow_launch(p, scale_a, scale_b, force >= 5 ? 64 : 32, force == 4 || force == 6);
+    // Small grids (at most one round of 64 x 64 tiles) and narrow products (N <=
+    // 128): the K-split kernel, with 64-row tiles when that costs no more rounds
+    // of one workgroup per CU than 32-row tiles.  Measured (us; K-split /
+    // 256 x 256 tiles): 8192 x 64 x 4096 11.1 / 63.5, 300 x 1500 x 4096 17.5 /
+    // 62.3, 1000^3 15.5 / 26.6, 65536 x 64 x 2048 33.5 / 44.7; but 1500^3 42.8 /
+    // 32.1 and 2000 x 3000 x 1000 71.0 / 28.6.
+    const int64_t cu = cus > 0 ? cus : 256;
+    const int64_t t32 = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64);
+    const int64_t t64 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+    if (force == 0 && (t64 <= cu || p.N <= 128) && fp8_narrow_general_eligible(p)) {
+        const bool rows64 = p.M >= 64 && 2 * ((t64 + cu - 1) / cu) <= (t32 + cu - 1) / cu;
+        return fp8_narrow_launch(p, scale_a, scale_b, rows64 ? 64 : 32, false);
+    }
     if (force == 0 && fp8_fast_eligible(p)) return fp8_fast_launch(p, scale_a, scale_b);
     // Any other shape with N >= 16 and K > 64: the guarded large-tile kernel
     // (measured: 4097 x 4095 x 4100 145 us against 1772 on the register-staged
     // kernels, 8200^2 x 8192 647 against 1886, 1000^3 26 against 89).
     if (force != 1 && fp8_general_eligible(p)) return fp8_general_launch(p, scale_a, scale_b);
-    const int64_t big = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
-    if (big >= 128) return launch_cfg<128, 128, 2, 2>(p, scale_a, scale_b);
+    const int64_t big128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
+    if (big128 >= 128) return launch_cfg<128, 128, 2, 2>(p, scale_a, scale_b);
     return launch_cfg<64, 64, 2, 1>(p, scale_a, scale_b);
 }
 

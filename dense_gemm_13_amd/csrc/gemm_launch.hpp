@@ -86,7 +86,10 @@ bool f32_general_eligible(const Problem &p);
 hipError_t f32_general_launch(const Problem &p);
 bool f32_narrow_general_eligible(const Problem &p);
 hipError_t f32_narrow_launch(const Problem &p, int tbm, bool force_general);
-hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b);
+hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale_b, int cus);
+bool fp8_narrow_general_eligible(const Problem &p);
+hipError_t fp8_narrow_launch(const Problem &p, const float *scale_a, const float *scale_b, int tbm,
+                             bool force_general);
 bool fp8_fast_eligible(const Problem &p);
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);
 bool fp8_general_eligible(const Problem &p);

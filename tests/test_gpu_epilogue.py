@@ -144,17 +144,24 @@ def test_f32_paths(path):
     check("f32", ops, M, N, K, 1.5, 0.25, True, "relu", seed, "f32 " + path, **kw)
 
 
-@pytest.mark.parametrize("path", ["large", "small", "guarded"])
+FP8_PATHS = {   # override, shape, leading dimensions, seed
+    "large": ("7", (512, 512, 512), {}, 61),
+    "small": ("1", (200, 136, 320), dict(ldc=139), 62),
+    "guarded": ("2", (300, 270, 200), dict(lda=203, ldb=275, ldc=277, offset=1), 63),
+    "ksplit32": ("3", (96, 192, 320), {}, 64),
+    "ksplit64_guarded": ("6", (130, 70, 200), dict(lda=203, ldb=75, ldc=77, offset=1), 65),
+}
+
+
+@pytest.mark.parametrize("path", list(FP8_PATHS))
 def test_fp8_paths(path):
-    """The large-tile kernel, the register-staged kernels ('1') and the guarded
-    large-tile kernel ('2', ragged shape, unaligned leading dimensions)."""
-    if path != "large":
-        os.environ["LIBGEMM_FP8_SMALL"] = "1" if path == "small" else "2"
-    M, N, K = {"large": (512, 512, 512), "small": (200, 136, 320), "guarded": (300, 270, 200)}[path]
-    kw = {"large": {}, "small": dict(ldc=139),
-          "guarded": dict(lda=203, ldb=275, ldc=277, offset=1)}[path]
+    """The whole-tile large-tile kernel ('7'), the register-staged kernels ('1'),
+    the guarded large-tile kernel ('2') and the K-split kernel ('3': 32-row
+    whole tiles, '6': 64-row guarded) on ragged shapes with unaligned leading
+    dimensions."""
+    force, (M, N, K), kw, seed = FP8_PATHS[path]
+    os.environ["LIBGEMM_FP8_SMALL"] = force
     ops = gi.operands("fp8", M, N, K, 61)
-    seed = {"large": 61, "small": 62, "guarded": 63}[path]
     check("fp8", ops, M, N, K, 0.5, 1.0, True, "relu", seed, "fp8 " + path, **kw)
 
 

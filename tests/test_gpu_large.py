@@ -33,10 +33,10 @@ TORCH_OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
 
 @pytest.fixture(autouse=True)
 def _clear_config_override():
-    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_F32_SMALL"):
+    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_F32_SMALL", "LIBGEMM_FP8_SMALL"):
         os.environ.pop(v, None)
     yield
-    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_F32_SMALL"):
+    for v in ("LIBGEMM_H16_CONFIG", "LIBGEMM_F32_SMALL", "LIBGEMM_FP8_SMALL"):
         os.environ.pop(v, None)
     torch.cuda.empty_cache()
 
@@ -111,14 +111,14 @@ BANK_ROWS = 1021
 
 
 @pytest.mark.parametrize("dtype,config", [("bf16", None), ("bf16", 2), ("bf16", 5),
-                                          ("fp8", None), ("f32", None), ("f32", 2)])
+                                          ("fp8", None), ("fp8", 2), ("f32", None), ("f32", 2)])
 def test_operand_past_2_31_entries_exact(dtype, config):
-    """A holds more than 2^31 entries; N = 64.  bf16 and f32 with the default
-    dispatch take their K-split kernels; bf16 configs 2 and 5 force the 64 x 64
-    register-staged kernel and the guarded large-tile kernel, f32 override 2 the
-    guarded large-tile kernel; fp8 takes its guarded large-tile kernel."""
+    """A holds more than 2^31 entries; N = 64.  Every dtype with the default
+    dispatch takes its K-split kernel; bf16 configs 2 and 5 force the 64 x 64
+    register-staged kernel and the guarded large-tile kernel, and fp8 / f32
+    override 2 their guarded large-tile kernels."""
     if config is not None:
-        var = "LIBGEMM_F32_SMALL" if dtype == "f32" else "LIBGEMM_H16_CONFIG"
+        var = {"f32": "LIBGEMM_F32_SMALL", "fp8": "LIBGEMM_FP8_SMALL"}.get(dtype, "LIBGEMM_H16_CONFIG")
         os.environ[var] = str(config)
     K, N = 2048, 64
     M = (1 << 31) // K + 64                        # M*K = 2^31 + 64K

@@ -171,7 +171,10 @@ def test_fp8_full_ragged(shape):
 
 @pytest.mark.parametrize("shape", [(256, 256, 256), (768, 512, 1024), (512, 1280, 768)])
 def test_fp8_large_tile_path(shape):
-    """Whole 256x256 tiles and K % 256 == 0 take the large-tile fp8 kernel."""
+    """Whole 256x256 tiles and K % 256 == 0: the large-tile fp8 kernel (forced
+    with the testing override '7': by default grids this small take the K-split
+    kernel)."""
+    os.environ["LIBGEMM_FP8_SMALL"] = "7"
     _full_check("fp8", *shape, 6, "fp8_large")
 
 
@@ -194,6 +197,65 @@ def test_fp8_guarded_large_tile_path(shape, lds):
     _, got = run_gemm("fp8", ops, M, N, K, **kw)
     ok, msg, _ = compare("fp8", got, reference("fp8", ops, M, N, K), "fp8-guarded")
     assert ok, msg
+
+
+@pytest.mark.parametrize("force,shape", [
+    ("3", (32, 64, 256)),       # 32-row tiles: one tile, one K block per wave
+    ("3", (96, 128, 320)),      # 5 K blocks: wave 0 takes two
+    ("3", (160, 192, 832)),     # 13 blocks: wave 0 goes round the 4-stage ring and more
+    ("3", (2048, 64, 1088)),    # 17 blocks, 64 row strips (rotated K walks)
+    ("5", (64, 64, 256)),       # 64-row tiles: one tile
+    ("5", (192, 128, 448)),     # 7 blocks: 2,2,2,1 per wave
+    ("5", (320, 256, 1088)),    # 17 blocks, several row strips
+])
+def test_fp8_ksplit_path(force, shape):
+    """The fp8 K-split kernel on whole tiles (testing overrides '3': 32-row
+    tiles, '5': 64-row tiles): one scale product per wave step, LDS reduction."""
+    os.environ["LIBGEMM_FP8_SMALL"] = force
+    M, N, K = shape
+    say(f"[fp8-ksplit {force}] {M}x{N}x{K}")
+    ops = gi.operands("fp8", M, N, K, 52)
+    _, got = run_gemm("fp8", ops, M, N, K)
+    ok, msg, _ = compare("fp8", got, reference("fp8", ops, M, N, K), "fp8-ksplit")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("force", ["4", "6"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 16, 1), None),                    # one row, sixteen columns, one k
+    ((5, 200, 64), None),                  # one K block: the register-loaded block only
+    ((33, 65, 65), None),                  # partial tiles both ways, partial K block
+    ((31, 64, 300), (303, 67, 71)),        # unaligned leading dimensions, offset pointers
+    ((64, 70, 129), None),                 # 3 K blocks: two waves without LDS-direct blocks
+    ((100, 300, 1000), (1001, 301, 303)),  # 16 blocks incl. the partial one
+    ((1000, 1000, 1000), None),            # the 1000^3 shape
+])
+def test_fp8_ksplit_general_edges(force, shape, lds):
+    """The guarded fp8 K-split kernel (testing overrides '4': 32-row tiles, '6':
+    64-row tiles): clamped rows and column chunks, the last K block through
+    registers with zero fill, masked stores."""
+    os.environ["LIBGEMM_FP8_SMALL"] = force
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[fp8-ksplit-general {force}] {M}x{N}x{K} {kw}")
+    ops = gi.operands("fp8", M, N, K, 53)
+    _, got = run_gemm("fp8", ops, M, N, K, **kw)
+    ok, msg, _ = compare("fp8", got, reference("fp8", ops, M, N, K), "fp8-ksplit-general")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("force", ["3", "6"])
+def test_fp8_ksplit_permutation_exact(force):
+    """A * P with unit scales: every output is one product by 1 plus zeros."""
+    M, K = 320, 256
+    os.environ["LIBGEMM_FP8_SMALL"] = force
+    say(f"[probe] fp8 K-split {force} A*P")
+    ops, perm = _perm_case("fp8", M, K, 19)
+    _, got = run_gemm("fp8", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "fp8")
+    bad = np.argwhere(oracle.decode(got, "bf16") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
 
 
 def test_fp8_guarded_permutation_exact():
@@ -387,6 +449,7 @@ def test_rows_permutation_exact(dtype):
 
 def test_fp8_large_tile_permutation_exact():
     M = K = 512
+    os.environ["LIBGEMM_FP8_SMALL"] = "7"
     say("[probe] fp8 large-tile A*P")
     ops, perm = _perm_case("fp8", M, K, 9)
     _, got = run_gemm("fp8", ops, M, K, K)
