@@ -280,26 +280,35 @@ hipError_t fp8_launch(const Problem &p, const float *scale_a, const float *scale
     // Testing override LIBGEMM_FP8_SMALL: '1' forces the register-staged kernels
     // below, '2' the guarded large-tile kernel, '3' / '4' the K-split kernel with
     // 32-row tiles (whole-tile where eligible / guarded), '5' / '6' the same with
-    // 64-row tiles and '7' the whole-tile large-tile kernel (each where it is
-    // eligible).
+    // 64-row tiles, '7' the whole-tile large-tile kernel and '8' / '9' its 128 x
+    // 128 tiles (whole-tile where eligible / guarded), each where it is eligible.
     const char *e = std::getenv("LIBGEMM_FP8_SMALL");
-    const int force = e && e[0] >= '1' && e[0] <= '7' ? e[0] - '0' : 0;
+    const int force = e && e[0] >= '1' && e[0] <= '9' ? e[0] - '0' : 0;
     if (force == 7 && fp8_fast_eligible(p)) return fp8_fast_launch(p, scale_a, scale_b);
+    if (force >= 8 && fp8_general_eligible(p))
+        return fp8_tiles128_launch(p, scale_a, scale_b, force == 9);
     if (force >= 3 && force <= 6 && fp8_narrow_general_eligible(p))
         return fp8_narrow_launch(p, scale_a, scale_b, force >= 5 ? 64 : 32, force == 4 || force == 6);
-    // Small grids (at most one round of 64 x 64 tiles) and narrow products (N <=
-    // 128): the K-split kernel, with 64-row tiles when that costs no more rounds
-    // of one workgroup per CU than 32-row tiles.  Measured (us; K-split /
-    // 256 x 256 tiles): 8192 x 64 x 4096 11.1 / 63.5, 300 x 1500 x 4096 17.5 /
-    // 62.3, 1000^3 15.5 / 26.6, 65536 x 64 x 2048 33.5 / 44.7; but 1500^3 42.8 /
-    // 32.1 and 2000 x 3000 x 1000 71.0 / 28.6.
+    // Narrow products (M < 128 or N <= 128) and small grids with a long K (at most
+    // one round of 64 x 64 tiles, K >= 2048): the K-split kernel, with 64-row
+    // tiles when that costs no more rounds of one workgroup per CU than 32-row
+    // tiles.  Measured (us; K-split / 128 x 128 tiles / 256 x 256 tiles):
+    // 8192 x 64 x 4096 11.5 / 25.6 / 62.0, 1 x 4096 x 4096 12.8 / 23.4 / 56.8,
+    // 512 x 2048 x 2048 11.4 / 14.6 / 31.9; but 1000^3 15.7 / 11.9 / 26.3.
     const int64_t cu = cus > 0 ? cus : 256;
     const int64_t t32 = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64);
     const int64_t t64 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
-    if (force == 0 && (t64 <= cu || p.N <= 128) && fp8_narrow_general_eligible(p)) {
+    if (force == 0 && (p.M < 128 || p.N <= 128 || (t64 <= cu && p.K >= 2048)) &&
+        fp8_narrow_general_eligible(p)) {
         const bool rows64 = p.M >= 64 && 2 * ((t64 + cu - 1) / cu) <= (t32 + cu - 1) / cu;
         return fp8_narrow_launch(p, scale_a, scale_b, rows64 ? 64 : 32, false);
     }
+    // Medium grids, which fill at most half the chip in 256 x 256 tiles: 128 x
+    // 128 tiles of the same kernel, two workgroups per CU (2048^3 17.0 us against
+    // 33.9, 1500^3 15.4 against 32.7, 2048 x 4096 x 4096 48.7 against 67.1).
+    const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (force == 0 && 2 * big <= cu && p.M >= 128 && p.N >= 128 && fp8_general_eligible(p))
+        return fp8_tiles128_launch(p, scale_a, scale_b, false);
     if (force == 0 && fp8_fast_eligible(p)) return fp8_fast_launch(p, scale_a, scale_b);
     // Any other shape with N >= 16 and K > 64: the guarded large-tile kernel
     // (measured: 4097 x 4095 x 4100 145 us against 1772 on the register-staged

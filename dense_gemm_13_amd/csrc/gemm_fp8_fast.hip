@@ -1,6 +1,7 @@
 // FP8 (OCP E4M3) block-scaled GEMM, large-tile path for gfx950: 256 x 256
-// tiles; whole tiles with K a multiple of 256 and 16-byte aligned rows, or (the
-// guarded instantiation) any shape with N >= 16 and K > 64.
+// tiles (128 x 128 for medium grids, two workgroups per CU); whole tiles with K
+// a multiple of 256 and 16-byte aligned rows, or (the guarded instantiation)
+// any shape with N >= 16 and K > 64.
 //
 //   C[i][j] = bf16( sum_kb  sa(i/64, kb) * sb(kb, j/64) * sum_{k in block kb} qa(i,k) qb(k,j) )
 //
@@ -41,35 +42,49 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void8_t;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
-constexpr int QBM = 256, QBN = 256, QBK = 64, QSTAGES = 4;
-constexpr int QWM = 2, QWN = 4, QNW = QWM * QWN;       // 8 waves
-constexpr int QWTM = QBM / QWM, QWTN = QBN / QWN;       // 128 x 64 per wave
-constexpr int QFM = QWTM / 32, QFN = QWTN / 32;         // 4 x 2 MFMA tiles
-constexpr int QA_STAGE = QBM * QBK;                      // bytes per stage (16 KiB)
-constexpr int QB_STAGE = QBK * QBN;
-constexpr int QA_BLK = QA_STAGE / 1024 / QNW;            // 1 KiB loads per wave per stage
-constexpr int QB_BLK = QB_STAGE / 1024 / QNW;
-constexpr int QNBLK = QA_BLK + QB_BLK;
+constexpr int QBK = 64, QSTAGES = 4;
+constexpr int QNW = 8;                                   // waves
 
-template <int TAG>
-__shared__ __attribute__((aligned(1024))) uint8_t q_stage[16384];
+// Tile shapes: TB = 256 (waves 2 x 4 of 128 x 64, 4 x 2 MFMA tiles each) or
+// TB = 128 (waves 4 x 2 of 32 x 64, 1 x 2 MFMA tiles each).  Every wave's
+// sub-tile is 64 columns wide, so each MFMA pair shares one A tile and the
+// step below runs the same way for both.
+template <int TB>
+struct QShape {
+    static constexpr int BM = TB, BN = TB;
+    static constexpr int WM = TB == 256 ? 2 : 4, WN = QNW / WM;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;   // 128 x 64 or 32 x 64 per wave
+    static constexpr int FM = WTM / 32, FN = WTN / 32;   // 4 x 2 or 1 x 2 MFMA tiles
+    static constexpr int A_STAGE = BM * QBK;             // bytes per stage (16 or 8 KiB)
+    static constexpr int B_STAGE = QBK * BN;
+    static constexpr int A_BLK = A_STAGE / 1024 / QNW;   // 1 KiB loads per wave per stage
+    static constexpr int B_BLK = B_STAGE / 1024 / QNW;
+    static constexpr int NBLK = A_BLK + B_BLK;
+    static constexpr int BCPR = BN / 16;                 // 16-byte chunks per B row
+    static constexpr int BRPK = 64 / BCPR;               // B rows per 1 KiB load
+    static_assert(WTN == 64 && A_BLK >= 1 && B_BLK >= 1, "tile shape");
+};
+
+template <int TAG, int BYTES>
+__shared__ __attribute__((aligned(1024))) uint8_t q_stage[BYTES];
 // The block scales of one stage (4 of A's scale rows, then 4 of B's scale
 // columns), 64 copies of each (one per lane of the wave that loads it), one
 // array per stage like the operand stages.
 template <int TAG>
 __shared__ __attribute__((aligned(256))) float q_scale[8 * 64];
 
+template <int BYTES>
 __device__ __forceinline__ uint8_t *q_ring(int idx)
 {
     switch (idx) {
-    case 0: return q_stage<0>;
-    case 1: return q_stage<1>;
-    case 2: return q_stage<2>;
-    case 3: return q_stage<3>;
-    case 4: return q_stage<4>;
-    case 5: return q_stage<5>;
-    case 6: return q_stage<6>;
-    default: return q_stage<7>;
+    case 0: return q_stage<0, BYTES>;
+    case 1: return q_stage<1, BYTES>;
+    case 2: return q_stage<2, BYTES>;
+    case 3: return q_stage<3, BYTES>;
+    case 4: return q_stage<4, BYTES>;
+    case 5: return q_stage<5, BYTES>;
+    case 6: return q_stage<6, BYTES>;
+    default: return q_stage<7, BYTES>;
     }
 }
 
@@ -77,7 +92,27 @@ __device__ __forceinline__ uint8_t *q_ring(int idx)
 __host__ __device__ __forceinline__ int qswz_a(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 // B rows: 256 bytes (16 chunks).  The 8 rows of one transposing read land in 8
 // distinct even chunks (and the neighbouring 16-column group in the odd ones).
-__host__ __device__ __forceinline__ int qswz_b(int k) { return (k & 7) << 1; }
+// Rows of 128 bytes (8 chunks): rows two apart share banks, so the 4 rows of
+// each parity take 4 distinct even chunks.
+template <int BN>
+__host__ __device__ __forceinline__ int qswz_b(int k)
+{
+    if constexpr (BN == 256) return (k & 7) << 1;
+    else return ((k >> 1) & 3) << 1;
+}
+
+// Global -> LDS loads of 16 bytes (operands) and 4 bytes (scales) per lane.
+// (Functions of their own: with arguments that depend on the kernel's template
+// parameters, the builtin called directly in the kernel's lambdas leaves the
+// host-side instantiation of the kernel invalid and its launch stub undefined.)
+__device__ __forceinline__ void q_dma16(const void *src, uint8_t *lds)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void8_t *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void q_dma4(const void *src, float *lds)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void8_t *)lds, 4, 0, 0);
+}
 
 template <int N>
 __device__ __forceinline__ void q_wait_vmcnt()
@@ -116,14 +151,20 @@ __device__ __forceinline__ void q_unroll(F &&f)
 // EPI: the fused epilogue is applied to the fp32 accumulators before they are
 // rounded; the lane that reads an entry's prior C does not store it, but the
 // store depends through LDS on the value that read produced.
-template <bool GEN, bool EPI>
-__global__ void __launch_bounds__(QNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool GEN, bool EPI, int TB>
+__global__ void __launch_bounds__(QNW * 64) __attribute__((amdgpu_waves_per_eu(
+    TB == 256 ? 2 : 4, TB == 256 ? 2 : 4)))
 fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                 uint16_t *__restrict__ C, int M, int N, int K, int64_t lda, int64_t ldb,
                 int64_t ldc, const float *__restrict__ scale_a, const float *__restrict__ scale_b,
                 int mblocks, int kblocks, int nblocks, int tiles_m, int tiles_n, int group_m,
                 Epilogue epi)
 {
+    using Sh = QShape<TB>;
+    constexpr int QBM = Sh::BM, QBN = Sh::BN, QWN = Sh::WN, QWTM = Sh::WTM, QWTN = Sh::WTN;
+    constexpr int QFM = Sh::FM, QFN = Sh::FN, QA_BLK = Sh::A_BLK, QB_BLK = Sh::B_BLK;
+    constexpr int QNBLK = Sh::NBLK, QSTAGE = Sh::A_STAGE;
+    static_assert(Sh::A_STAGE == Sh::B_STAGE, "square tiles");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,7 +178,8 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     // ---- this wave's 1 KiB loads.  A block b: 16 rows of 64 bytes, lane ->
     // row 16b + lane/4, slot lane%4 holding logical chunk slot ^ qswz_a(row).
-    // B block b: 4 rows of 256 bytes, lane -> row 4b + lane/16, slot lane%16.
+    // B block b: BRPK rows of BN bytes (4 of 256 or 8 of 128), lane -> row
+    // BRPK*b + lane/BCPR, slot lane%BCPR.
     uint32_t a_off[QA_BLK], b_off[QB_BLK];
 #pragma unroll
     for (int j = 0; j < QA_BLK; ++j) {
@@ -148,8 +190,8 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // (GEN: the column, n0 included, is part of the per-lane offset.)
 #pragma unroll
     for (int j = 0; j < QB_BLK; ++j) {
-        const int row = 4 * (wave * QB_BLK + j) + (lane >> 4);
-        int col = 16 * ((lane & 15) ^ qswz_b(row));
+        const int row = Sh::BRPK * (wave * QB_BLK + j) + lane / Sh::BCPR;
+        int col = 16 * ((lane % Sh::BCPR) ^ qswz_b<QBN>(row));
         if (GEN) col = n0 + col >= N ? N - 16 : n0 + col;
         b_off[j] = (uint32_t)(row * ldb + col);
     }
@@ -161,10 +203,10 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const uint8_t *bb = b_base + kt * b_step;
 #pragma unroll
         for (int j = 0; j < QA_BLK; ++j)
-            __builtin_amdgcn_global_load_lds(ab + a_off[j], (lds_void8_t *)(as + (wave * QA_BLK + j) * 1024), 16, 0, 0);
+            q_dma16(ab + a_off[j], as + (wave * QA_BLK + j) * 1024);
 #pragma unroll
         for (int j = 0; j < QB_BLK; ++j)
-            __builtin_amdgcn_global_load_lds(bb + b_off[j], (lds_void8_t *)(bs + (wave * QB_BLK + j) * 1024), 16, 0, 0);
+            q_dma16(bb + b_off[j], bs + (wave * QB_BLK + j) * 1024);
     };
 
     // ---- fragment addressing (bytes, relative to a stage)
@@ -183,7 +225,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
     for (int j = 0; j < QFN; ++j) {
         const int n = wn0 + 32 * j + 16 * (g & 1) + 8 * (w16 & 1);
-        b_off_r[j] = (32 * (g >> 1) + r8) * QBN + (((n >> 4) ^ qswz_b(r8)) << 4) + (n & 15);
+        b_off_r[j] = (32 * (g >> 1) + r8) * QBN + (((n >> 4) ^ qswz_b<QBN>(r8)) << 4) + (n & 15);
     }
 
     // ---- block scales.  Every stage also carries the 8 scales of its K block
@@ -202,9 +244,8 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // K step s loads K block s (GEN: block s - 1; step 0 is the last block).
     auto issue_all = [&](auto S, int s) {
         const int kb = GEN ? s - 1 : s;
-        issue(q_stage<S>, q_stage<QSTAGES + S>, kb);
-        __builtin_amdgcn_global_load_lds(sc_src + kb * sc_step,
-                                         (lds_void8_t *)&q_scale<S>[64 * wave], 4, 0, 0);
+        issue(q_stage<S, QSTAGE>, q_stage<QSTAGES + S, QSTAGE>, kb);
+        q_dma4(sc_src + kb * sc_step, &q_scale<S>[64 * wave]);
     };
     constexpr int QLOADS = QNBLK + 1;                    // loads per wave per stage
     const int ktiles = (K + QBK - 1) / QBK;              // !GEN: K / QBK, a multiple of QSTAGES
@@ -305,18 +346,18 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         __builtin_amdgcn_sched_barrier(0);
         const int nxt = s + QSTAGES;
         issue_all(S, nxt < ktiles ? nxt : ktiles - 1);
-        read_b(q_stage<QSTAGES + N1>, 0);
+        read_b(q_stage<QSTAGES + N1, QSTAGE>, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = NT / 2; t < NT; ++t) {
             mma(t);
             promote(t - 1, cs0, cs1);
-            read_a(q_stage<N1>, t - NT / 2);
+            read_a(q_stage<N1, QSTAGE>, t - NT / 2);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        read_b(q_stage<QSTAGES + N1>, 1);
+        read_b(q_stage<QSTAGES + N1, QSTAGE>, 1);
         ps0 = cs0;
         ps1 = cs1;
         read_scales(q_scale<N1>);
@@ -333,7 +374,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // its scales (written before any LDS-direct load is issued).
     if constexpr (GEN) {
         const int k0 = QBK * (ktiles - 1);
-        uint8_t *as = q_stage<0>, *bs = q_stage<QSTAGES>;
+        uint8_t *as = q_stage<0, QSTAGE>, *bs = q_stage<QSTAGES, QSTAGE>;
         for (int q = tid; q < QBM * QBK / 16; q += QNW * 64) {
             const int r = q >> 2, c = q & 3;
             const int gm = m0 + r, gk = k0 + 16 * c;
@@ -352,7 +393,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             *reinterpret_cast<u32x4 *>(as + r * QBK + ((c ^ qswz_a(r)) << 4)) = v;
         }
         for (int q = tid; q < QBK * QBN / 16; q += QNW * 64) {
-            const int r = q >> 4, c = q & 15;
+            const int r = q / Sh::BCPR, c = q % Sh::BCPR;
             const int gk = k0 + r, gn = n0 + 16 * c;
             u32x4 v = u32x4{0, 0, 0, 0};
             if (gk < K) {
@@ -366,7 +407,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                     v = u32x4{w[0], w[1], w[2], w[3]};
                 }
             }
-            *reinterpret_cast<u32x4 *>(bs + r * QBN + ((c ^ qswz_b(r)) << 4)) = v;
+            *reinterpret_cast<u32x4 *>(bs + r * QBN + ((c ^ qswz_b<QBN>(r)) << 4)) = v;
         }
         q_scale<0>[64 * wave + lane] = sc_src[(int64_t)(ktiles - 1) * sc_step];
         q_unroll<QSTAGES - 1>([&](auto S) {
@@ -380,9 +421,9 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     }
     q_barrier();
 #pragma unroll
-    for (int i = 0; i < QFM; ++i) read_a(q_stage<0>, i);
+    for (int i = 0; i < QFM; ++i) read_a(q_stage<0, QSTAGE>, i);
 #pragma unroll
-    for (int j = 0; j < QFN; ++j) read_b(q_stage<QSTAGES>, j);
+    for (int j = 0; j < QFN; ++j) read_b(q_stage<QSTAGES, QSTAGE>, j);
     read_scales(q_scale<0>);
     part[(NT - 1) & 1] = f32x16{};
     // Whole turns of the ring without conditions (a step skipped at run time
@@ -406,7 +447,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // half with bit 3 of the row), then out as whole 128-byte row segments.
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
     q_barrier();
-    uint16_t *st = reinterpret_cast<uint16_t *>(q_ring(wave));
+    uint16_t *st = reinterpret_cast<uint16_t *>(q_ring<QSTAGE>(wave));
     // EPI: the bias of this lane's columns, loaded once for all its rows.
     [[maybe_unused]] float ebias[EPI ? QFN : 1][4][4];
     if constexpr (EPI) {
@@ -484,13 +525,15 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
 }  // namespace
 
-bool fp8_fast_eligible(const Problem &p)
+static bool fp8_whole(const Problem &p, int tb)
 {
-    return p.M % QBM == 0 && p.N % QBN == 0 && p.K % (QBK * QSTAGES) == 0 &&
+    return p.M % tb == 0 && p.N % tb == 0 && p.K % (QBK * QSTAGES) == 0 &&
            ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 &&
            ((uintptr_t)p.C & 15) == 0 && p.lda % 16 == 0 && p.ldb % 16 == 0 && p.ldc % 8 == 0 &&
            p.lda < (1 << 23) && p.ldb < (1 << 24);
 }
+bool fp8_fast_eligible(const Problem &p) { return fp8_whole(p, 256); }
+bool fp8_fast128_eligible(const Problem &p) { return fp8_whole(p, 128); }
 
 // The guarded instantiation: any M, N >= 16 (a clamped column chunk starts at
 // N - 16), two K blocks at least, and per-lane 32-bit byte offsets that fit (256
@@ -501,10 +544,10 @@ bool fp8_general_eligible(const Problem &p)
            (int64_t)QBK * p.ldb + p.N < ((int64_t)1 << 31);
 }
 
-template <bool GEN>
+template <bool GEN, int TB>
 static hipError_t fp8_fast_typed(const Problem &p, const float *scale_a, const float *scale_b)
 {
-    const int tiles_m = (p.M + QBM - 1) / QBM, tiles_n = (p.N + QBN - 1) / QBN;
+    const int tiles_m = (p.M + TB - 1) / TB, tiles_n = (p.N + TB - 1) / TB;
     const int64_t nwg = (int64_t)tiles_m * tiles_n;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
@@ -513,11 +556,11 @@ static hipError_t fp8_fast_typed(const Problem &p, const float *scale_a, const f
     const int mblocks = (p.M + 63) / 64, kblocks = (p.K + 63) / 64, nblocks = (p.N + 63) / 64;
     const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (p.epi)
-        hipLaunchKernelGGL((fp8_fast_kernel<GEN, true>), dim3((unsigned)nwg), dim3(QNW * 64), 0,
+        hipLaunchKernelGGL((fp8_fast_kernel<GEN, true, TB>), dim3((unsigned)nwg), dim3(QNW * 64), 0,
                            p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b,
                            mblocks, kblocks, nblocks, tiles_m, tiles_n, group_m, epi);
     else
-        hipLaunchKernelGGL((fp8_fast_kernel<GEN, false>), dim3((unsigned)nwg), dim3(QNW * 64), 0,
+        hipLaunchKernelGGL((fp8_fast_kernel<GEN, false, TB>), dim3((unsigned)nwg), dim3(QNW * 64), 0,
                            p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, scale_a, scale_b,
                            mblocks, kblocks, nblocks, tiles_m, tiles_n, group_m, epi);
     return hipGetLastError();
@@ -526,13 +569,23 @@ static hipError_t fp8_fast_typed(const Problem &p, const float *scale_a, const f
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b)
 {
     if (!fp8_fast_eligible(p)) return hipErrorInvalidValue;
-    return fp8_fast_typed<false>(p, scale_a, scale_b);
+    return fp8_fast_typed<false, 256>(p, scale_a, scale_b);
 }
 
 hipError_t fp8_general_launch(const Problem &p, const float *scale_a, const float *scale_b)
 {
     if (!fp8_general_eligible(p)) return hipErrorInvalidValue;
-    return fp8_fast_typed<true>(p, scale_a, scale_b);
+    return fp8_fast_typed<true, 256>(p, scale_a, scale_b);
+}
+
+// 128 x 128 tiles (whole where eligible, else guarded).
+hipError_t fp8_tiles128_launch(const Problem &p, const float *scale_a, const float *scale_b,
+                               bool force_general)
+{
+    if (!force_general && fp8_fast128_eligible(p))
+        return fp8_fast_typed<false, 128>(p, scale_a, scale_b);
+    if (!fp8_general_eligible(p)) return hipErrorInvalidValue;
+    return fp8_fast_typed<true, 128>(p, scale_a, scale_b);
 }
 
 }  // namespace gemm

@@ -94,6 +94,9 @@ bool fp8_fast_eligible(const Problem &p);
 hipError_t fp8_fast_launch(const Problem &p, const float *scale_a, const float *scale_b);
 bool fp8_general_eligible(const Problem &p);
 hipError_t fp8_general_launch(const Problem &p, const float *scale_a, const float *scale_b);
+bool fp8_fast128_eligible(const Problem &p);
+hipError_t fp8_tiles128_launch(const Problem &p, const float *scale_a, const float *scale_b,
+                               bool force_general);
 // One quantiser call after argument checking: rows, cols >= 1, block 32 or 64,
 // fmt 0 (E4M3) or 1 (E5M2).
 struct QuantProblem {

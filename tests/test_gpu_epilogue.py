@@ -150,6 +150,8 @@ FP8_PATHS = {   # override, shape, leading dimensions, seed
     "guarded": ("2", (300, 270, 200), dict(lda=203, ldb=275, ldc=277, offset=1), 63),
     "ksplit32": ("3", (96, 192, 320), {}, 64),
     "ksplit64_guarded": ("6", (130, 70, 200), dict(lda=203, ldb=75, ldc=77, offset=1), 65),
+    "tiles128": ("8", (256, 384, 512), {}, 66),
+    "tiles128_guarded": ("9", (300, 270, 200), dict(lda=203, ldb=275, ldc=277, offset=1), 67),
 }
 
 

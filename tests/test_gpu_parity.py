@@ -258,6 +258,40 @@ def test_fp8_ksplit_permutation_exact(force):
     assert bad.size == 0, f"first mismatch at {bad[0]}"
 
 
+@pytest.mark.parametrize("force,shape,lds", [
+    ("8", (128, 128, 256), None),             # one 128 x 128 tile, one turn of the ring
+    ("8", (384, 256, 512), None),             # 6 tiles, two turns
+    ("8", (640, 896, 1024), None),            # 35 tiles
+    ("9", (129, 130, 129), None),             # a row and two columns past a tile, partial K block
+    ("9", (300, 520, 333), (337, 521, 525)),  # unaligned leading dimensions, offset pointers
+    ("9", (1000, 1000, 1000), None),          # the 1000^3 shape
+])
+def test_fp8_tiles128_path(force, shape, lds):
+    """128 x 128 tiles of the large-tile fp8 kernel (testing overrides '8': whole
+    tiles, '9': guarded): 8 waves of 32 x 64, B rows of 128 bytes."""
+    os.environ["LIBGEMM_FP8_SMALL"] = force
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[fp8-tiles128 {force}] {M}x{N}x{K} {kw}")
+    ops = gi.operands("fp8", M, N, K, 54)
+    _, got = run_gemm("fp8", ops, M, N, K, **kw)
+    ok, msg, _ = compare("fp8", got, reference("fp8", ops, M, N, K), "fp8-tiles128")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("force", ["8", "9"])
+def test_fp8_tiles128_permutation_exact(force):
+    M, K = 384, 512
+    os.environ["LIBGEMM_FP8_SMALL"] = force
+    say(f"[probe] fp8 128x128 tiles {force} A*P")
+    ops, perm = _perm_case("fp8", M, K, 20)
+    _, got = run_gemm("fp8", ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], "fp8")
+    bad = np.argwhere(oracle.decode(got, "bf16") != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
 def test_fp8_guarded_permutation_exact():
     M, K = 300, 320
     os.environ["LIBGEMM_FP8_SMALL"] = "2"
