@@ -8,7 +8,8 @@ oracle, entry by entry, on seeded inputs.
   launch configuration the benchmark times;
 * every half-precision tile configuration forced on ragged shapes, with
   aligned and unaligned leading dimensions and offset pointers;
-* random small shapes, K = 0, degenerate sizes, and a guard band around C.
+* random small and medium shapes through the automatic dispatch, K = 0,
+  degenerate sizes, and a guard band around C.
 """
 import os
 
@@ -716,6 +717,31 @@ def test_fuzz_small_shapes(dtype):
         _, got = run_gemm(dtype, ops, M, N, K, **kw)
         ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), f"fuzz {M}x{N}x{K}")
         assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "fp8"])
+def test_fuzz_medium_shapes(dtype):
+    """Random medium shapes through the automatic dispatch (the range where it
+    picks between the K-split, 128 x 128, 128 x 256, 256 x 256 and register-staged
+    kernels), every entry against the oracle; odd cases with padded leading
+    dimensions and an offset pointer, whose padding must stay unwritten."""
+    rng = np.random.default_rng({"f16": 11, "bf16": 12, "f32": 13, "fp8": 14}[dtype])
+    for case in range(8):
+        M, N = (int(x) for x in rng.integers(64, 2601, 2))
+        K = int(rng.integers(32, 3001))
+        kw = {}
+        if case % 2:
+            kw = dict(lda=K + int(rng.integers(1, 9)), ldb=N + int(rng.integers(1, 9)),
+                      ldc=N + int(rng.integers(1, 9)), offset=int(rng.integers(1, 4)))
+        say(f"[fuzz-medium] {dtype} case {case}: {M}x{N}x{K} {kw}")
+        ops = gi.operands(dtype, M, N, K, 200 + case)
+        C, got = run_gemm(dtype, ops, M, N, K, **kw)
+        ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), f"fuzz {M}x{N}x{K}")
+        assert ok, msg
+        if "ldc" in kw:
+            pad = kw["ldc"] - N
+            band = C.as_strided((M, pad), (kw["ldc"], 1), C.storage_offset() + N).float().cpu()
+            assert torch.isnan(band).all(), "padding between N and ldc was written"
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "fp8"])
