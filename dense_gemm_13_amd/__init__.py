@@ -125,20 +125,44 @@ def _torch():
 
 
 def _ld(t) -> int:
-    """Leading dimension of a 2-D row-major tensor (row stride in elements)."""
+    """Leading dimension of a 2-D row-major tensor (row stride in elements).
+
+    Rows must not overlap: a row stride below the row length (a broadcast row,
+    stride 0, or any other overlapping view) is rejected, since the kernels
+    address row i at i * ld and would read or write past the tensor.
+    """
     if t.dim() != 2:
         raise ValueError(f"expected a 2-D tensor, got {t.dim()}-D")
     if t.numel() == 0:          # no elements: strides are meaningless
         return max(t.size(1), 1)
     if t.size(1) > 1 and t.stride(1) != 1:
         raise ValueError("tensor must have unit column stride (row-major)")
-    return max(t.stride(0), t.size(1), 1) if t.size(0) > 1 else max(t.size(1), 1)
+    if t.size(0) > 1 and t.stride(0) < t.size(1):
+        raise ValueError(f"tensor rows overlap (row stride {t.stride(0)} < row length "
+                         f"{t.size(1)}); pass a tensor with distinct rows, e.g. .contiguous()")
+    return max(t.stride(0), 1) if t.size(0) > 1 else max(t.size(1), 1)
+
+
+def _on_device(name, device, **tensors):
+    """Every tensor handed to the library must live in GPU memory on `device`
+    (the device of the first operand): the kernels dereference data_ptr() on
+    that GPU, so a host tensor or one on another GPU would be read as a wild
+    device address.  None entries are optional arguments that were not given."""
+    for nm, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name}: {nm} must be a GPU tensor (got one on {t.device})")
+        if t.device != device:
+            raise ValueError(f"{name}: {nm} is on {t.device}, the operands on {device}")
 
 
 def _stream_handle(stream, device):
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream(device)
+    elif getattr(stream, "device", device) != device:
+        raise ValueError(f"stream belongs to {stream.device}, the operands to {device}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -156,10 +180,9 @@ def _epilogue_args(name, C, N, alpha, beta, bias, activation, device):
         raise ValueError(f"{name}: beta != 0 reads C, so C must be given")
     bptr = None
     if bias is not None:
-        if bias.dtype != torch.float32 or tuple(bias.shape) != (N,) or not bias.is_contiguous() \
-                or bias.device != device:
-            raise ValueError(f"{name}: bias must be a contiguous float32 vector of {N} values "
-                             "on C's device")
+        if bias.dtype != torch.float32 or tuple(bias.shape) != (N,) or not bias.is_contiguous():
+            raise ValueError(f"{name}: bias must be a contiguous float32 vector of {N} values")
+        _on_device(name, device, bias=bias)
         bptr = bias.data_ptr()
     return float(alpha), float(beta), bptr, ACTIVATIONS[activation]
 
@@ -179,8 +202,11 @@ def _h16(name, want_dtype, A, B, C, stream, epilogue=None):
         C = torch.empty((M, N), dtype=want_dtype, device=A.device)
     if C.dtype != want_dtype or tuple(C.shape) != (M, N):
         raise ValueError(f"{name}: C must be {want_dtype} of shape ({M}, {N})")
-    _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A), _ld(B),
-                              _ld(C), *extra, _stream_handle(stream, A.device)), name)
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
+    _on_device(name, A.device, A=A, B=B, C=C)
+    sh = _stream_handle(stream, A.device)
+    _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, lda, ldb, ldc,
+                              *extra, sh), name)
     return C
 
 
@@ -219,9 +245,11 @@ def _fp8(name, A, B, scale_a, scale_b, C, stream, epilogue=None):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, N):
         raise ValueError(f"{name}: C must be bfloat16 of shape ({M}, {N})")
-    _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A), _ld(B),
-                              _ld(C), scale_a.data_ptr(), scale_b.data_ptr(), *extra,
-                              _stream_handle(stream, A.device)), name)
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
+    _on_device(name, A.device, A=A, B=B, C=C, scale_a=scale_a, scale_b=scale_b)
+    sh = _stream_handle(stream, A.device)
+    _check(getattr(lib, name)(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, lda, ldb, ldc,
+                              scale_a.data_ptr(), scale_b.data_ptr(), *extra, sh), name)
     return C
 
 
@@ -286,9 +314,11 @@ def gemm_h16_ladder(rung, A, B, C=None, stream=None):
     LADDER_RUNGS or its number); float16 or bfloat16 operands."""
     r = LADDER_RUNGS[rung] if isinstance(rung, str) else int(rung)
     M, N, K, bf, C = _h16_pair("gemm_h16_ladder", A, B, C)
-    _check(lib.gemm_h16_ladder(r, bf, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, _ld(A),
-                               _ld(B), _ld(C), _stream_handle(stream, A.device)),
-           "gemm_h16_ladder")
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
+    _on_device("gemm_h16_ladder", A.device, A=A, B=B, C=C)
+    sh = _stream_handle(stream, A.device)
+    _check(lib.gemm_h16_ladder(r, bf, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, lda,
+                               ldb, ldc, sh), "gemm_h16_ladder")
     return C
 
 
@@ -296,9 +326,11 @@ def gemm_h16_mfma_ceiling(A, B, C=None, stream=None):
     """The large-tile kernel's MFMA sequence with register-held operands (no
     memory traffic); writes C = (K/32) * A[:, :32] @ B[:32, :]."""
     M, N, K, bf, C = _h16_pair("gemm_h16_mfma_ceiling", A, B, C)
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
+    _on_device("gemm_h16_mfma_ceiling", A.device, A=A, B=B, C=C)
+    sh = _stream_handle(stream, A.device)
     _check(lib.gemm_h16_mfma_ceiling(bf, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
-                                     _ld(A), _ld(B), _ld(C), _stream_handle(stream, A.device)),
-           "gemm_h16_mfma_ceiling")
+                                     lda, ldb, ldc, sh), "gemm_h16_mfma_ceiling")
     return C
 
 
@@ -357,11 +389,15 @@ def gemm_conv2d_nhwc(X, Wt, stride=1, padding=0, dilation=1, bias=None, activati
                          f"{(shape.n, ho, wo, shape.c_out)}")
     _, _, bptr, act = _epilogue_args("gemm_conv2d_nhwc", Y, shape.c_out, 1.0, 0.0, bias,
                                      activation, X.device)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("gemm_conv2d_nhwc: workspace must be contiguous")
+    _on_device("gemm_conv2d_nhwc", X.device, X=X, Wt=Wt, Y=Y, workspace=workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    sh = _stream_handle(stream, X.device)
     _check(lib.gemm_conv2d_nhwc(DTYPES[dt], X.data_ptr(), Wt.data_ptr(), Y.data_ptr(), ws_ptr,
-                                ws_bytes, ctypes.byref(shape), bptr, act,
-                                _stream_handle(stream, X.device)), "gemm_conv2d_nhwc")
+                                ws_bytes, ctypes.byref(shape), bptr, act, sh),
+           "gemm_conv2d_nhwc")
     return Y
 
 
@@ -380,9 +416,11 @@ def gemm_im2col_nhwc(X, kernel, stride=1, padding=0, dilation=1, col=None, strea
         col = torch.empty((rows, cols), dtype=X.dtype, device=X.device)
     if col.dtype != X.dtype or tuple(col.shape) != (rows, cols):
         raise ValueError(f"gemm_im2col_nhwc: col must be {X.dtype} of shape ({rows}, {cols})")
-    _check(lib.gemm_im2col_nhwc(DTYPES[dt], X.data_ptr(), col.data_ptr(), _ld(col),
-                                ctypes.byref(shape), _stream_handle(stream, X.device)),
-           "gemm_im2col_nhwc")
+    ldcol = _ld(col)
+    _on_device("gemm_im2col_nhwc", X.device, X=X, col=col)
+    sh = _stream_handle(stream, X.device)
+    _check(lib.gemm_im2col_nhwc(DTYPES[dt], X.data_ptr(), col.data_ptr(), ldcol,
+                                ctypes.byref(shape), sh), "gemm_im2col_nhwc")
     return col
 
 
@@ -412,9 +450,12 @@ def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
     if scales.dtype != torch.float32 or tuple(scales.shape) != shape or \
             not scales.is_contiguous():
         raise ValueError(f"gemm_quantize_fp8: scales must be contiguous float32 {shape}")
-    _check(lib.gemm_quantize_fp8(X.data_ptr(), QUANT_INPUTS[in_type], rows, cols, _ld(X), block,
-                                 FP8_FORMATS[fmt], Q.data_ptr(), _ld(Q), scales.data_ptr(),
-                                 _stream_handle(stream, X.device)), "gemm_quantize_fp8")
+    ldx, ldq = _ld(X), _ld(Q)
+    _on_device("gemm_quantize_fp8", X.device, X=X, Q=Q, scales=scales)
+    sh = _stream_handle(stream, X.device)
+    _check(lib.gemm_quantize_fp8(X.data_ptr(), QUANT_INPUTS[in_type], rows, cols, ldx, block,
+                                 FP8_FORMATS[fmt], Q.data_ptr(), ldq, scales.data_ptr(), sh),
+           "gemm_quantize_fp8")
     return Q, scales
 
 

@@ -83,7 +83,10 @@ int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t esize)
     return ((rows - 1) * ld + cols) * esize;
 }
 
-constexpr int64_t DIM_LIMIT = 0x7fffffff;
+// Largest M, N or K: 2^31 - 2^16.  Kernels round a dimension up to whole tiles
+// or K blocks (at most 1024 past it) in 32-bit arithmetic; the headroom keeps
+// every such index below 2^31.
+constexpr int64_t DIM_LIMIT = 0x7fff0000;
 
 // Checks shared by all dtypes.  On success returns GEMM_OK and, when there is
 // work to do, leaves *work = true.

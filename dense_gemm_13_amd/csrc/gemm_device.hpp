@@ -56,6 +56,19 @@ __host__ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles
     tn = in_g / rows;
 }
 
+// ----------------------------------------------------------- strided K walks
+//
+// Element index of lane offset r in group g of a walk over `ngroups` groups of
+// `per` consecutive elements, or `limit` (one past the last element, read as
+// zero by the caller) when g lies past the last group.  The group index is
+// compared before it is multiplied, so a wave that steps past the end never
+// forms g * per: with ngroups = ceil(limit / per), every index formed is below
+// limit + per, which stays in 32-bit range for limit <= 2^31 - 2^16.
+__host__ __device__ __forceinline__ int group_elem(int g, int ngroups, int per, int r, int limit)
+{
+    return g < ngroups ? g * per + r : limit;
+}
+
 // ------------------------------------------------------------ output rounding
 
 // Round to nearest, ties to even (hardware conversions on gfx950).

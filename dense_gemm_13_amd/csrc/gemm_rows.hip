@@ -117,7 +117,7 @@ rows_kernel(const void *__restrict__ Av, const void *__restrict__ Bv, void *__re
         float av[RUNROLL][MR];
 #pragma unroll
         for (int u = 0; u < RUNROLL; ++u) {
-            const int k = (g0 + RWAVES * u) * RPL + r;
+            const int k = group_elem(g0 + RWAVES * u, ngroups, RPL, r, K);
             bv[u] = b_at(k);
 #pragma unroll
             for (int m = 0; m < MR; ++m) av[u][m] = a_at(m, k);

@@ -17,7 +17,8 @@
  *   - A, B, C (and the fp8 scales) are DEVICE pointers owned by the caller, on the
  *     current HIP device; the library never allocates, frees or synchronises, keeps
  *     no state between calls and may be called from several host threads.
- *   - M, N, K >= 0; lda >= K, ldb >= N, ldc >= N (elements, not bytes).
+ *   - 0 <= M, N, K <= 2^31 - 2^16 (else GEMM_ERR_DIM); lda >= K, ldb >= N,
+ *     ldc >= N (elements, not bytes).
  *   - Pointers must be aligned to their element size and non-NULL whenever the
  *     region they describe is non-empty.  C must not overlap A, B or the scales.
  *   - M == 0 or N == 0: nothing to do, returns GEMM_OK without a launch.
@@ -211,7 +212,8 @@ int gemm_h16_mfma_ceiling(int is_bf16, const void *A, const void *B, void *C, in
  * with ho = floor((h + 2 pad_h - dil_h (kh - 1) - 1) / stride_h) + 1 and wo
  * likewise (0 when the dilated kernel does not fit).  kh, kw, strides and
  * dilations >= 1; paddings >= 0 (zeros); h, w, kh, kw, strides, paddings and
- * dilations at most 32768; n*ho*wo and kh*kw*c_in at most 2^31 - 1. */
+ * dilations at most 32768; n, c_in, c_out, n*ho*wo and kh*kw*c_in at most
+ * 2^31 - 2^16. */
 typedef struct gemm_conv2d_shape {
     int64_t n, h, w, c_in, c_out, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
 } gemm_conv2d_shape;

@@ -81,6 +81,12 @@ def test_argument_errors(name):
     assert h16(fn, M=-1) == -2
     assert h16(fn, K=-5) == -2
     assert h16(fn, N=1 << 31) == -2
+    # the largest dimension is 2^31 - 2^16: one more is refused before anything
+    # else is looked at (kernels round dimensions up in 32-bit arithmetic)
+    lim = (1 << 31) - (1 << 16)
+    assert h16(fn, K=lim + 1, lda=lim + 1) == -2
+    assert h16(fn, M=lim + 1) == -2
+    assert h16(fn, N=lim + 1, ldb=lim + 1, ldc=lim + 1) == -2
     assert h16(fn, lda=63) == -3
     assert h16(fn, ldb=63) == -3
     assert h16(fn, ldc=10) == -3

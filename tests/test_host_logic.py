@@ -68,6 +68,26 @@ int main() {
       for (int r = 0; r < 8; ++r) m |= 1 << (((base + r) & 1) * 4 + (c ^ swz4(base + r)));
       if (m != 255) { printf("swz4 %d %d\n", base, c); return 1; }
     }
+  // strided K walks (the few-row kernel): 16 waves, 7 groups each per round, up
+  // to 8 rows per group; for K up to the library's limit 2^31 - 2^16 every
+  // index formed stays below 2^31 and indexes past the last group read as K
+  {
+    const long long lim = (1LL << 31) - (1LL << 16);
+    const int Ks[] = {1, 7, 8, 9, 1000, 4100, (int)lim - 1, (int)lim};
+    for (int K : Ks)
+      for (int per : {4, 8}) {
+        const int ngroups = (int)(((long long)K + per - 1) / per);
+        const int first = ngroups > 200 ? ngroups - 200 : 0;
+        for (int g0 = first; g0 < ngroups; ++g0)
+          for (int u = 0; u < 7; ++u)
+            for (int r = 0; r < per; ++r) {
+              const long long g = (long long)g0 + 16LL * u;
+              const int k = group_elem(g0 + 16 * u, ngroups, per, r, K);
+              const long long want = g < ngroups ? g * per + r : K;
+              if (k != want || k < 0) { printf("group_elem K=%d g=%lld r=%d: %d\n", K, g, r, k); return 1; }
+            }
+      }
+  }
   printf("OK\n");
   return 0;
 }
