@@ -89,10 +89,29 @@ def measured_traffic(name: str):
         return None
 
 
+_FLUSH = {}
+
+
+def flush_buffer(device):
+    """A 512 MiB device buffer, written once (twice the Infinity Cache)."""
+    import torch
+    if device not in _FLUSH:
+        _FLUSH[device] = torch.ones((512 << 20) // 4, dtype=torch.int32, device=device)
+    return _FLUSH[device]
+
+
+def flush_read(buf):
+    """Read every byte of `buf` (a reduction kernel; nothing is written back)."""
+    return buf.sum()
+
+
 class Workload:
-    def __init__(self, key, name, dtype, M, N, K, wid):
+    sustain = 0          # launches of the sustained pass (0: none)
+
+    def __init__(self, key, name, dtype, M, N, K, wid, sustain=0):
         self.key, self.name, self.dtype = key, name, dtype
         self.M, self.N, self.K, self.wid = M, N, K, wid
+        self.sustain = sustain
 
     def setup(self):
         import numpy as np
@@ -132,21 +151,36 @@ class Workload:
 
     def cold(self, steps: int) -> float:
         """Mean launch time with L2 and the Infinity Cache flushed before each
-        launch by a 512 MiB write (the operands of every workload fit in the
-        256 MiB Infinity Cache otherwise)."""
+        launch (the operands of every workload fit in the 256 MiB Infinity Cache
+        otherwise).  The flush READS a 512 MiB buffer that was written once at
+        allocation: the lines it leaves in the caches are clean, and whatever the
+        previous launch left dirty is written back during the flush, so the timed
+        launch pays for its own HBM traffic only."""
         import torch
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=self.C.device)
+        flush = flush_buffer(self.C.device)
         evs = []
         for _ in range(steps):
-            flush.fill_(1)
+            flush_read(flush)
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record(self.stream)
             self.call()
             e.record(self.stream)
             evs.append((s, e))
         torch.cuda.synchronize()
-        del flush
         return sum(s.elapsed_time(e) for s, e in evs) / steps * 1e-3
+
+    def sustained(self, launches: int) -> float:
+        """Mean launch time over `launches` back-to-back launches in one region:
+        long enough (hundreds of launches, tens of milliseconds) for the chip's
+        power controller to settle at the clock it holds under this load."""
+        import torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(launches):
+            self.call()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / launches
 
     def run(self, steps: int, warmup: int, cold_steps: int) -> dict:
         """Timed region: `steps` back-to-back launches on one stream between two
@@ -179,7 +213,14 @@ class Workload:
         per = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
         median = per[len(per) // 2]
         cold = self.cold(cold_steps) if cold_steps > 0 else None
-        return self.report(region, wall, mean, median, cold)
+        r = self.report(region, wall, mean, median, cold)
+        if self.sustain:
+            t = self.sustained(self.sustain)
+            r["sustained_launches"] = self.sustain
+            r["sustained_mean_launch_us"] = t * 1e6
+            if self.K:
+                r["sustained_tflops"] = tflops(self.M, self.N, self.K, t)
+        return r
 
     def report(self, region, wall, mean, median, cold) -> dict:
         M, N, K, dt = self.M, self.N, self.K, self.dtype
@@ -192,6 +233,9 @@ class Workload:
             "alg_gbs": algorithmic_bytes(dt, M, N, K) / mean / 1e9,
             "cold_mean_launch_us": cold * 1e6 if cold else None,
             "cold_tflops": tflops(M, N, K, cold) if cold else None,
+            "cold_alg_gbs": algorithmic_bytes(dt, M, N, K) / cold / 1e9 if cold else None,
+            "cold_pct_hbm_peak": 100.0 * algorithmic_bytes(dt, M, N, K) / cold / 1e9
+                                 / HBM_PEAK_GBS if cold else None,
         }
 
     def summary(self, r) -> str:
@@ -239,6 +283,8 @@ class QuantWorkload(Workload):
             "alg_gbs": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
             "cold_mean_launch_us": cold * 1e6 if cold else None,
             "cold_alg_gbs": self.alg_bytes() / cold / 1e9 if cold else None,
+            "cold_pct_hbm_peak": 100.0 * self.alg_bytes() / cold / 1e9 / HBM_PEAK_GBS
+                                 if cold else None,
         }
 
     def summary(self, r) -> str:
@@ -337,10 +383,16 @@ class ConvWorkload(Workload):
         if self.pack_only:
             r["alg_gbs"] = pack_bytes / mean / 1e9
             r["pct_hbm_peak"] = 100.0 * r["alg_gbs"] / HBM_PEAK_GBS
+            if cold:
+                r["cold_alg_gbs"] = pack_bytes / cold / 1e9
+                r["cold_pct_hbm_peak"] = 100.0 * r["cold_alg_gbs"] / HBM_PEAK_GBS
             for k in ("tflops", "pct_peak", "cold_tflops"):
                 r.pop(k, None)
         else:
-            r["alg_gbs"] = (2 * n * hw * hw * (ci + co) + 2 * 9 * ci * co + 4 * co) / mean / 1e9
+            conv_bytes = 2 * n * hw * hw * (ci + co) + 2 * 9 * ci * co + 4 * co
+            r["alg_gbs"] = conv_bytes / mean / 1e9
+            r.pop("cold_pct_hbm_peak", None)
+            r["cold_alg_gbs"] = conv_bytes / cold / 1e9 if cold else None
         return r
 
     def summary(self, r) -> str:
@@ -387,8 +439,8 @@ class EpilogueWorkload(Workload):
 
 
 WORKLOADS = [
-    Workload("bf16_4096", "bf16 GEMM M=N=K=4096", "bf16", 4096, 4096, 4096, 2),
-    Workload("f16_4096", "fp16 GEMM M=N=K=4096", "f16", 4096, 4096, 4096, 2),
+    Workload("bf16_4096", "bf16 GEMM M=N=K=4096", "bf16", 4096, 4096, 4096, 2, sustain=300),
+    Workload("f16_4096", "fp16 GEMM M=N=K=4096", "f16", 4096, 4096, 4096, 2, sustain=300),
     Workload("f16_256", "fp16 GEMM M=N=K=256", "f16", 256, 256, 256, 1),
     Workload("bf16_1000", "bf16 GEMM 1000x1000x1000", "bf16", 1000, 1000, 1000, 3),
     Workload("bf16_ragged", "bf16 GEMM 4097x4095x4100", "bf16", 4097, 4095, 4100, 3),
@@ -421,20 +473,78 @@ WORKLOADS = [
 ]
 
 
-def cpu_baseline(headline: Workload) -> dict:
-    """The CPU oracle, as it stands, on the first rows of the headline product."""
+# Oracle timings: (key, dtype, M, N, K, workload id, rows timed (None: all),
+# threads (None: the host's CPU share)).  The workloads are the five configured
+# ones at their full shapes; large products are timed on their first rows (the
+# oracle's rows are independent and cost the same each, so the rate carries
+# over).  Two single-core runs give the per-core rate on the small shapes.
+ORACLE_CASES = (
+    ("f16_256", "f16", 256, 256, 256, 1, None, None),
+    ("bf16_4096", "bf16", 4096, 4096, 4096, 2, 2048, None),
+    ("f16_4096", "f16", 4096, 4096, 4096, 2, 2048, None),
+    ("bf16_1000", "bf16", 1000, 1000, 1000, 3, None, None),
+    ("bf16_ragged", "bf16", 4097, 4095, 4100, 3, 1024, None),
+    ("bf16_skinny", "bf16", 8192, 64, 4096, 3, None, None),
+    ("f32_4096", "f32", 4096, 4096, 4096, 4, 1024, None),
+    ("fp8_8192", "fp8", 8192, 8192, 8192, 5, 256, None),
+    ("f16_256_1core", "f16", 256, 256, 256, 1, None, 1),
+    ("bf16_1000_1core", "bf16", 1000, 1000, 1000, 3, None, 1),
+)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cpu_share() -> int:
+    """Threads the oracle may use: the CPUs this process may run on, capped by
+    the share the host grants one GPU job when it states one (OMP_NUM_THREADS)."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(share)) if share.isdigit() and int(share) > 0 else n
+
+
+def cpu_baseline() -> dict:
+    """The CPU oracle, as it stands, timed on every configured workload (first
+    rows of the large ones) with the host's CPU share, plus two single-core
+    runs.  `value` is the rate on the headline workload."""
+    import gemm_inputs as gi
     import oracle
-    threads = min(16, os.cpu_count() or 1)
-    rows = 2048
-    A = headline.ops["A"][:rows]
-    t0 = time.perf_counter()
-    oracle.gemm(headline.dtype, A, headline.ops["B"], rows, headline.N, headline.K,
-                nthreads=threads)
-    t = time.perf_counter() - t0
-    return {"value": tflops(rows, headline.N, headline.K, t), "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {headline.M} rows of the {headline.name} product "
-                      f"(fp64, bit-exact decode included), {t:.2f} s wall"}
+    share = host_cpu_share()
+    cases, total = [], 0.0
+    for key, dt, M, N, K, wid, rows, threads in ORACLE_CASES:
+        nt = threads or share
+        ops = gi.operands(dt, M, N, K, wid)
+        r = rows or M
+        sa = ops.get("scale_a")
+        if sa is not None:
+            sa = sa[:-(-r // 64)]
+        t0 = time.perf_counter()
+        oracle.gemm(dt, ops["A"][:r], ops["B"], r, N, K, sa, ops.get("scale_b"), nthreads=nt)
+        t = time.perf_counter() - t0
+        total += t
+        rate = tflops(r, N, K, t)
+        cases.append({"workload": key, "dtype": dt, "M": M, "N": N, "K": K, "rows_timed": r,
+                      "threads": nt, "seconds": round(t, 3), "tflops": rate,
+                      "gflops": round(rate * 1e3, 2),
+                      "full_product_s_est": round(2.0 * M * N * K / (rate * 1e12), 2)})
+        print(f"[bench] oracle {key}: {r} of {M} rows, {nt} threads, {t:.2f} s, "
+              f"{rate * 1e3:.1f} GFLOP/s", file=sys.stderr, flush=True)
+    head = next(c for c in cases if c["workload"] == "bf16_4096")
+    return {"value": head["tflops"], "unit": "TFLOP/s", "cores": head["threads"],
+            "kind": "oracle",
+            "sample": f"first {head['rows_timed']} of 4096 rows of the bf16 M=N=K=4096 product "
+                      f"(fp64, bit-exact decode included), {head['seconds']:.2f} s wall; every "
+                      f"configured workload timed the same way under 'per_workload' "
+                      f"({total:.1f} s in all)",
+            "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count(),
+            "threads_used": share, "per_workload": cases}
 
 
 def main():
@@ -525,6 +635,13 @@ def main():
             "frac": round(flops / (h["mean_launch_us"] * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"], 4),
             "traffic": measured_traffic("bf16_4096"),
         },
+        # the same launches repeated 300 times back to back in one region, after
+        # the timed steps: the rate once the power controller has settled
+        "sustained": None if "sustained_tflops" not in h else {
+            "launches": h["sustained_launches"],
+            "mean_launch_us": round(h["sustained_mean_launch_us"], 2),
+            "tflops": round(h["sustained_tflops"], 2),
+            "frac_of_peak": round(h["sustained_tflops"] / PEAK_TFLOPS["bf16"], 4)},
         "kernel_source_digest": kernel_source_digest(),
         # the same MFMA instruction sequence with register-held operands and no
         # memory traffic: what the matrix cores sustain on these operand values
@@ -537,7 +654,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(headline)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 

@@ -4,8 +4,8 @@ oracle, entry by entry, on seeded inputs.
 * exact probes: permutation matrices and all-ones inputs give results that are
   exactly representable, so they must match bit for bit (this pins the MFMA
   operand/accumulator layouts, LDS swizzles, tile remap and epilogue);
-* the five workloads at full size (fp8 8192^3 on sampled entries), in the
-  launch configuration the benchmark times;
+* the five workloads at full size, every entry, in the launch configuration
+  the benchmark times;
 * every half-precision tile configuration forced on ragged shapes, with
   aligned and unaligned leading dimensions and offset pointers;
 * random small and medium shapes through the automatic dispatch, K = 0,
@@ -140,7 +140,14 @@ def test_workload_f32_4096():
     _full_check("f32", 4096, 4096, 4096, 4, "f32_4096")
 
 
-def test_workload_fp8_8192_sampled():
+@pytest.mark.timeout(900)
+def test_workload_fp8_8192_every_entry():
+    """The fp8 workload (E4M3, 64x64 block scales, M = N = K = 8192, bf16 C) in
+    the launch configuration the benchmark times, checked on all 67,108,864
+    entries against the oracle.  A sampled pre-check (random entries, whole
+    rows and columns, tile and scale-block edges) runs first so that a layout
+    mistake fails fast with a pointed message; then the oracle forms the whole
+    product in row blocks of 1024 on the host's cores."""
     M = N = K = 8192
     say("[fp8_8192] generating")
     ops = gi.operands("fp8", M, N, K, 5)
@@ -157,12 +164,29 @@ def test_workload_fp8_8192_sampled():
     rr, cc = np.meshgrid(edges, edges)
     rows.append(rr.ravel()); cols.append(cc.ravel())
     rows, cols = np.concatenate(rows), np.concatenate(cols)
-    say(f"[fp8_8192] oracle on {rows.size} entries")
+    say(f"[fp8_8192] sampled pre-check: oracle on {rows.size} entries")
     ref = oracle.gemm_entries("fp8", ops["A"], ops["B"], M, N, K, rows, cols,
                               ops["scale_a"], ops["scale_b"])
     ok, msg, _ = compare("fp8", got[rows, cols], ref, "fp8_8192 sampled")
     say(msg)
     assert ok, msg
+    threads = min(16, len(os.sched_getaffinity(0)))
+    rtol, atol = TOL["fp8"]
+    nfail, worst, worst_at = 0, 0.0, None
+    for r0 in range(0, M, 1024):
+        say(f"[fp8_8192] oracle rows {r0}..{r0 + 1023} on {threads} threads")
+        sa = ops["scale_a"][r0 // 64:(r0 + 1024) // 64]
+        ref = oracle.gemm("fp8", ops["A"][r0:r0 + 1024], ops["B"], 1024, N, K, sa,
+                          ops["scale_b"], nthreads=threads)
+        blk_ok, blk_fail, blk_worst, idx = oracle.within_tolerance(
+            oracle.decode(got[r0:r0 + 1024], "bf16"), ref, rtol, atol)
+        nfail += blk_fail
+        if blk_worst > worst:
+            worst, worst_at = blk_worst, (idx[0] + r0, idx[1]) if idx is not None else None
+    msg = (f"fp8_8192 every entry: {nfail} of {M * N} entries outside "
+           f"|d| <= {rtol}|ref|+{atol}; worst err/tol {worst:.3g} at {worst_at}")
+    say(msg)
+    assert nfail == 0, msg
 
 
 @pytest.mark.parametrize("shape", [(1000, 900, 700), (512, 512, 512), (130, 70, 200)])
