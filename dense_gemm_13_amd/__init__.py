@@ -16,6 +16,8 @@ Entry points (same names as the C ABI in include/libgemm.h):
         bias=None, activation="none", stream=None)
     gemm_conv2d_nhwc(X, Wt, stride=1, padding=0, dilation=1, bias=None, activation="none",
         Y=None, workspace=None, stream=None)   (NHWC input, HWIO weights: im2col + GEMM)
+    gemm_conv2d_nhwc_noalloc(X, Wt, Y, stride=1, padding=0, dilation=1, bias=None,
+        activation="none", stream=None)        (the same, allocating nothing)
     gemm_im2col_nhwc(X, kernel, stride=1, padding=0, dilation=1, col=None, stream=None)
     gemm_h16_ladder(rung, A, B, C=None, stream=None)      (measurement only)
     gemm_h16_mfma_ceiling(A, B, C=None, stream=None)      (measurement only)
@@ -39,12 +41,17 @@ LIB_PATH = os.path.join(_HERE, "libgemm.so")
 GEMM_OK = 0
 STATUS_NAMES = {0: "GEMM_OK", -1: "GEMM_ERR_NULL", -2: "GEMM_ERR_DIM", -3: "GEMM_ERR_LD",
                 -4: "GEMM_ERR_ALIGN", -5: "GEMM_ERR_ALIAS", -6: "GEMM_ERR_DEVICE",
-                -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG", -9: "GEMM_ERR_WORKSPACE"}
+                -7: "GEMM_ERR_LAUNCH", -8: "GEMM_ERR_ARG", -9: "GEMM_ERR_WORKSPACE",
+                -10: "GEMM_ERR_SCRATCH"}
 ENTRY_POINTS = ("gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled",
                 "gemm_f16_epilogue", "gemm_bf16_epilogue", "gemm_f32_epilogue",
                 "gemm_fp8_blockscaled_epilogue", "gemm_quantize_fp8", "gemm_h16_ladder",
-                "gemm_h16_mfma_ceiling", "gemm_conv2d_nhwc", "gemm_conv2d_workspace_bytes",
-                "gemm_im2col_nhwc", "gemm_status_string", "gemm_version")
+                "gemm_h16_mfma_ceiling", "gemm_conv2d_nhwc", "gemm_conv2d_nhwc_noalloc",
+                "gemm_conv2d_workspace_bytes", "gemm_im2col_nhwc", "gemm_status_string",
+                "gemm_version")
+# Bytes of the per-GPU device array gemm_conv2d_nhwc_noalloc builds its im2col
+# matrix in (GEMM_CONV2D_SCRATCH_BYTES).
+CONV2D_SCRATCH_BYTES = 64 << 20
 DTYPES = {"f16": 0, "bf16": 1, "f32": 2}      # enum gemm_dtype
 
 
@@ -101,6 +108,8 @@ def _load():
     sp = ctypes.POINTER(Conv2dShape)
     h.gemm_conv2d_nhwc.argtypes = [ci, vp, vp, vp, vp, i64, sp, vp, ci, vp]
     h.gemm_conv2d_nhwc.restype = ctypes.c_int
+    h.gemm_conv2d_nhwc_noalloc.argtypes = [ci, vp, vp, vp, sp, vp, ci, vp]
+    h.gemm_conv2d_nhwc_noalloc.restype = ctypes.c_int
     h.gemm_conv2d_workspace_bytes.argtypes = [ci, sp]
     h.gemm_conv2d_workspace_bytes.restype = ctypes.c_int64
     h.gemm_im2col_nhwc.argtypes = [ci, vp, vp, i64, sp, vp]
@@ -401,6 +410,29 @@ def gemm_conv2d_nhwc(X, Wt, stride=1, padding=0, dilation=1, bias=None, activati
     return Y
 
 
+def gemm_conv2d_nhwc_noalloc(X, Wt, Y, stride=1, padding=0, dilation=1, bias=None,
+                             activation="none", stream=None):
+    """gemm_conv2d_nhwc for callers that cannot allocate: the im2col matrix is
+    built in the library's fixed per-GPU scratch array (CONV2D_SCRATCH_BYTES)
+    and Y must be given, so neither the library nor this call allocates device
+    memory.  Calls whose matrix does not fit raise GemmError (GEMM_ERR_SCRATCH).
+    Calls on one GPU share the array: issue them on one stream."""
+    dt = _conv_dtype("gemm_conv2d_nhwc_noalloc", X, Wt, Y)
+    shape = conv2d_shape(X, Wt, stride, padding, dilation)
+    ho, wo = conv2d_output_hw(shape)
+    if tuple(Y.shape) != (shape.n, ho, wo, shape.c_out):
+        raise ValueError(f"gemm_conv2d_nhwc_noalloc: Y must be contiguous {X.dtype} "
+                         f"{(shape.n, ho, wo, shape.c_out)}")
+    _, _, bptr, act = _epilogue_args("gemm_conv2d_nhwc_noalloc", Y, shape.c_out, 1.0, 0.0, bias,
+                                     activation, X.device)
+    _on_device("gemm_conv2d_nhwc_noalloc", X.device, X=X, Wt=Wt, Y=Y)
+    sh = _stream_handle(stream, X.device)
+    _check(lib.gemm_conv2d_nhwc_noalloc(DTYPES[dt], X.data_ptr(), Wt.data_ptr(), Y.data_ptr(),
+                                        ctypes.byref(shape), bptr, act, sh),
+           "gemm_conv2d_nhwc_noalloc")
+    return Y
+
+
 def gemm_im2col_nhwc(X, kernel, stride=1, padding=0, dilation=1, col=None, stream=None):
     """The im2col matrix of an NHWC tensor: (n*ho*wo) x (kh*kw*c_in), row
     (n, oh, ow), column (kh, kw, ci); zeros where a tap falls in the padding."""
@@ -462,5 +494,5 @@ def gemm_quantize_fp8(X, block=64, fmt="e4m3", Q=None, scales=None, stream=None)
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f32", "gemm_fp8_blockscaled", "gemm_f16_epilogue",
            "gemm_bf16_epilogue", "gemm_f32_epilogue", "gemm_fp8_blockscaled_epilogue",
            "gemm_quantize_fp8", "gemm_h16_ladder", "gemm_h16_mfma_ceiling", "gemm_conv2d_nhwc",
-           "gemm_im2col_nhwc", "Conv2dShape", "status_string",
+           "gemm_conv2d_nhwc_noalloc", "gemm_im2col_nhwc", "CONV2D_SCRATCH_BYTES", "Conv2dShape", "status_string",
            "GemmError", "lib", "LIB_PATH"]

@@ -520,9 +520,43 @@ extern "C" int gemm_im2col_nhwc(int dtype, const void *X, void *col, int64_t ldc
     return to_status(im2col_launch((int)esize, X, col, ldcol, s, (int)ho, (int)wo, stream));
 }
 
-extern "C" int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *Y, void *workspace,
-                                int64_t workspace_bytes, const gemm_conv2d_shape *shape,
-                                const float *bias, int activation, hipStream_t stream)
+namespace {
+
+// Scratch for the convolution entry point that allocates nothing: the im2col
+// matrix of a call lives here instead of in a caller workspace.  Each GPU the
+// library runs on holds its own copy from the moment the code object is loaded
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns for the
+// current device may be handed to kernels.
+constexpr int64_t SCRATCH_BYTES = GEMM_CONV2D_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+// Per device: the device address of `scratch`, looked up on the first call that
+// needs it with that device current (0: not looked up yet).
+std::atomic<uintptr_t> g_scratch[MAX_DEVICES];
+
+// The current device's scratch address, or nullptr when it cannot be had.
+void *scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+            return nullptr;
+        p = (uintptr_t)addr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return (void *)p;
+}
+
+// Both convolution entry points.  use_scratch: the im2col matrix goes to the
+// current device's scratch array (workspace and workspace_bytes are ignored)
+// and calls that need more than it holds are refused with GEMM_ERR_SCRATCH.
+int conv_entry(int dtype, const void *X, const void *Wt, void *Y, void *workspace,
+               int64_t workspace_bytes, bool use_scratch, const gemm_conv2d_shape *shape,
+               const float *bias, int activation, hipStream_t stream)
 {
     if (activation != GEMM_ACT_NONE && activation != GEMM_ACT_RELU) return GEMM_ERR_ARG;
     ConvShape s;
@@ -536,16 +570,22 @@ extern "C" int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *
     if (Y == nullptr || (K > 0 && (X == nullptr || Wt == nullptr))) return GEMM_ERR_NULL;
     if ((uintptr_t)Y % esize || (K > 0 && ((uintptr_t)X % esize || (uintptr_t)Wt % esize)))
         return GEMM_ERR_ALIGN;
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GEMM_ERR_WORKSPACE;
-    if (need > 0 && (uintptr_t)workspace % esize) return GEMM_ERR_ALIGN;
+    if (use_scratch) {
+        if (need > SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
+    } else {
+        if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GEMM_ERR_WORKSPACE;
+        if (need > 0 && (uintptr_t)workspace % esize) return GEMM_ERR_ALIGN;
+    }
     const int64_t yb = M * N * esize, xb = (int64_t)s.n * s.h * s.w * s.c_in * esize;
     const int64_t wb = K * N * esize;
     if (K > 0 && (overlaps(Y, yb, X, xb) || overlaps(Y, yb, Wt, wb))) return GEMM_ERR_ALIAS;
-    if (need > 0 && (overlaps(workspace, need, X, xb) || overlaps(workspace, need, Wt, wb) ||
-                     overlaps(workspace, need, Y, yb)))
+    if (!use_scratch && need > 0 &&
+        (overlaps(workspace, need, X, xb) || overlaps(workspace, need, Wt, wb) ||
+         overlaps(workspace, need, Y, yb)))
         return GEMM_ERR_ALIAS;
     if ((st = check_bias(bias, Y, M, N, N, esize)) != GEMM_OK) return st;
     if ((st = check_device()) != GEMM_OK) return st;
+    if (use_scratch && need > 0 && (workspace = scratch_ptr()) == nullptr) return GEMM_ERR_DEVICE;
     Epilogue epi{1.f, 0.f, bias, activation == GEMM_ACT_RELU ? 1 : 0};
     const Epilogue *pe = bias || activation == GEMM_ACT_RELU ? &epi : nullptr;
     const int out = dtype == GEMM_DTYPE_F32 ? OUT_F32 : dtype == GEMM_DTYPE_BF16 ? OUT_BF16 : OUT_F16;
@@ -560,6 +600,23 @@ extern "C" int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *
         return f32_entry(static_cast<const float *>(A), static_cast<const float *>(Wt),
                          static_cast<float *>(Y), M, N, K, K, N, N, pe, stream);
     return h16_entry(dtype == GEMM_DTYPE_BF16, A, Wt, Y, M, N, K, K, N, N, pe, stream);
+}
+
+}  // namespace
+
+extern "C" int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *Y, void *workspace,
+                                int64_t workspace_bytes, const gemm_conv2d_shape *shape,
+                                const float *bias, int activation, hipStream_t stream)
+{
+    return conv_entry(dtype, X, Wt, Y, workspace, workspace_bytes, false, shape, bias, activation,
+                      stream);
+}
+
+extern "C" int gemm_conv2d_nhwc_noalloc(int dtype, const void *X, const void *Wt, void *Y,
+                                        const gemm_conv2d_shape *shape, const float *bias,
+                                        int activation, hipStream_t stream)
+{
+    return conv_entry(dtype, X, Wt, Y, nullptr, 0, true, shape, bias, activation, stream);
 }
 
 extern "C" int gemm_quantize_fp8(const void *X, int in_type, int64_t rows, int64_t cols,
@@ -599,6 +656,8 @@ extern "C" const char *gemm_status_string(int status)
     case GEMM_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case GEMM_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_ERR_WORKSPACE: return "workspace missing or smaller than the call needs";
+    case GEMM_ERR_SCRATCH:
+        return "the call needs more scratch than the library's fixed per-GPU array holds";
     case GEMM_ERR_ARG:
         return "unsupported option (input type, block size, FP8 format, activation, or a "
                "non-finite alpha or beta)";

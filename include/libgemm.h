@@ -52,7 +52,8 @@ enum gemm_status {
     GEMM_ERR_DEVICE = -6,  /* the current device is not a gfx950 GPU, or it cannot be queried */
     GEMM_ERR_LAUNCH = -7,  /* the kernel launch was rejected by the runtime */
     GEMM_ERR_ARG = -8,     /* an option (input type, block size, FP8 format, activation, alpha/beta) is not supported */
-    GEMM_ERR_WORKSPACE = -9 /* a caller-provided workspace is missing or too small */
+    GEMM_ERR_WORKSPACE = -9, /* a caller-provided workspace is missing or too small */
+    GEMM_ERR_SCRATCH = -10   /* the call needs more than the library's fixed scratch array holds */
 };
 
 /* Element types of the convolution entry points. */
@@ -245,6 +246,31 @@ typedef struct gemm_conv2d_shape {
 int gemm_conv2d_nhwc(int dtype, const void *X, const void *Wt, void *Y, void *workspace,
                      int64_t workspace_bytes, const gemm_conv2d_shape *shape, const float *bias,
                      int activation, hipStream_t stream);
+
+/* Bytes of the device array gemm_conv2d_nhwc_noalloc builds its im2col matrix
+ * in: 64 MiB, held by every GPU the library runs on until the process ends. */
+#define GEMM_CONV2D_SCRATCH_BYTES (64LL << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): gemm_conv2d_nhwc with
+ * the im2col matrix built in a library-owned device array of
+ * GEMM_CONV2D_SCRATCH_BYTES instead of a caller workspace.  Same operation,
+ * arguments (less the workspace), layouts, checks, errors and kernels as
+ * gemm_conv2d_nhwc; the call allocates and frees nothing.
+ *   - A call whose im2col matrix (n*ho*wo * kh*kw*c_in elements, see
+ *     gemm_conv2d_workspace_bytes) exceeds GEMM_CONV2D_SCRATCH_BYTES returns
+ *     GEMM_ERR_SCRATCH and launches nothing.  The direct 1 x 1 case uses no
+ *     scratch.
+ *   - There is one array per GPU, shared by every call on that GPU, and it
+ *     keeps whatever the last call wrote (every call rewrites all of the matrix
+ *     it reads).  Calls that overlap in time on one GPU (two host threads, or
+ *     two streams whose work runs concurrently) race on it and must not be
+ *     issued; calls on one stream are ordered and safe.
+ *   - The array's device address is looked up on the first call on each device
+ *     (GEMM_ERR_DEVICE if that fails). */
+int gemm_conv2d_nhwc_noalloc(int dtype, const void *X, const void *Wt, void *Y,
+                             const gemm_conv2d_shape *shape, const float *bias, int activation,
+                             hipStream_t stream);
 
 /* Bytes of workspace gemm_conv2d_nhwc needs for this dtype and geometry (the
  * im2col matrix, n*ho*wo * kh*kw*c_in elements; 0 for the direct 1 x 1 case),

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = dg.status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert dg.status_string(-99) == "unknown status"
@@ -219,6 +219,30 @@ def test_conv_argument_errors():
     import torch
     if not torch.cuda.is_available():
         assert conv(s=S(kh=1, kw=1, pad_h=0, pad_w=0), ws=0, wsb=0) == -6
+    # the variant that allocates nothing: same checks, less the workspace, and
+    # a refusal (no launch) when the im2col matrix exceeds its fixed scratch
+    na = lambda s=S(), x=X, w=W, y=Y, dtype=1, bias=None, act=0: \
+        lib.gemm_conv2d_nhwc_noalloc(dtype, x, w, y, ctypes.byref(s), bias, act, None)
+    assert na(act=2) == -8
+    assert na(dtype=5) == -8
+    assert na(y=0) == -1
+    assert na(y=Y + 1) == -4
+    assert na(y=X + 64) == -5
+    assert na(bias=BIAS + 2) == -4
+    assert na(s=S(c_out=0)) == 0
+    # a 1x1 convolution with stride 2 still needs its im2col matrix: 2 images of
+    # 128 x 128 outputs = 32768 rows of 1024 bf16 = 2^26 bytes exactly fits, one
+    # more channel group does not
+    one = dict(kh=1, kw=1, pad_h=0, pad_w=0, stride_h=2, stride_w=2)
+    fits = S(n=2, h=256, w=256, c_in=1024, c_out=8, **one)
+    assert lib.gemm_conv2d_workspace_bytes(1, ctypes.byref(fits)) == dg.CONV2D_SCRATCH_BYTES
+    over = S(n=2, h=256, w=256, c_in=1032, c_out=8, **one)
+    assert lib.gemm_conv2d_workspace_bytes(1, ctypes.byref(over)) > dg.CONV2D_SCRATCH_BYTES
+    assert na(s=over) == -10
+    assert na(s=S(n=64, h=64, w=64, c_in=64, c_out=64)) == -10
+    if not torch.cuda.is_available():
+        assert na(s=fits) == -6                   # fits: reaches the device check
+        assert na(s=S(kh=1, kw=1, pad_h=0, pad_w=0, n=1 << 20)) != -10   # direct: no scratch
     im2col = lambda s=S(), x=X, col=WS, ld=9 * 16: \
         lib.gemm_im2col_nhwc(1, x, col, ld, ctypes.byref(s), None)
     assert im2col(ld=9 * 16 - 1) == -3
