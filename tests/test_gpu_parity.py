@@ -476,6 +476,8 @@ ROWS_ENV = {"bf16": ("LIBGEMM_H16_CONFIG", "10"), "f16": ("LIBGEMM_H16_CONFIG", 
     ((3, 4095, 517), None),                 # 64 workgroups, the last one ragged
     ((4, 130, 2048), (2051, 131, 133)),     # four rows, unaligned leading dimensions
     ((1, 4095, 4100), (4100, 4095, 4095)),  # the tail row of 4097 x 4095 x 4100
+    ((2, 16500, 300), (301, 16501, 16503)), # 258 workgroups, unaligned ld, offset pointers
+    ((4, 17, 70), (71, 17, 19)),            # one chunk whole, the next straddling N
 ])
 def test_rows_path(dtype, shape, lds):
     """The vector-ALU kernel for at most 4 rows (testing overrides: half-precision
