@@ -26,6 +26,7 @@
 
 #include "gemm_device.hpp"
 #include "gemm_launch.hpp"
+#include "gemm_lds_layout.hpp"
 
 namespace gemm {
 
@@ -45,11 +46,10 @@ constexpr int SB_BLK = SB_STAGE * 4 / 1024 / SNW;
 template <int TAG>
 __shared__ __attribute__((aligned(1024))) float s_stage[2048];
 
-// A rows are 64 bytes (4 chunks).  A 16-byte read by 16 lanes covers 16
-// consecutive rows: moving the chunks of rows 4a .. 4a+3 by a puts all 16
-// reads on distinct banks.
-__host__ __device__ __forceinline__ int swz_af(int row) { return (row >> 2) & 3; }
-__host__ __device__ __forceinline__ int swz_bf(int k) { return ((k >> 2) & 1) << 3; }
+// The XOR swizzles of the stages and the lane -> address maps of every LDS
+// access below are in gemm_lds_layout.hpp (checked on the host for banks).
+using lds::swz_af;
+using lds::swz_bf;
 
 __device__ __forceinline__ void s_barrier_nf() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -119,15 +119,17 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
     uint32_t a_off[SA_BLK], b_off[SB_BLK];
 #pragma unroll
     for (int j = 0; j < SA_BLK; ++j) {
-        const int row = 16 * (wave * SA_BLK + j) + (lane >> 2);
+        int row, chunk;
+        lds::f32_a_dma(wave * SA_BLK + j, lane, row, chunk);
         const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
-        a_off[j] = (uint32_t)(lrow * lda + 4 * ((lane & 3) ^ swz_af(row))) * 4u;
+        a_off[j] = (uint32_t)(lrow * lda + 4 * chunk) * 4u;
     }
     // (GEN: the column, n0 included, is part of the per-lane offset.)
 #pragma unroll
     for (int j = 0; j < SB_BLK; ++j) {
-        const int row = 2 * (wave * SB_BLK + j) + (lane >> 5);
-        int col = 4 * ((lane & 31) ^ swz_bf(row));
+        int row, chunk;
+        lds::f32_b_dma(wave * SB_BLK + j, lane, row, chunk);
+        int col = 4 * chunk;
         if (GEN) col = n0 + col >= N ? N - 4 : n0 + col;
         b_off[j] = (uint32_t)(row * ldb + col) * 4u;
     }
@@ -159,13 +161,10 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
 
     // Fragments (floats, relative to a stage).  Sub-step s covers k = 8s .. 8s+7;
     // the e-th MFMA of it takes k = 8s + 4*half + e in both operands.
-    int a_off_r[SFM], a_swz[SFM];
+    static_assert(SBK == 16 && SBN == 128, "stage rows of 16 and 128 floats");
+    int a_row[SFM];
 #pragma unroll
-    for (int i = 0; i < SFM; ++i) {
-        const int row = wm0 + 32 * i + l32;
-        a_off_r[i] = row * SBK;
-        a_swz[i] = swz_af(row);
-    }
+    for (int i = 0; i < SFM; ++i) a_row[i] = wm0 + 32 * i + l32;
     int b_col[SFN];
 #pragma unroll
     for (int j = 0; j < SFN; ++j) b_col[j] = wn0 + 32 * j + l32;
@@ -186,14 +185,14 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         const int c = 2 * s + half;
 #pragma unroll
         for (int i = 0; i < SFM; ++i)
-            f.a[i] = *reinterpret_cast<const f32x4 *>(as + a_off_r[i] + ((c ^ a_swz[i]) << 2));
+            f.a[i] = *reinterpret_cast<const f32x4 *>(as + lds::f32_a_frag(a_row[i], c));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int k = 8 * s + 4 * half + e;
 #pragma unroll
             for (int j = 0; j < SFN; ++j) {
                 const int n = b_col[j];
-                f.b[j][e] = bs[k * SBN + (((n >> 2) ^ swz_bf(k)) << 2) + (n & 3)];
+                f.b[j][e] = bs[lds::f32_b_elem(k, n)];
             }
         }
     };
@@ -297,7 +296,7 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
                         if (gk + e < K) v[e] = src[e];
                 }
             }
-            *reinterpret_cast<f32x4 *>(as + r * SBK + ((c ^ swz_af(r)) << 2)) = v;
+            *reinterpret_cast<f32x4 *>(as + lds::f32_a_frag(r, c)) = v;
         }
         for (int q = tid; q < SBK * SBN / 4; q += SNW * 64) {
             const int r = q >> 5, c = q & 31;
@@ -313,7 +312,7 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
                         if (gn + e < N) v[e] = src[e];
                 }
             }
-            *reinterpret_cast<f32x4 *>(bs + r * SBN + ((c ^ swz_bf(r)) << 2)) = v;
+            *reinterpret_cast<f32x4 *>(bs + lds::f32_b_elem(r, 4 * c)) = v;
         }
     }
     // (GEN: steps past the last one re-load the last full block, K > SBK.)

@@ -33,6 +33,7 @@
 
 #include "gemm_device.hpp"
 #include "gemm_launch.hpp"
+#include "gemm_lds_layout.hpp"
 
 namespace gemm {
 
@@ -88,18 +89,8 @@ __device__ __forceinline__ uint8_t *q_ring(int idx)
     }
 }
 
-// A rows: 64 bytes (4 chunks), same pattern as the 64-byte half-precision rows.
-__host__ __device__ __forceinline__ int qswz_a(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-// B rows: 256 bytes (16 chunks).  The 8 rows of one transposing read land in 8
-// distinct even chunks (and the neighbouring 16-column group in the odd ones).
-// Rows of 128 bytes (8 chunks): rows two apart share banks, so the 4 rows of
-// each parity take 4 distinct even chunks.
-template <int BN>
-__host__ __device__ __forceinline__ int qswz_b(int k)
-{
-    if constexpr (BN == 256) return (k & 7) << 1;
-    else return ((k >> 1) & 3) << 1;
-}
+// The XOR swizzles of the stages and the lane -> address maps of every LDS
+// access below are in gemm_lds_layout.hpp (checked on the host for banks).
 
 // Global -> LDS loads of 16 bytes (operands) and 4 bytes (scales) per lane.
 // (Functions of their own: with arguments that depend on the kernel's template
@@ -183,15 +174,17 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     uint32_t a_off[QA_BLK], b_off[QB_BLK];
 #pragma unroll
     for (int j = 0; j < QA_BLK; ++j) {
-        const int row = 16 * (wave * QA_BLK + j) + (lane >> 2);
+        int row, chunk;
+        lds::fp8_a_dma(wave * QA_BLK + j, lane, row, chunk);
         const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
-        a_off[j] = (uint32_t)(lrow * lda + 16 * ((lane & 3) ^ qswz_a(row)));
+        a_off[j] = (uint32_t)(lrow * lda + 16 * chunk);
     }
     // (GEN: the column, n0 included, is part of the per-lane offset.)
 #pragma unroll
     for (int j = 0; j < QB_BLK; ++j) {
-        const int row = Sh::BRPK * (wave * QB_BLK + j) + lane / Sh::BCPR;
-        int col = 16 * ((lane % Sh::BCPR) ^ qswz_b<QBN>(row));
+        int row, chunk;
+        lds::fp8_b_dma<QBN>(wave * QB_BLK + j, lane, row, chunk);
+        int col = 16 * chunk;
         if (GEN) col = n0 + col >= N ? N - 16 : n0 + col;
         b_off[j] = (uint32_t)(row * ldb + col);
     }
@@ -211,12 +204,13 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 
     // ---- fragment addressing (bytes, relative to a stage)
     // A tile i: lane reads row wm0 + 32i + l32, k bytes 32*half .. +31 (chunks 2h, 2h+1).
+    static_assert(QBK == 64, "64-byte A rows");
     int a_off0[QFM], a_off1[QFM];
 #pragma unroll
     for (int i = 0; i < QFM; ++i) {
         const int row = wm0 + 32 * i + l32;
-        a_off0[i] = row * QBK + (((2 * half) ^ qswz_a(row)) << 4);
-        a_off1[i] = row * QBK + (((2 * half + 1) ^ qswz_a(row)) << 4);
+        a_off0[i] = lds::fp8_a_frag(row, 2 * half);
+        a_off1[i] = lds::fp8_a_frag(row, 2 * half + 1);
     }
     // B tile j, read q: 16-lane group g, lane w: row 32*(g/2) + 8q + w/2, columns
     // wn0 + 32j + 16*(g%2) + 8*(w%2) .. +7.  (k rows with the same k % 8 share a swizzle.)
@@ -225,7 +219,8 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
     for (int j = 0; j < QFN; ++j) {
         const int n = wn0 + 32 * j + 16 * (g & 1) + 8 * (w16 & 1);
-        b_off_r[j] = (32 * (g >> 1) + r8) * QBN + (((n >> 4) ^ qswz_b<QBN>(r8)) << 4) + (n & 15);
+        // rows 32 (g/2) + 8q + r8 share their swizzle with row r8
+        b_off_r[j] = (32 * (g >> 1) + r8) * QBN + lds::fp8_b_col<QBN>(r8, n);
     }
 
     // ---- block scales.  Every stage also carries the 8 scales of its K block
@@ -390,7 +385,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                     v = u32x4{w[0], w[1], w[2], w[3]};
                 }
             }
-            *reinterpret_cast<u32x4 *>(as + r * QBK + ((c ^ qswz_a(r)) << 4)) = v;
+            *reinterpret_cast<u32x4 *>(as + lds::fp8_a_frag(r, c)) = v;
         }
         for (int q = tid; q < QBK * QBN / 16; q += QNW * 64) {
             const int r = q / Sh::BCPR, c = q % Sh::BCPR;
@@ -407,7 +402,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
                     v = u32x4{w[0], w[1], w[2], w[3]};
                 }
             }
-            *reinterpret_cast<u32x4 *>(bs + r * QBN + ((c ^ qswz_b<QBN>(r)) << 4)) = v;
+            *reinterpret_cast<u32x4 *>(bs + r * QBN + lds::fp8_b_col<QBN>(r, 16 * c)) = v;
         }
         q_scale<0>[64 * wave + lane] = sc_src[(int64_t)(ktiles - 1) * sc_step];
         q_unroll<QSTAGES - 1>([&](auto S) {
@@ -463,7 +458,6 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     for (int i = 0; i < QFM; ++i) {
         const int row = 32 * i + l32;
         uint16_t *buf = st + row * QWTN;
-        const int hsw = half ^ ((row >> 3) & 1);
         if constexpr (EPI) {
             // The prior C of the row's entries first, then the arithmetic.
             const bool row_in = !GEN || m0 + wm0 + row < M;
@@ -492,8 +486,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         for (int j = 0; j < QFN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int chunk = (4 * j + q) ^ (row & 7);
-                *reinterpret_cast<u32x2 *>(buf + chunk * 8 + hsw * 4) =
+                *reinterpret_cast<u32x2 *>(buf + lds::fp8_epi_write(row, 4 * j + q, half)) =
                     u32x2{pack2<true>(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                           pack2<true>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
             }
@@ -503,7 +496,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
 #pragma unroll
     for (int it = 0; it < QWTM / 8; ++it) {
         const int row = 8 * it + (lane >> 3);
-        u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * QWTN + ((cl ^ (row & 7)) << 3));
+        u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * QWTN + lds::fp8_epi_read(row, cl));
         if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
         uint16_t *dst = cbase + (int64_t)row * ldc + 8 * cl;
         if (!GEN) {

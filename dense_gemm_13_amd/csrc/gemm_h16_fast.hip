@@ -30,6 +30,7 @@
 
 #include "gemm_device.hpp"
 #include "gemm_launch.hpp"
+#include "gemm_lds_layout.hpp"
 
 namespace gemm {
 
@@ -46,21 +47,10 @@ constexpr int FAST_WM = 2, FAST_WN = 2;                  // waves along M and N
 template <int TAG, int HALVES>
 __shared__ __attribute__((aligned(1024))) uint16_t lds_stage[HALVES];
 
-// A rows of 64 bytes (4 chunks): rows r..r+7 and r..r+15 at one logical chunk
-// land in distinct banks whether the LDS serves 8 or 16 lanes of a 16-byte read
-// per cycle.  Rows of 128 bytes use swz8.
-__host__ __device__ __forceinline__ int swz_a4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-template <int BK>
-__host__ __device__ __forceinline__ int swz_a(int row)
-{
-    if constexpr (BK == 64) return swz8(row);
-    else return swz_a4(row);
-}
-
-// B rows are 512 bytes (32 chunks).  Rows k..k+3 read by one transposing load
-// get their 32-byte pieces XOR-moved by 64 bytes per row, so the 16 lanes of a
-// group (and the two groups sharing rows) cover distinct banks.
-__host__ __device__ __forceinline__ int swz_b(int k) { return (k & 3) << 2; }
+// The XOR swizzles of the stages and the lane -> address maps of every LDS
+// access below are in gemm_lds_layout.hpp (checked on the host for banks).
+using lds::swz_a;
+using lds::swz_b;
 
 __device__ __forceinline__ void dma16(const void *src, uint16_t *lds_block)
 {
@@ -182,9 +172,10 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     uint32_t a_off[A_BLK];
 #pragma unroll
     for (int j = 0; j < A_BLK; ++j) {
-        const int row = ROWS_PER_KB * (wave * A_BLK + j) + lane / CPR;
+        int row, chunk;
+        lds::h16_a_dma<BK>(wave * A_BLK + j, lane, row, chunk);
         const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
-        a_off[j] = (uint32_t)(lrow * lda + 8 * ((lane % CPR) ^ swz_a<BK>(row))) * 2u;
+        a_off[j] = (uint32_t)(lrow * lda + 8 * chunk) * 2u;
     }
     // B block b (BRPK rows of FBN halves: 2 rows of 512 bytes, or 4 of 256):
     // lane -> row BRPK*b + lane/BCPR, slot lane%BCPR.  For GEN the column
@@ -193,8 +184,9 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     uint32_t b_off_g[B_BLK];
 #pragma unroll
     for (int j = 0; j < B_BLK; ++j) {
-        const int row = BRPK * (wave * B_BLK + j) + lane / BCPR;
-        int col = 8 * ((lane % BCPR) ^ swz_b(row));
+        int row, chunk;
+        lds::h16_b_dma<FBN>(wave * B_BLK + j, lane, row, chunk);
+        int col = 8 * chunk;
         if (GEN) col = n0 + col >= N ? N - 8 : n0 + col;
         b_off_g[j] = (uint32_t)(row * ldb + col) * 2u;
     }
@@ -215,13 +207,9 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     // ---- fragment addressing (in halves, relative to a stage)
     // A: lane reads row wm0 + 32i + l32, logical chunk 2s + half.
-    int a_row_off[FFM], a_swz[FFM];
+    int a_row[FFM];
 #pragma unroll
-    for (int i = 0; i < FFM; ++i) {
-        const int row = wm0 + 32 * i + l32;
-        a_row_off[i] = row * BK;
-        a_swz[i] = swz_a<BK>(row);
-    }
+    for (int i = 0; i < FFM; ++i) a_row[i] = wm0 + 32 * i + l32;
     // B: 16-lane group g, lane w in it: row r = w/4 of the 4 rows read, column
     // piece 4*(w%4); groups 0/1 take columns 0-15 / 16-31 of the 32-wide tile,
     // groups 0,1 / 2,3 take k 0-7 / 8-15 of the 16-wide step.
@@ -230,7 +218,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
     for (int j = 0; j < FFN; ++j) {
         const int n = wn0 + 32 * j + 16 * (g & 1) + 4 * c4;
-        b_off[j] = (((n >> 3) ^ swz_b(r4)) << 3) + (n & 7);
+        b_off[j] = lds::h16_b_col(r4, n);     // rows 16 s + b_krow (+4) share r4 = k % 4
     }
     const int b_krow = 8 * (g >> 1) + r4;    // + 16 s + 4 q
 
@@ -249,7 +237,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int c = 2 * s + half;
 #pragma unroll
         for (int i = 0; i < FFM; ++i)
-            f.a[i] = *reinterpret_cast<const u32x4 *>(as + a_row_off[i] + ((c ^ a_swz[i]) << 3));
+            f.a[i] = *reinterpret_cast<const u32x4 *>(as + lds::h16_a_frag<BK>(a_row[i], c));
 #pragma unroll
         for (int j = 0; j < FFN; ++j) {
             const uint16_t *p0 = bs + (16 * s + b_krow) * FBN + b_off[j];
@@ -367,8 +355,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                         if (gk + e < K) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
                 }
             }
-            *reinterpret_cast<u32x4 *>(as + r * BK + ((c ^ swz_a<BK>(r)) << 3)) =
-                u32x4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4 *>(as + lds::h16_a_frag<BK>(r, c)) = u32x4{w[0], w[1], w[2], w[3]};
         }
 #pragma unroll
         for (int q = tid; q < B_STAGE / 8; q += NT) {
@@ -386,7 +373,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                         if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
                 }
             }
-            *reinterpret_cast<u32x4 *>(bs + r * FBN + ((c ^ swz_b(r)) << 3)) =
+            *reinterpret_cast<u32x4 *>(bs + r * FBN + lds::h16_b_col(r, 8 * c)) =
                 u32x4{w[0], w[1], w[2], w[3]};
         }
     }
@@ -444,8 +431,10 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // whole row segments of the sub-tile with 16 bytes per lane.  Lane l holds
     // C[32i + l%32][32j + 8q + 4*(l/32) .. +3]: 8 bytes in 16-byte chunk 4j + q,
     // half l/32.  Chunks are XORed with the row modulo the chunks per row and the
-    // half with the next row bit, so the rows one store touches spread over the
-    // banks.
+    // half with row bit 3 (lds::h16_epi_write), so the 16 rows one write cycle
+    // touches spread over the banks.  (Flipping it with the row bit above the
+    // chunk count, as before, left 256-byte rows with chunks c and c + 8 on
+    // the same banks: 256 conflict cycles per wave, all of the kernel's.)
     // Square tiles stage in the A and B arrays alike; wider tiles (B stages
     // larger than A stages) in the B arrays only, one per wave.
     constexpr int SQ = A_STAGE == B_STAGE;
@@ -479,7 +468,6 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     for (int i = 0; i < FFM; ++i) {
         const int row = 32 * i + l32;
         uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
-        const int hsw = half ^ ((row / CPRC) & 1);
         [[maybe_unused]] const int gm = m0 + wm0 + row;
         [[maybe_unused]] const uint16_t *crow = C + (int64_t)gm * ldc;
         // EPI, whole tiles: the prior C of the row's entries first (all loads in
@@ -507,8 +495,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 } else if constexpr (EPI) {
                     epilogue_apply<4>(epi, v, ebias[j][q], prior[j][q], 4);
                 }
-                const int chunk = (4 * j + q) ^ (row % CPRC);
-                *reinterpret_cast<u32x2 *>(buf + chunk * 8 + hsw * 4) =
+                *reinterpret_cast<u32x2 *>(buf + lds::h16_epi_write<CPRC>(row, 4 * j + q, half)) =
                     u32x2{pack2<IS_BF16>(v[0], v[1]), pack2<IS_BF16>(v[2], v[3])};
             }
     }
@@ -523,8 +510,8 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     for (int it = 0; it < FWTM / RPI; ++it) {
         const int row = RPI * it + lane / CPRC;
         const uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
-        u32x4 v = *reinterpret_cast<const u32x4 *>(buf + ((cl ^ (row % CPRC)) << 3));
-        if ((row / CPRC) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        u32x4 v = *reinterpret_cast<const u32x4 *>(buf + lds::h16_epi_read<CPRC>(row, cl));
+        if (lds::h16_epi_swap(row)) v = u32x4{v[2], v[3], v[0], v[1]};
         uint16_t *dst = cbase + (int64_t)row * ldc + 8 * cl;
         if (!GEN) {
             // Non-temporal (here and for the guarded kernel's whole chunks in
