@@ -96,7 +96,24 @@ __device__ __forceinline__ uint8_t *q_ring(int idx)
 // (Functions of their own: with arguments that depend on the kernel's template
 // parameters, the builtin called directly in the kernel's lambdas leaves the
 // host-side instantiation of the kernel invalid and its launch stub undefined.)
-__device__ __forceinline__ void q_dma16(const void *src, uint8_t *lds)
+// Operands go through a buffer descriptor: the base in scalar registers, the
+// lane's 32-bit offset in a vector register, so no per-load 64-bit address
+// arithmetic runs on the vector ALU that the promotion keeps busy.  `reach` is
+// the number of bytes the tile may touch from the base; an offset past it would
+// read zeros instead of leaving the operand.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t q_rsrc(const void *base, int reach)
+{
+    // 4th word 0x00020000: 32-bit data format, the raw-buffer setting for gfx9.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, reach, 0x00020000);
+}
+// (Whole tiles only: their rows are 16-byte aligned.  Buffer loads at byte
+// offsets that are not were measured to return wrong data, so the guarded
+// instantiation, which takes any leading dimension, uses q_gdma16.)
+__device__ __forceinline__ void q_dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void8_t *)lds, 16, (int)off, 0, 0, 0);
+}
+__device__ __forceinline__ void q_gdma16(const void *src, uint8_t *lds)
 {
     __builtin_amdgcn_global_load_lds(src, (lds_void8_t *)lds, 16, 0, 0);
 }
@@ -191,15 +208,24 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     const uint8_t *a_base = A + (int64_t)m0 * lda;
     const uint8_t *b_base = GEN ? B : B + n0;
     const int64_t b_step = (int64_t)QBK * ldb;
+    // (QBM rows of A and QBK rows of B from the step's base: below 2^31 bytes
+    // under the eligibility limits lda < 2^23, ldb < 2^24.)
+    const int a_reach = (int)(QBM * lda), b_reach = (int)(QBK * ldb);
     auto issue = [&](uint8_t *as, uint8_t *bs, int kt) {
         const uint8_t *ab = a_base + kt * QBK;
         const uint8_t *bb = b_base + kt * b_step;
+        if constexpr (GEN) {
 #pragma unroll
-        for (int j = 0; j < QA_BLK; ++j)
-            q_dma16(ab + a_off[j], as + (wave * QA_BLK + j) * 1024);
+            for (int j = 0; j < QA_BLK; ++j) q_gdma16(ab + a_off[j], as + (wave * QA_BLK + j) * 1024);
 #pragma unroll
-        for (int j = 0; j < QB_BLK; ++j)
-            q_dma16(bb + b_off[j], bs + (wave * QB_BLK + j) * 1024);
+            for (int j = 0; j < QB_BLK; ++j) q_gdma16(bb + b_off[j], bs + (wave * QB_BLK + j) * 1024);
+        } else {
+            const __amdgpu_buffer_rsrc_t ra = q_rsrc(ab, a_reach), rb = q_rsrc(bb, b_reach);
+#pragma unroll
+            for (int j = 0; j < QA_BLK; ++j) q_dma16(ra, a_off[j], as + (wave * QA_BLK + j) * 1024);
+#pragma unroll
+            for (int j = 0; j < QB_BLK; ++j) q_dma16(rb, b_off[j], bs + (wave * QB_BLK + j) * 1024);
+        }
     };
 
     // ---- fragment addressing (bytes, relative to a stage)
@@ -239,7 +265,11 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // K step s loads K block s (GEN: block s - 1; step 0 is the last block).
     auto issue_all = [&](auto S, int s) {
         const int kb = GEN ? s - 1 : s;
-        issue(q_stage<S, QSTAGE>, q_stage<QSTAGES + S, QSTAGE>, kb);
+        // (B stages take the first array tags and A stages the last: placed
+        // that way, every B read's stage base fits the LDS instruction's
+        // 16-bit offset field, and only the two A read bases need an add per
+        // step: 5 -> 2 vector adds per K step.)
+        issue(q_stage<QSTAGES + S, QSTAGE>, q_stage<S, QSTAGE>, kb);
         q_dma4(sc_src + kb * sc_step, &q_scale<S>[64 * wave]);
     };
     constexpr int QLOADS = QNBLK + 1;                    // loads per wave per stage
@@ -341,18 +371,18 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         __builtin_amdgcn_sched_barrier(0);
         const int nxt = s + QSTAGES;
         issue_all(S, nxt < ktiles ? nxt : ktiles - 1);
-        read_b(q_stage<QSTAGES + N1, QSTAGE>, 0);
+        read_b(q_stage<N1, QSTAGE>, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = NT / 2; t < NT; ++t) {
             mma(t);
             promote(t - 1, cs0, cs1);
-            read_a(q_stage<N1, QSTAGE>, t - NT / 2);
+            read_a(q_stage<QSTAGES + N1, QSTAGE>, t - NT / 2);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        read_b(q_stage<QSTAGES + N1, QSTAGE>, 1);
+        read_b(q_stage<N1, QSTAGE>, 1);
         ps0 = cs0;
         ps1 = cs1;
         read_scales(q_scale<N1>);
@@ -369,7 +399,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     // its scales (written before any LDS-direct load is issued).
     if constexpr (GEN) {
         const int k0 = QBK * (ktiles - 1);
-        uint8_t *as = q_stage<0, QSTAGE>, *bs = q_stage<QSTAGES, QSTAGE>;
+        uint8_t *as = q_stage<QSTAGES, QSTAGE>, *bs = q_stage<0, QSTAGE>;
         for (int q = tid; q < QBM * QBK / 16; q += QNW * 64) {
             const int r = q >> 2, c = q & 3;
             const int gm = m0 + r, gk = k0 + 16 * c;
@@ -416,9 +446,9 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     }
     q_barrier();
 #pragma unroll
-    for (int i = 0; i < QFM; ++i) read_a(q_stage<0, QSTAGE>, i);
+    for (int i = 0; i < QFM; ++i) read_a(q_stage<QSTAGES, QSTAGE>, i);
 #pragma unroll
-    for (int j = 0; j < QFN; ++j) read_b(q_stage<QSTAGES, QSTAGE>, j);
+    for (int j = 0; j < QFN; ++j) read_b(q_stage<0, QSTAGE>, j);
     read_scales(q_scale<0>);
     part[(NT - 1) & 1] = f32x16{};
     // Whole turns of the ring without conditions (a step skipped at run time
