@@ -56,6 +56,22 @@ __device__ __forceinline__ void dma16(const void *src, uint16_t *lds_block)
 {
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)lds_block, 16, 0, 0);
 }
+// Whole tiles load through buffer descriptors: the step's base in scalar
+// registers and the lane's 32-bit offset in a vector register, so the loop
+// spends no vector instructions on 64-bit load addresses (4096^3: 103.9 ->
+// 102.4 us).  `reach` bounds the bytes a tile may touch from the base (an
+// offset past it reads zeros).  The 4th descriptor word 0x00020000 is the raw
+// 32-bit data format of gfx9.  The guarded instantiation keeps dma16: its rows
+// need not be 16-byte aligned, and buffer loads at such offsets were measured
+// to return wrong data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(const void *base, int reach)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, reach, 0x00020000);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t *lds_block)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_block, 16, (int)off, 0, 0, 0);
+}
 
 // s_waitcnt vmcnt(N) (N < 64), leaving expcnt and lgkmcnt alone.
 template <int N>
@@ -195,14 +211,24 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int64_t a_step = (int64_t)BK * 2, b_step = (int64_t)BK * ldb * 2;
 
     // Step s loads K block s (GEN: block s-1; step 0 is the last block, below).
+    // (below 2^31 under the whole-tile limits lda, ldb < 2^22)
+    const int a_reach = (int)(FBM * lda * 2), b_reach = (int)(BK * ldb * 2);
     auto issue = [&](uint16_t *as, uint16_t *bs, int s) {
         const int kb = GEN ? s - 1 : s;
         const char *ab = a_base + kb * a_step;
         const char *bb = b_base + kb * b_step;
+        if constexpr (GEN) {
 #pragma unroll
-        for (int j = 0; j < A_BLK; ++j) dma16(ab + a_off[j], as + (wave * A_BLK + j) * 512);
+            for (int j = 0; j < A_BLK; ++j) dma16(ab + a_off[j], as + (wave * A_BLK + j) * 512);
 #pragma unroll
-        for (int j = 0; j < B_BLK; ++j) dma16(bb + b_off_g[j], bs + (wave * B_BLK + j) * 512);
+            for (int j = 0; j < B_BLK; ++j) dma16(bb + b_off_g[j], bs + (wave * B_BLK + j) * 512);
+        } else {
+            const __amdgpu_buffer_rsrc_t ra = h_rsrc(ab, a_reach), rb = h_rsrc(bb, b_reach);
+#pragma unroll
+            for (int j = 0; j < A_BLK; ++j) bdma16(ra, a_off[j], as + (wave * A_BLK + j) * 512);
+#pragma unroll
+            for (int j = 0; j < B_BLK; ++j) bdma16(rb, b_off_g[j], bs + (wave * B_BLK + j) * 512);
+        }
     };
 
     // ---- fragment addressing (in halves, relative to a stage)
