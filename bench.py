@@ -4,15 +4,20 @@ the dense matrix-core peak, on seeded synthetic matrices resident in HBM.
 
 A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
 (row-major A and B, fp32 accumulation, bf16 C).  The other workloads (fp16
-4096^3, the ragged bf16 shapes, fp32 4096^3, fp8 block-scaled 8192^3, fp16
-256^3, the 4096^3 bf16 product with a fused bias + relu epilogue and with a
-fused residual add, the MFMA-only ceiling of the headline kernel, the seven
-rungs of the optimisation ladder on fp16 4096^3, two 3x3 convolution layers
-through im2col + GEMM and the im2col pack alone, and the FP8 block quantiser on
-the fp8 workload's 8192 x 8192 operand) are measured in the same run and listed
-under "workloads".
+4096^3, the ragged bf16 shapes, bf16 2048^3 and 2560^3 on the medium-grid
+tiles, fp32 4096^3, fp8 block-scaled 8192^3, fp16 256^3, the 4096^3 bf16
+product with a fused bias + relu epilogue and with a fused residual add, the
+MFMA-only ceiling of the headline kernel, the seven rungs of the optimisation
+ladder on fp16 4096^3, two 3x3 convolution layers through im2col + GEMM and the
+im2col pack alone, and the FP8 block quantiser on the fp8 workload's 8192 x 8192
+operand) are measured in the same run and listed under "workloads".
+
+Each workload first runs a settle pass (about 50 ms of back-to-back launches:
+the clock ramps up from idle over the first ~20 ms of work), then W warm-up
+launches, then the K timed launches.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
+                    [--settle-ms MS] [--cold-steps N] [--no-cpu-baseline]
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -58,7 +63,7 @@ def algorithmic_bytes(dtype: str, M: int, N: int, K: int) -> int:
 
 # Sources that define the headline kernel's machine code: the measured traffic
 # below stays valid while these are unchanged.
-HEADLINE_KERNEL_SOURCES = ("gemm_h16_fast.hip", "gemm_device.hpp")
+HEADLINE_KERNEL_SOURCES = ("gemm_h16_fast.hip", "gemm_device.hpp", "gemm_lds_layout.hpp")
 
 
 def kernel_source_digest(files=HEADLINE_KERNEL_SOURCES) -> str:
@@ -95,6 +100,11 @@ SETTLE_SECONDS = 0.05
 SETTLE_MAX_LAUNCHES = 2000
 
 _FLUSH = {}
+
+
+def set_settle(seconds: float):
+    global SETTLE_SECONDS
+    SETTLE_SECONDS = seconds
 
 
 def flush_buffer(device):
@@ -197,6 +207,8 @@ class Workload:
         e1.record(self.stream)
         torch.cuda.synchronize()
         t1 = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+        if SETTLE_SECONDS <= 0:
+            return 0
         return max(self.sustain, min(SETTLE_MAX_LAUNCHES, int(SETTLE_SECONDS / t1)))
 
     def run(self, steps: int, warmup: int, cold_steps: int) -> dict:
@@ -478,6 +490,9 @@ WORKLOADS = [
     Workload("bf16_1000", "bf16 GEMM 1000x1000x1000", "bf16", 1000, 1000, 1000, 3),
     Workload("bf16_ragged", "bf16 GEMM 4097x4095x4100", "bf16", 4097, 4095, 4100, 3),
     Workload("bf16_skinny", "bf16 GEMM 8192x64x4096", "bf16", 8192, 64, 4096, 3),
+    # medium grids: 128 x 128 tiles (two workgroups per CU) and 128 x 256 tiles
+    Workload("bf16_2048", "bf16 GEMM M=N=K=2048", "bf16", 2048, 2048, 2048, 6),
+    Workload("bf16_2560", "bf16 GEMM M=N=K=2560", "bf16", 2560, 2560, 2560, 7),
     Workload("f32_4096", "fp32 SGEMM M=N=K=4096", "f32", 4096, 4096, 4096, 4),
     Workload("fp8_8192", "fp8 E4M3 64x64-block-scaled GEMM M=N=K=8192, bf16 C", "fp8",
              8192, 8192, 8192, 5),
@@ -591,10 +606,14 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="launches timed after a 512 MiB cache-flushing write each (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_SECONDS * 1e3,
+                    help="back-to-back launches before each workload's warm-up, in ms of "
+                         "GPU time (0: none; counter runs use 0)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy (torch.neg) of this many MiB, "
                          "5 times: the known-size kernel that calibrates HBM byte counters")
     args = ap.parse_args()
+    set_settle(args.settle_ms * 1e-3)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library "
               "has no multi-GPU path.", file=sys.stderr)
@@ -671,7 +690,7 @@ def main():
         # the settle pass (>= 300 launches back to back in one region, before
         # the warm-up and the timed steps): the rate over the clock's ramp from
         # idle and after it
-        "settle_launches": h["settle_launches"],
+        "settle_launches": h.get("settle_launches"),
         "sustained": None if "sustained_tflops" not in h else {
             "launches": h["sustained_launches"],
             "mean_launch_us": round(h["sustained_mean_launch_us"], 2),
