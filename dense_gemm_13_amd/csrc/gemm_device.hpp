@@ -187,6 +187,65 @@ __device__ __forceinline__ void epilogue_prior(const Epilogue &e, const void *ro
     for (int t = 0; t < W; ++t) c[t] = t < cnt ? load_out<OUT>(row, n + t) : 0.f;
 }
 
+// The bias and prior-C loads for whole groups of W columns at offsets that are
+// multiples of W, as in a whole tile.  Whether the vector loads apply then
+// depends only on the base pointers and ldc, so the caller decides it once per
+// kernel (`vec`, a uniform branch) instead of from each lane's own address,
+// which made every group a divergent branch with an element-wise fallback.
+template <int W>
+__device__ __forceinline__ void epilogue_bias_whole(const Epilogue &e, int n, bool vec, float *b)
+{
+    static_assert(W == 4 || W == 8, "epilogue width");
+    if (vec) {
+#pragma unroll
+        for (int h = 0; h < W / 4; ++h) {
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(e.bias + n + 4 * h);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) b[4 * h + t] = x[t];
+        }
+    } else if (e.bias) {
+#pragma unroll
+        for (int t = 0; t < W; ++t) b[t] = e.bias[n + t];
+    } else {
+#pragma unroll
+        for (int t = 0; t < W; ++t) b[t] = 0.f;
+    }
+}
+// Prior C of W whole 16-bit columns; `vec`: row + n is 2W-byte aligned for
+// every row and group.  The caller reads nothing when beta == 0.
+template <int OUT, int W>
+__device__ __forceinline__ void epilogue_prior_whole(const void *row, int n, bool vec, float *c)
+{
+    static_assert(OUT != OUT_F32 && W == 4, "16-bit groups of 4");
+    const uint16_t *p = static_cast<const uint16_t *>(row) + n;
+    if (vec) {
+        const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+#pragma unroll
+        for (int t = 0; t < W; ++t) {
+            const uint16_t bits = (uint16_t)(x[t >> 1] >> (16 * (t & 1)));
+            if constexpr (OUT == OUT_BF16) c[t] = __uint_as_float((uint32_t)bits << 16);
+            else c[t] = (float)__builtin_bit_cast(_Float16, bits);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < W; ++t) c[t] = load_out<OUT>(row, n + t);
+    }
+}
+
+// One entry before the activation: alpha * v + b in one fused multiply-add,
+// then + beta * c (a second one) when the prior C is read.  Every kernel's
+// epilogue evaluates it this way.
+__device__ __forceinline__ float epilogue_value(const Epilogue &e, float v, float b)
+{
+    return fmaf(e.alpha, v, b);
+}
+__device__ __forceinline__ float epilogue_value(const Epilogue &e, float v, float b, float c)
+{
+    return fmaf(e.beta, c, fmaf(e.alpha, v, b));
+}
+// relu; NaN and -0 become +0, as with x > 0 ? x : 0.
+__device__ __forceinline__ float epilogue_relu(float x) { return x > 0.f ? x : 0.f; }
+
 // v = act(alpha * v + beta * c + b) for the first cnt entries.
 template <int W>
 __device__ __forceinline__ void epilogue_apply(const Epilogue &e, float *v, const float *b,
@@ -195,10 +254,8 @@ __device__ __forceinline__ void epilogue_apply(const Epilogue &e, float *v, cons
 #pragma unroll
     for (int t = 0; t < W; ++t) {
         if (t < cnt) {
-            float x = e.alpha * v[t];
-            if (e.beta != 0.f) x = fmaf(e.beta, c[t], x);
-            x += b[t];
-            if (e.relu) x = x > 0.f ? x : 0.f;
+            float x = e.beta != 0.f ? epilogue_value(e, v[t], b[t], c[t]) : epilogue_value(e, v[t], b[t]);
+            if (e.relu) x = epilogue_relu(x);
             v[t] = x;
         }
     }

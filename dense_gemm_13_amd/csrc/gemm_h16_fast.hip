@@ -481,49 +481,78 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         else st[a] = b_ring_array<ARR_SZ, STAGES>(wave * ARR + a);
     }
     // EPI, whole tiles: the bias of this lane's columns, loaded once for all
-    // its rows.
+    // its rows.  Column offsets are multiples of 4, so whether the 16-byte bias
+    // loads and 8-byte prior loads are aligned is a property of the kernel's
+    // arguments, decided once.
     [[maybe_unused]] float ebias[EPI && !GEN ? FFN : 1][4][4];
+    [[maybe_unused]] const bool prior_on = EPI && !GEN && epi.beta != 0.f;
+    [[maybe_unused]] const bool prior_vec = ((uintptr_t)C & 7) == 0 && (ldc & 3) == 0;
     if constexpr (EPI && !GEN) {
+        const bool bias_vec = epi.bias && ((uintptr_t)epi.bias & 15) == 0;
 #pragma unroll
         for (int j = 0; j < FFN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                epilogue_bias<4>(epi, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4, ebias[j][q]);
+                epilogue_bias_whole<4>(epi, n0 + wn0 + 32 * j + 8 * q + 4 * half, bias_vec,
+                                       ebias[j][q]);
     }
+    // The rows, as one body per combination of the two uniform epilogue
+    // switches (prior C read, relu), so that no entry branches on them.
+    auto stage_rows = [&](auto PRIOR, auto RELU) {
 #pragma unroll
-    for (int i = 0; i < FFM; ++i) {
-        const int row = 32 * i + l32;
-        uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
-        [[maybe_unused]] const int gm = m0 + wm0 + row;
-        [[maybe_unused]] const uint16_t *crow = C + (int64_t)gm * ldc;
-        // EPI, whole tiles: the prior C of the row's entries first (all loads in
-        // flight at once), then the arithmetic.  The guarded variant, short of
-        // registers, takes each group of 4 entries on its own.
-        [[maybe_unused]] float prior[EPI && !GEN ? FFN : 1][4][4];
-        if constexpr (EPI && !GEN) {
+        for (int i = 0; i < FFM; ++i) {
+            const int row = 32 * i + l32;
+            uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
+            [[maybe_unused]] const int gm = m0 + wm0 + row;
+            [[maybe_unused]] const uint16_t *crow = C + (int64_t)gm * ldc;
+            // EPI, whole tiles: the prior C of the row's entries first (all
+            // loads in flight at once), then the arithmetic.  The guarded
+            // variant, short of registers, takes each group of 4 entries on its
+            // own.
+            [[maybe_unused]] float prior[EPI && !GEN && PRIOR ? FFN : 1][4][4];
+            if constexpr (EPI && !GEN && PRIOR) {
+#pragma unroll
+                for (int j = 0; j < FFN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        epilogue_prior_whole<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(
+                            crow, n0 + wn0 + 32 * j + 8 * q + 4 * half, prior_vec, prior[j][q]);
+            }
 #pragma unroll
             for (int j = 0; j < FFN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    epilogue_prior<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(
-                        epi, crow, n0 + wn0 + 32 * j + 8 * q + 4 * half, 4, prior[j][q]);
-        }
+                for (int q = 0; q < 4; ++q) {
+                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                  acc[i][j][4 * q + 3]};
+                    if constexpr (EPI && GEN) {
+                        const int gn = n0 + wn0 + 32 * j + 8 * q + 4 * half;
+                        if (gm < M)
+                            epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(epi, v, crow, gn, N - gn);
+                    } else if constexpr (EPI) {
 #pragma unroll
-        for (int j = 0; j < FFN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                              acc[i][j][4 * q + 3]};
-                if constexpr (EPI && GEN) {
-                    const int gn = n0 + wn0 + 32 * j + 8 * q + 4 * half;
-                    if (gm < M)
-                        epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(epi, v, crow, gn, N - gn);
-                } else if constexpr (EPI) {
-                    epilogue_apply<4>(epi, v, ebias[j][q], prior[j][q], 4);
+                        for (int t = 0; t < 4; ++t) {
+                            if constexpr (PRIOR)
+                                v[t] = epilogue_value(epi, v[t], ebias[j][q][t], prior[j][q][t]);
+                            else
+                                v[t] = epilogue_value(epi, v[t], ebias[j][q][t]);
+                            if constexpr (RELU) v[t] = epilogue_relu(v[t]);
+                        }
+                    }
+                    *reinterpret_cast<u32x2 *>(buf + lds::h16_epi_write<CPRC>(row, 4 * j + q, half)) =
+                        u32x2{pack2<IS_BF16>(v[0], v[1]), pack2<IS_BF16>(v[2], v[3])};
                 }
-                *reinterpret_cast<u32x2 *>(buf + lds::h16_epi_write<CPRC>(row, 4 * j + q, half)) =
-                    u32x2{pack2<IS_BF16>(v[0], v[1]), pack2<IS_BF16>(v[2], v[3])};
-            }
+        }
+    };
+    if constexpr (EPI && !GEN) {
+        if (prior_on) {
+            if (epi.relu) stage_rows(yes{}, yes{});
+            else stage_rows(yes{}, no{});
+        } else {
+            if (epi.relu) stage_rows(no{}, yes{});
+            else stage_rows(no{}, no{});
+        }
+    } else {
+        stage_rows(no{}, no{});
     }
     uint16_t *const cbase = C + (int64_t)(m0 + wm0) * ldc + n0 + wn0;
     const int cl = lane % CPRC;
