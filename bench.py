@@ -14,7 +14,9 @@ operand) are measured in the same run and listed under "workloads".
 
 Each workload first runs a settle pass (about 50 ms of back-to-back launches:
 the clock ramps up from idle over the first ~20 ms of work), then W warm-up
-launches, then the K timed launches.
+launches, then the K timed launches.  Plain GEMM workloads whose launches take
+less than 40 us are also timed from a HIP graph of captured launches, since the
+host's per-call launch cost bounds them otherwise.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
                     [--settle-ms MS] [--cold-steps N] [--no-cpu-baseline]
@@ -102,6 +104,11 @@ SETTLE_MAX_LAUNCHES = 2000
 _FLUSH = {}
 
 
+# Plain GEMM workloads whose launches take less than this are also timed from a
+# HIP graph (the host's launch rate bounds them otherwise).
+GRAPH_BELOW_S = 40e-6
+
+
 def set_settle(seconds: float):
     global SETTLE_SECONDS
     SETTLE_SECONDS = seconds
@@ -153,16 +160,53 @@ class Workload:
             self.sb = torch.from_numpy(ops["scale_b"]).to(dev)
             self.C = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
         self.stream = torch.cuda.current_stream(dev)
-        s = ctypes.c_void_p(self.stream.cuda_stream)
         M, N, K = self.M, self.N, self.K
         a, b, c = self.A.data_ptr(), self.B.data_ptr(), self.C.data_ptr()
         if self.dtype == "fp8":
             fn, sa, sb = dg.lib.gemm_fp8_blockscaled, self.sa.data_ptr(), self.sb.data_ptr()
-            self.call = lambda: fn(a, b, c, M, N, K, K, N, N, sa, sb, s)
+            self.call_on = lambda st: (lambda h=ctypes.c_void_p(st.cuda_stream):
+                                       fn(a, b, c, M, N, K, K, N, N, sa, sb, h))
         else:
             fn = getattr(dg.lib, "gemm_" + self.dtype)
-            self.call = lambda: fn(a, b, c, M, N, K, K, N, N, s)
+            self.call_on = lambda st: (lambda h=ctypes.c_void_p(st.cuda_stream):
+                                       fn(a, b, c, M, N, K, K, N, N, h))
+        self.call = self.call_on(self.stream)
         torch.cuda.synchronize()
+
+    def graph(self, launches: int, replays: int = 5):
+        """Mean launch time with `launches` launches captured in one HIP graph and
+        the graph replayed `replays` times between two events: the kernel's own
+        rate, without the host's per-call launch cost, which is longer than
+        kernels of a few microseconds.  Every replay's C is checked bit for bit
+        against the eager launches' C (the kernels are deterministic)."""
+        import torch
+        torch.cuda.synchronize()
+        ref = self.C.clone()
+        self.C.fill_(0)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            call = self.call_on(cap)
+            for _ in range(launches):
+                rc = call()
+                if rc != 0:
+                    raise RuntimeError(f"{self.name}: libgemm returned {rc} under capture")
+        for _ in range(2):
+            self.C.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(self.C.view(torch.uint8), ref.view(torch.uint8)):
+                raise RuntimeError(f"{self.name}: graph replay differs from the eager result")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if not torch.equal(self.C.view(torch.uint8), ref.view(torch.uint8)):
+            raise RuntimeError(f"{self.name}: graph replay differs from the eager result")
+        del g
+        return e0.elapsed_time(e1) * 1e-3 / (replays * launches)
 
     def cold(self, steps: int) -> float:
         """Mean launch time with L2 and the Infinity Cache flushed before each
@@ -256,6 +300,11 @@ class Workload:
         median = per[len(per) // 2]
         cold = self.cold(cold_steps) if cold_steps > 0 else None
         r = self.report(region, wall, mean, median, cold)
+        if type(self) is Workload and mean < GRAPH_BELOW_S:
+            g = self.graph(max(steps, 50))
+            r["graph_mean_launch_us"] = g * 1e6
+            r["graph_tflops"] = tflops(self.M, self.N, self.K, g)
+            r["graph_alg_gbs"] = algorithmic_bytes(self.dtype, self.M, self.N, self.K) / g / 1e9
         r["settle_launches"] = settle
         if sustained is not None:
             r["sustained_launches"] = settle
@@ -281,8 +330,10 @@ class Workload:
         }
 
     def summary(self, r) -> str:
+        g = (f"; from a graph {r['graph_mean_launch_us']:.1f} us, {r['graph_tflops']:.1f} TFLOP/s"
+             if "graph_mean_launch_us" in r else "")
         return (f"{r['tflops']:.1f} TFLOP/s ({r['pct_peak']:.1f}% peak), "
-                f"{r['mean_launch_us']:.1f} us/launch")
+                f"{r['mean_launch_us']:.1f} us/launch{g}")
 
 
 class QuantWorkload(Workload):
