@@ -19,7 +19,7 @@ less than 40 us are also timed from a HIP graph of captured launches, since the
 host's per-call launch cost bounds them otherwise.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
-                    [--settle-ms MS] [--cold-steps N] [--no-cpu-baseline]
+                    [--settle-ms MS] [--cold-steps N] [--no-cpu-baseline] [--no-graph]
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -655,7 +655,9 @@ def main():
                     help="all | headline | comma-separated keys: "
                          + ",".join(w.key for w in WORKLOADS))
     ap.add_argument("--cold-steps", type=int, default=10,
-                    help="launches timed after a 512 MiB cache-flushing write each (0: skip)")
+                    help="launches timed after a 512 MiB cache-flushing read each (0: skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph timing of short workloads (counter runs use it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_SECONDS * 1e3,
                     help="back-to-back launches before each workload's warm-up, in ms of "
@@ -665,6 +667,9 @@ def main():
                          "5 times: the known-size kernel that calibrates HBM byte counters")
     args = ap.parse_args()
     set_settle(args.settle_ms * 1e-3)
+    if args.no_graph:
+        global GRAPH_BELOW_S
+        GRAPH_BELOW_S = 0.0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library "
               "has no multi-GPU path.", file=sys.stderr)
