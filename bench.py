@@ -7,7 +7,7 @@ A step is one GEMM call.  The headline is bf16 C = A*B at M = N = K = 4096
 4096^3, the ragged bf16 shapes, bf16 2048^3 and 2560^3 on the medium-grid
 tiles, fp32 4096^3, fp8 block-scaled 8192^3, fp16 256^3, the 4096^3 bf16
 product with a fused bias + relu epilogue and with a fused residual add, the
-MFMA-only ceiling of the headline kernel, the seven rungs of the optimisation
+MFMA-only ceiling of the headline kernel, the nine rungs of the optimisation
 ladder on fp16 4096^3, two 3x3 convolution layers through im2col + GEMM and the
 im2col pack alone, and the FP8 block quantiser on the fp8 workload's 8192 x 8192
 operand) are measured in the same run and listed under "workloads".
@@ -559,7 +559,9 @@ WORKLOADS = [
                    4096, 4096, 4096, 2, r, max_steps=5 if r <= 2 else None)
     for r, name in enumerate(("naive", "64x64 LDS tiles", "register tiles, conflict-free LDS",
                               "MFMA, one LDS stage", "MFMA + double buffer",
-                              "MFMA + double buffer + swizzle", "library kernel"))
+                              "MFMA + double buffer + swizzle", "library kernel",
+                              "MFMA, one LDS stage, one workgroup per CU",
+                              "MFMA + double buffer, one workgroup per CU"))
 ] + [
     ConvWorkload("conv_56x64", "bf16 3x3 conv 32x56x56x64 -> 64 (im2col + GEMM, bias + relu)",
                  32, 56, 64, 64, 8),

@@ -61,7 +61,8 @@ class Conv2dShape(ctypes.Structure):
                 ("n", "h", "w", "c_in", "c_out", "kh", "kw", "stride_h", "stride_w", "pad_h",
                  "pad_w", "dil_h", "dil_w")]
 LADDER_RUNGS = {"naive": 0, "lds_tiled": 1, "register_tiled": 2, "mfma": 3,
-                "mfma_double_buffer": 4, "mfma_swizzle": 5, "library": 6}   # enum gemm_ladder_rung
+                "mfma_double_buffer": 4, "mfma_swizzle": 5, "library": 6,
+                "mfma_one_wg": 7, "mfma_double_buffer_one_wg": 8}   # enum gemm_ladder_rung
 ACTIVATIONS = {"none": 0, "relu": 1}          # enum gemm_activation
 FP8_FORMATS = {"e4m3": 0, "e5m2": 1}          # enum gemm_fp8_format
 QUANT_INPUTS = {"f32": 0, "bf16": 1}          # enum gemm_quant_input

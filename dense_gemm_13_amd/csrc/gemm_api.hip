@@ -404,7 +404,8 @@ extern "C" int gemm_h16_ladder(int rung, int is_bf16, const void *A, const void 
                                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                                int64_t ldc, hipStream_t stream)
 {
-    if (rung < GEMM_LADDER_NAIVE || rung > GEMM_LADDER_LIBRARY) return GEMM_ERR_ARG;
+    if (rung < GEMM_LADDER_NAIVE || rung > GEMM_LADDER_MFMA_DOUBLE_BUFFER_ONE_WG)
+        return GEMM_ERR_ARG;
     if (is_bf16 != 0 && is_bf16 != 1) return GEMM_ERR_ARG;
     if (rung == GEMM_LADDER_LIBRARY)
         return h16_entry(is_bf16 == 1, A, B, C, M, N, K, lda, ldb, ldc, nullptr, stream);

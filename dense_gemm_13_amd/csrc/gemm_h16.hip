@@ -281,6 +281,12 @@ hipError_t launch_typed(int config, const Problem &p)
 // Rungs of the measured optimisation ladder that use this kernel: 128 x 128
 // tiles of 4 waves, MFMA; rung 3 plain LDS, one stage; rung 4 with the two-stage
 // ring; rung 5 with the ring and the swizzle (the library's own 128 x 128 kernel).
+// Rungs 7 and 8 are rungs 3 and 4 launched with LADDER_RESERVE_LDS bytes of LDS
+// reserved (and unused) per workgroup, so that at most one workgroup fits on a
+// CU: with several resident workgroups, one workgroup's loads already overlap
+// another's MFMAs, which hides what the two-stage ring adds.
+constexpr unsigned LADDER_RESERVE_LDS = 80 * 1024;
+
 template <bool IS_BF16>
 hipError_t ladder_typed(int rung, const Problem &p)
 {
@@ -294,14 +300,24 @@ hipError_t ladder_typed(int rung, const Problem &p)
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const Epilogue none{1.f, 0.f, nullptr, 0};
-#define LADDER_LAUNCH(DB, SW)                                                                      \
-    hipLaunchKernelGGL((h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, false, DB, SW>), grid, block,     \
-                       0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, \
-                       group_m, none)
+#define LADDER_LAUNCH(DB, SW, LDS)                                                                 \
+    do {                                                                                           \
+        auto *kern = h16_gemm_kernel<IS_BF16, BM, BN, WM, WN, false, DB, SW>;                       \
+        if ((LDS) > 0) {                                                                           \
+            const hipError_t e = hipFuncSetAttribute(                                              \
+                reinterpret_cast<const void *>(kern),                                              \
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(LDS));                           \
+            if (e != hipSuccess) return e;                                                         \
+        }                                                                                          \
+        hipLaunchKernelGGL(kern, grid, block, (LDS), p.stream, A, B, C, p.M, p.N, p.K, p.lda,      \
+                           p.ldb, p.ldc, tiles_m, tiles_n, group_m, none);                         \
+    } while (0)
     switch (rung) {
-    case 3: LADDER_LAUNCH(false, false); break;
-    case 4: LADDER_LAUNCH(true, false); break;
-    case 5: LADDER_LAUNCH(true, true); break;
+    case 3: LADDER_LAUNCH(false, false, 0u); break;
+    case 4: LADDER_LAUNCH(true, false, 0u); break;
+    case 5: LADDER_LAUNCH(true, true, 0u); break;
+    case 7: LADDER_LAUNCH(false, false, LADDER_RESERVE_LDS); break;
+    case 8: LADDER_LAUNCH(true, false, LADDER_RESERVE_LDS); break;
     default: return hipErrorInvalidValue;
     }
 #undef LADDER_LAUNCH

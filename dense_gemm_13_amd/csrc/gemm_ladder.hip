@@ -14,7 +14,8 @@
 // Rungs 0-2 live here and run on the vector ALUs (fp32 FMAs on fp16/bf16
 // values, fp32 accumulation).  Rungs 3-5 are the library's 128 x 128 MFMA
 // kernel with its two-stage ring and its swizzle switched off and on
-// (gemm_h16.hip); rung 6 is the library's own dispatch.  Also here: the
+// (gemm_h16.hip); rung 6 is the library's own dispatch; rungs 7-8 repeat rungs
+// 3-4 with one workgroup per CU.  Also here: the
 // MFMA-only ceiling, which issues the large-tile kernel's MFMA sequence with
 // register-resident operands and no memory traffic, i.e. what the matrix cores
 // sustain on these operand values at the clock the chip holds under that load.
@@ -59,42 +60,12 @@ ladder_naive_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__
 // Both tiled VALU rungs: 64 x 64 tiles of C, K in steps of 16, 256 threads.
 constexpr int LT = 64, LBK = 16;
 
-// Guarded global -> LDS copy of one K step: A (64 x 16) and B (16 x 64), 4
-// consecutive elements per thread each, zero outside the matrix.  A is written
-// as rows of k (TRANS_A false) or transposed into rows of m with `a_pad`
-// elements of padding per row (TRANS_A true).
-template <bool TRANS_A, int A_LD>
-__device__ __forceinline__ void ladder_load_tile(const uint16_t *__restrict__ A,
-                                                 const uint16_t *__restrict__ B, int M, int N,
-                                                 int K, int64_t lda, int64_t ldb, int m0, int n0,
-                                                 int k0, uint16_t *As, uint16_t *Bs)
-{
-    const int t = threadIdx.x;
-    {   // A: thread t -> row t / 4, k 4*(t % 4) .. +3
-        const int r = t >> 2, c = 4 * (t & 3);
-        const int gm = m0 + r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int gk = k0 + c + e;
-            const uint16_t v = gm < M && gk < K ? A[(int64_t)gm * lda + gk] : 0;
-            if (TRANS_A) As[(c + e) * A_LD + r] = v;
-            else As[r * LBK + c + e] = v;
-        }
-    }
-    {   // B: thread t -> row k t / 16, columns 4*(t % 16) .. +3
-        const int r = t >> 4, c = 4 * (t & 15);
-        const int gk = k0 + r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int gn = n0 + c + e;
-            Bs[r * LT + c + e] = gk < K && gn < N ? B[(int64_t)gk * ldb + gn] : 0;
-        }
-    }
-}
-
-// ---- rung 1: 64 x 64 tiles staged in LDS.  Thread (ty, tx) of the 16 x 16
-// block owns entries (ty + 16i, tx + 16j), i, j < 4, and reads every operand
-// it multiplies from LDS.
+// ---- rung 1: 64 x 64 tiles staged in LDS as they are in memory (16-bit).
+// Thread (ty, tx) of the 16 x 16 block owns entries (ty + 16i, tx + 16j), i,
+// j < 4, and each of its multiply-adds reads both operands from LDS: every
+// entry runs its own loop over the step's k, so no operand fetched for one
+// entry is reused for another.  That per-entry LDS traffic is what the register
+// caching of the next rung removes (the pages put it at 4-8x fewer LDS reads).
 template <bool IS_BF16>
 __global__ void __launch_bounds__(256)
 ladder_lds_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -102,19 +73,37 @@ ladder_lds_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
                   int64_t ldc)
 {
     __shared__ uint16_t As[LT * LBK], Bs[LBK * LT];
-    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
     const int m0 = blockIdx.y * LT, n0 = blockIdx.x * LT;
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += LBK) {
-        ladder_load_tile<false, LBK>(A, B, M, N, K, lda, ldb, m0, n0, k0, As, Bs);
+        {   // A: thread t -> row t / 4, k 4*(t % 4) .. +3; B: row k t / 16, columns 4*(t % 16) ..
+            const int r = t >> 2, c = 4 * (t & 3), gm = m0 + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gk = k0 + c + e;
+                As[r * LBK + c + e] = gm < M && gk < K ? A[(int64_t)gm * lda + gk] : 0;
+            }
+            const int rb = t >> 4, cb = 4 * (t & 15), gk = k0 + rb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gn = n0 + cb + e;
+                Bs[rb * LT + cb + e] = gk < K && gn < N ? B[(int64_t)gk * ldb + gn] : 0;
+            }
+        }
         __syncthreads();
-        for (int k = 0; k < LBK; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = fmaf(h2f<IS_BF16>(As[(ty + 16 * i) * LBK + k]),
-                                     h2f<IS_BF16>(Bs[k * LT + tx + 16 * j]), acc[i][j]);
+            for (int j = 0; j < 4; ++j) {
+                const uint16_t *ar = As + (ty + 16 * i) * LBK;
+                const uint16_t *bc = Bs + tx + 16 * j;
+                float v = acc[i][j];
+#pragma unroll 1
+                for (int k = 0; k < LBK; ++k)
+                    v = fmaf(h2f<IS_BF16>(ar[k]), h2f<IS_BF16>(bc[k * LT]), v);
+                acc[i][j] = v;
+            }
         __syncthreads();
     }
 #pragma unroll
@@ -127,10 +116,12 @@ ladder_lds_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
 }
 
 // ---- rung 2: register caching and bank-conflict avoidance.  Thread (ty, tx)
-// owns the contiguous 4 x 4 block at rows 4ty, columns 4tx.  A is held in LDS
-// transposed (rows of m, padded by 4 elements so the transposing writes of a
-// wave spread over the banks), so each k gives the thread its 4 A values and
-// its 4 B values as two 8-byte reads; the 16 products then run from registers.
+// owns the contiguous 4 x 4 block at rows 4ty, columns 4tx.  Operands are
+// widened to fp32 once, as they are staged, and A is held transposed (rows of
+// m, padded by 4 floats, so the transposing writes of a wave cover 64 distinct
+// banks).  For each k the thread then reads its 4 A values and its 4 B values
+// with one 16-byte LDS read each and runs the 16 multiply-adds from registers:
+// 2 LDS reads per 16 products instead of rung 1's 32.
 template <bool IS_BF16>
 __global__ void __launch_bounds__(256)
 ladder_reg_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -138,24 +129,36 @@ ladder_reg_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
                   int64_t ldc)
 {
     constexpr int A_LD = LT + 4;
-    __shared__ __attribute__((aligned(16))) uint16_t As[LBK * A_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[LBK * LT];
-    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    __shared__ __attribute__((aligned(16))) float As[LBK * A_LD];
+    __shared__ __attribute__((aligned(16))) float Bs[LBK * LT];
+    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
     const int m0 = blockIdx.y * LT, n0 = blockIdx.x * LT;
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += LBK) {
-        ladder_load_tile<true, A_LD>(A, B, M, N, K, lda, ldb, m0, n0, k0, As, Bs);
+        {   // A: thread t -> row t / 4, k 4*(t % 4) .. +3, written transposed
+            const int r = t >> 2, c = 4 * (t & 3), gm = m0 + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gk = k0 + c + e;
+                As[(c + e) * A_LD + r] =
+                    gm < M && gk < K ? h2f<IS_BF16>(A[(int64_t)gm * lda + gk]) : 0.f;
+            }
+        }
+        {   // B: thread t -> row k t / 16, columns 4*(t % 16) .. +3, one 16-byte write
+            const int r = t >> 4, c = 4 * (t & 15), gk = k0 + r;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int gn = n0 + c + e;
+                v[e] = gk < K && gn < N ? h2f<IS_BF16>(B[(int64_t)gk * ldb + gn]) : 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(Bs + r * LT + c) = v;
+        }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < LBK; ++k) {
-            const u32x2 av = *reinterpret_cast<const u32x2 *>(As + k * A_LD + 4 * ty);
-            const u32x2 bv = *reinterpret_cast<const u32x2 *>(Bs + k * LT + 4 * tx);
-            float a[4], b[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[e] = h2f<IS_BF16>((uint16_t)(av[e >> 1] >> (16 * (e & 1))));
-                b[e] = h2f<IS_BF16>((uint16_t)(bv[e >> 1] >> (16 * (e & 1))));
-            }
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(As + k * A_LD + 4 * ty);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(Bs + k * LT + 4 * tx);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll

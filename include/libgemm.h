@@ -170,7 +170,10 @@ enum gemm_ladder_rung {
     GEMM_LADDER_MFMA = 3,            /* matrix cores: 128 x 128 tiles, 4 waves, one LDS stage */
     GEMM_LADDER_MFMA_DOUBLE_BUFFER = 4,  /* + two-stage LDS ring (loads overlap the MFMAs) */
     GEMM_LADDER_MFMA_SWIZZLE = 5,    /* + XOR-swizzled 16-byte LDS chunks */
-    GEMM_LADDER_LIBRARY = 6          /* the library's own dispatch (gemm_f16 / gemm_bf16) */
+    GEMM_LADDER_LIBRARY = 6,         /* the library's own dispatch (gemm_f16 / gemm_bf16) */
+    GEMM_LADDER_MFMA_ONE_WG = 7,     /* rung 3 with LDS reserved so that one workgroup runs per CU */
+    GEMM_LADDER_MFMA_DOUBLE_BUFFER_ONE_WG = 8  /* rung 4, likewise: the ring's overlap is no longer
+                                                  hidden by other resident workgroups */
 };
 
 /* The optimisation ladder, for measurement: the same product as gemm_f16
@@ -180,7 +183,9 @@ enum gemm_ladder_rung {
  * conflicts avoided; matrix-core instructions; double buffering; swizzled
  * layout), with the kernel design of sections 3.1-3.2 for the tiled rungs and
  * the last steps of "[CUDA 优化实战] hgemm - 超越 cuBLAS" for the top rung (the
- * library's LDS-direct, coalesced-store kernel).  Rungs 0-2 run on the vector
+ * library's LDS-direct, coalesced-store kernel).  Rungs 7 and 8 repeat rungs 3
+ * and 4 at one workgroup per CU, where double buffering is not hidden by other
+ * resident workgroups.  Rungs 0-2 run on the vector
  * ALUs (fp32 FMAs, k ascending); rungs 3-6 on the matrix cores.  Every rung
  * takes every shape and layout gemm_f16 takes, except that rungs 0-2 allow at
  * most 65535 grid rows (M <= 1048560 for rung 0, M <= 4194240 for rungs 1-2;

@@ -166,7 +166,7 @@ def test_ladder_and_ceiling_argument_errors():
         return lad(rung, bf, a, B, c, M, N, K, K if lda is None else lda, N, N, None)
 
     assert L(rung=-1) == -8
-    assert L(rung=7) == -8
+    assert L(rung=9) == -8
     assert L(bf=2) == -8
     assert L(M=-1) == -2
     assert L(lda=3) == -3

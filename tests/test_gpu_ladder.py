@@ -18,7 +18,7 @@ from gpu_helpers import TOL, c_bits, reference, say, to_device
 
 pytestmark = pytest.mark.gpu
 
-RUNGS = range(7)
+RUNGS = range(9)
 
 
 def run_ladder(rung, dtype, ops, M, N, K, lda=None, ldb=None, ldc=None, offset=0):
