@@ -20,6 +20,7 @@ host's per-call launch cost bounds them otherwise.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads headline|all]
                     [--settle-ms MS] [--cold-steps N] [--no-cpu-baseline] [--no-graph]
+                    [--no-loop-fit]
 
 Prints ONE JSON line.  Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -593,6 +594,65 @@ ORACLE_CASES = (
 )
 
 
+def loop_fit(rounds: int = 2, settle: int = 300, launches: int = 200) -> dict:
+    """Launch time against K at M = N = 4096 for the headline kernel and for the
+    MFMA-only ceiling: each at K = 4096 and 8192, alternated, `settle` launches
+    then the mean of `launches` back-to-back ones, medians over `rounds`.  The
+    line through the two points splits a launch into a fixed part (prologue,
+    epilogue, launch) and a per-K loop rate, so the two kernels' loops can be
+    compared without their different fixed costs."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_13_amd as dg
+    import gemm_inputs as gi
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream(dev)
+    s = ctypes.c_void_p(st.cuda_stream)
+    M = N = 4096
+    bufs, calls = [], {}
+    for K in (4096, 8192):
+        ops = gi.operands("bf16", M, N, K, 2)
+        A = torch.from_numpy(ops["A"].view(np.int16)).view(torch.bfloat16).to(dev)
+        B = torch.from_numpy(ops["B"].view(np.int16)).view(torch.bfloat16).to(dev)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        bufs += [A, B, C]
+        a, b, c = A.data_ptr(), B.data_ptr(), C.data_ptr()
+        calls[("gemm", K)] = (lambda a=a, b=b, c=c, K=K:
+                              dg.lib.gemm_bf16(a, b, c, M, N, K, K, N, N, s))
+        calls[("ceiling", K)] = (lambda a=a, b=b, c=c, K=K:
+                                 dg.lib.gemm_h16_mfma_ceiling(1, a, b, c, M, N, K, K, N, N, s))
+    times = {key: [] for key in calls}
+    for _ in range(rounds):
+        for key, f in calls.items():
+            if f() != 0:
+                raise RuntimeError(f"loop fit: {key} returned an error")
+            for _ in range(settle):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(launches):
+                f()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times[key].append(e0.elapsed_time(e1) * 1e3 / launches)
+    del bufs
+    torch.cuda.empty_cache()
+    out = {"method": f"K = 4096 and 8192 at M = N = 4096, {settle} launches to settle then the "
+                     f"mean of {launches}, alternated, median of {rounds} rounds"}
+    for kind in ("gemm", "ceiling"):
+        t1 = float(np.median(times[(kind, 4096)]))
+        t2 = float(np.median(times[(kind, 8192)]))
+        slope = t2 - t1
+        out[kind] = {"k4096_us": round(t1, 2), "k8192_us": round(t2, 2),
+                     "us_per_4096_of_k": round(slope, 2), "intercept_us": round(t1 - slope, 2),
+                     "loop_tflops": round(2 * M * N * 4096 / (slope * 1e-6) / 1e12, 1)}
+    out["gemm_loop_frac_of_ceiling_loop"] = round(out["ceiling"]["us_per_4096_of_k"]
+                                                  / out["gemm"]["us_per_4096_of_k"], 4)
+    out["ceiling_loop_frac_of_peak"] = round(out["ceiling"]["loop_tflops"] / PEAK_TFLOPS["bf16"], 4)
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -658,6 +718,8 @@ def main():
                          + ",".join(w.key for w in WORKLOADS))
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="launches timed after a 512 MiB cache-flushing read each (0: skip)")
+    ap.add_argument("--no-loop-fit", action="store_true",
+                    help="skip the K = 4096 / 8192 fit of the headline kernel and the ceiling")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph timing of short workloads (counter runs use it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -764,6 +826,18 @@ def main():
         "workloads": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
                       for r in results],
     }
+    if ceiling is not None and not args.no_loop_fit:
+        print("[bench] loop fit: bf16 4096 x 4096 x {4096, 8192}, GEMM and MFMA-only ceiling",
+              file=sys.stderr, flush=True)
+        out["loop_fit"] = loop_fit()
+        lf = out["loop_fit"]
+        print(f"[bench] loop fit: GEMM {lf['gemm']['intercept_us']} us + "
+              f"{lf['gemm']['us_per_4096_of_k']} us per 4096 of K ({lf['gemm']['loop_tflops']} "
+              f"TFLOP/s in the loop); ceiling {lf['ceiling']['intercept_us']} us + "
+              f"{lf['ceiling']['us_per_4096_of_k']} us ({lf['ceiling']['loop_tflops']} TFLOP/s, "
+              f"{100 * lf['ceiling_loop_frac_of_peak']:.1f}% of peak); GEMM loop at "
+              f"{lf['gemm_loop_frac_of_ceiling_loop']:.3f} of the ceiling's",
+              file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()
