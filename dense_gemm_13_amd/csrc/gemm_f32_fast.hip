@@ -86,7 +86,7 @@ __device__ __forceinline__ void s_unroll(F &&f)
 //     with zero fill past K, M and N; steps 1, 2, ... load blocks 0, 1, ...
 //     LDS-direct, whole blocks that never touch B's last row;
 //   * A rows past M are clamped to row M-1 and B column chunks starting past N
-//     to the chunk at N-4 (their products only reach C entries that are not
+//     to the last whole chunk at a multiple of 4 columns (their products only reach C entries that are not
 //     stored; a chunk straddling N reads a few floats past N inside a row that
 //     is not B's last);
 //   * whole turns of the ring are followed by the remaining steps, and C
@@ -130,7 +130,7 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         int row, chunk;
         lds::f32_b_dma(wave * SB_BLK + j, lane, row, chunk);
         int col = 4 * chunk;
-        if (GEN) col = n0 + col >= N ? N - 4 : n0 + col;
+        if (GEN) col = n0 + col >= N ? ((N - 4) & ~3) : n0 + col;
         b_off[j] = (uint32_t)(row * ldb + col) * 4u;
     }
     auto a_tile = [&](int tile_m) {
@@ -423,7 +423,7 @@ bool f32_fast_eligible(const Problem &p)
 }
 
 // The guarded instantiation: any M, N >= 4 (a clamped column chunk starts at
-// N - 4), two K blocks at least, and per-lane 32-bit byte offsets that fit.
+// N - 4 rounded down to a multiple of 4), two K blocks at least, and per-lane 32-bit byte offsets that fit.
 bool f32_general_eligible(const Problem &p)
 {
     return p.M >= 1 && p.N >= 4 && p.K > SBK && p.lda < (1 << 22) &&

@@ -23,8 +23,8 @@
 // to the wave's running total.
 //
 // GEN = true takes any M, N >= 4, K >= 1 and any leading dimensions: A rows past
-// M are clamped to row M-1 and B column chunks starting past N to the chunk at
-// N-4 (their products only reach C entries that are not stored; a chunk
+// M are clamped to row M-1 and B column chunks starting past N to the last whole
+// chunk at a multiple of 4 columns (their products only reach C entries that are not stored; a chunk
 // straddling N reads a few floats past N inside a row that is not B's last);
 // the last K block, possibly partial, is loaded through registers with zero
 // fill by the wave whose turn it would be, so no LDS-direct load touches B's
@@ -121,7 +121,7 @@ f32_narrow_kernel(const float *__restrict__ A, const float *__restrict__ B, floa
     for (int j = 0; j < FB_BLK; ++j) {
         const int row = 4 * j + (lane >> 4);
         int col = 4 * ((lane & 15) ^ swz_fb(row));
-        if (GEN) col = n0 + col >= N ? N - 4 : n0 + col;
+        if (GEN) col = n0 + col >= N ? ((N - 4) & ~3) : n0 + col;
         b_off_g[j] = (uint32_t)(row * ldb + col) * 4u;
     }
     const char *a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
@@ -344,7 +344,7 @@ static bool f32_narrow_whole(const Problem &p, int tbm)
 }
 
 // The guarded instantiation: any M, N >= 4 (a clamped column chunk starts at
-// N-4), any K >= 1, any leading dimensions with 32-bit per-lane byte offsets.
+// N-4 rounded down to a multiple of 4), any K >= 1, any leading dimensions with 32-bit per-lane byte offsets.
 bool f32_narrow_general_eligible(const Problem &p)
 {
     return p.M >= 1 && p.N >= 4 && p.K >= 1 && p.lda < (1 << 24) &&

@@ -150,7 +150,7 @@ __device__ __forceinline__ void q_unroll(F &&f)
 //     load blocks 0, 1, ... LDS-direct, all of them whole blocks that never
 //     touch B's last row;
 //   * A rows past M are clamped to row M-1 and B column chunks starting past N
-//     to the chunk at N-16 (their products only reach C entries that are not
+//     to the last whole chunk at a multiple of 16 columns (their products only reach C entries that are not
 //     stored; a chunk straddling N reads a few bytes past N inside a row that is
 //     not B's last), scale rows and columns past the grids to the last ones;
 //   * after the whole turns of the ring the remaining steps run once, guarded;
@@ -202,7 +202,7 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         int row, chunk;
         lds::fp8_b_dma<QBN>(wave * QB_BLK + j, lane, row, chunk);
         int col = 16 * chunk;
-        if (GEN) col = n0 + col >= N ? N - 16 : n0 + col;
+        if (GEN) col = n0 + col >= N ? ((N - 16) & ~15) : n0 + col;
         b_off[j] = (uint32_t)(row * ldb + col);
     }
     const uint8_t *a_base = A + (int64_t)m0 * lda;
@@ -533,13 +533,26 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
             *reinterpret_cast<u32x4 *>(dst) = v;
         } else {
             const int gm = m0 + wm0 + row, gn = n0 + wn0 + 8 * cl;
-            if (gm < M) {
-                if (gn + 8 <= N) {
-                    *reinterpret_cast<u32x4 *>(dst) = v;
-                } else {
+            if (gm < M && gn + 8 <= N) *reinterpret_cast<u32x4 *>(dst) = v;
+            // (a chunk straddling N is stored below; chunks past N are not)
+        }
+    }
+    if constexpr (GEN) {
+        // The chunk of each row that straddles N, with every lane on a row of
+        // its own rather than one lane in 8 active per row group of the loop.
+        const int wcols = N - (n0 + wn0);                    // wave-uniform
+        if (wcols > 0 && wcols < QWTN && (wcols & 7) != 0) {
+            const int cs = wcols >> 3, cnt = wcols & 7;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gn + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            for (int r0 = 0; r0 < QWTM; r0 += 64) {
+                const int row = r0 + lane;
+                if (row < QWTM && m0 + wm0 + row < M) {
+                    u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * QWTN + lds::fp8_epi_read(row, cs));
+                    if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+                    uint16_t *dst = cbase + (int64_t)row * ldc + 8 * cs;
+#pragma unroll
+                    for (int e = 0; e < 7; ++e)
+                        if (e < cnt) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
                 }
             }
         }
@@ -559,7 +572,7 @@ bool fp8_fast_eligible(const Problem &p) { return fp8_whole(p, 256); }
 bool fp8_fast128_eligible(const Problem &p) { return fp8_whole(p, 128); }
 
 // The guarded instantiation: any M, N >= 16 (a clamped column chunk starts at
-// N - 16), two K blocks at least, and per-lane 32-bit byte offsets that fit (256
+// N - 16 rounded down to a multiple of 16), two K blocks at least, and per-lane 32-bit byte offsets that fit (256
 // rows of A from the tile's first row; 64 rows of B plus the column).
 bool fp8_general_eligible(const Problem &p)
 {

@@ -21,7 +21,7 @@
 //
 // GEN = true takes any M, N >= 16, K >= 1 and any leading dimensions: A rows
 // past M are clamped to row M-1 and B column chunks starting past N to the
-// chunk at N-16 (their products only reach C entries that are not stored; a
+// last whole chunk at a multiple of 16 columns (their products only reach C entries that are not stored; a
 // chunk straddling N reads a few bytes past N inside a row that is not B's
 // last); the last K block, possibly partial, is loaded through registers with
 // zero fill by the wave whose turn it would be, so no LDS-direct load touches
@@ -135,7 +135,7 @@ fp8_narrow_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     for (int j = 0; j < GB_BLK; ++j) {
         const int row = 16 * j + (lane >> 2);
         int col = 16 * ((lane & 3) ^ gswz_b(row));
-        if (GEN) col = n0 + col >= N ? N - 16 : n0 + col;
+        if (GEN) col = n0 + col >= N ? ((N - 16) & ~15) : n0 + col;
         b_off_g[j] = (uint32_t)(row * ldb + col);
     }
     const uint8_t *a_base = A + (int64_t)m0 * lda;
@@ -374,7 +374,7 @@ static bool fp8_narrow_whole(const Problem &p, int tbm)
 }
 
 // The guarded instantiation: any M, N >= 16 (a clamped column chunk starts at
-// N - 16), any K >= 1 up to the staged scale row, any leading dimensions with
+// N - 16 rounded down to a multiple of 16), any K >= 1 up to the staged scale row, any leading dimensions with
 // 32-bit per-lane offsets.
 bool fp8_narrow_general_eligible(const Problem &p)
 {

@@ -139,8 +139,10 @@ __device__ __forceinline__ uint16_t *b_ring_array(int idx)
 //     registers with zero fill, so every LDS-direct block is a full one that
 //     never touches B's last row;
 //   * A rows past M are clamped to row M-1 and B column chunks starting past N
-//     to the chunk at N-8 (their products only reach C entries that are not
-//     stored); a chunk straddling N reads a few elements past N inside a row
+//     to the last whole chunk at a multiple of 8 columns (their products only
+//     reach C entries that are not stored; the clamped loads stay 16-byte
+//     aligned when B's rows are); a chunk straddling N reads a few elements
+//     past N inside a row
 //     that is not B's last, i.e. inside the operand;
 //   * steps are guarded when the number of K steps is not a multiple of the
 //     ring depth, and C stores are masked to the M x N window.
@@ -203,7 +205,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         int row, chunk;
         lds::h16_b_dma<FBN>(wave * B_BLK + j, lane, row, chunk);
         int col = 8 * chunk;
-        if (GEN) col = n0 + col >= N ? N - 8 : n0 + col;
+        if (GEN) col = n0 + col >= N ? ((N - 8) & ~7) : n0 + col;
         b_off_g[j] = (uint32_t)(row * ldb + col) * 2u;
     }
     const char *a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
@@ -583,10 +585,32 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
                     else
                         *reinterpret_cast<u32x4 *>(dst) = v;
-                } else {
+                }
+                // (a chunk straddling N is stored below; chunks past N are not)
+            }
+        }
+    }
+    if constexpr (GEN) {
+        // The chunk of each row that straddles N, if this wave's columns hold
+        // one: taken out of the loop above, where its element-wise stores ran
+        // with one lane in 16 active in every iteration, and stored here with
+        // every lane on a row of its own (measured: 4096 x 4095 x 4096 cost
+        // 6 us more than 4096 x 4088 x 4096 that way).
+        static_assert(FWTM % 64 == 0, "one row per lane");
+        const int wcols = N - (n0 + wn0);                    // wave-uniform
+        if (wcols > 0 && wcols < FWTN && (wcols & 7) != 0) {
+            const int cs = wcols >> 3, cnt = wcols & 7;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gn + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            for (int r0 = 0; r0 < FWTM; r0 += 64) {
+                const int row = r0 + lane;
+                if (m0 + wm0 + row < M) {
+                    const uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
+                    u32x4 v = *reinterpret_cast<const u32x4 *>(buf + lds::h16_epi_read<CPRC>(row, cs));
+                    if (lds::h16_epi_swap(row)) v = u32x4{v[2], v[3], v[0], v[1]};
+                    uint16_t *dst = cbase + (int64_t)row * ldc + 8 * cs;
+#pragma unroll
+                    for (int e = 0; e < 7; ++e)
+                        if (e < cnt) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
                 }
             }
         }

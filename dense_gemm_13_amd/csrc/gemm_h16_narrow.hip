@@ -16,8 +16,8 @@
 //
 // GEN = true takes any M, N >= 8, K >= 1 and any leading dimensions (used for
 // the few rows left over below a grid of 256 x 256 tiles): A rows past M are
-// clamped to row M-1 and B column chunks starting past N to the chunk at N-8
-// (their products only reach C entries that are not stored); the last K block,
+// clamped to row M-1 and B column chunks starting past N to the last whole
+// chunk at a multiple of 8 columns (their products only reach C entries that are not stored); the last K block,
 // possibly partial, is loaded through registers with zero fill by the wave whose
 // turn it would be, so no LDS-direct load touches B's last row; stores are
 // masked to the M x N window.  The hardware runs in unaligned-access mode, so
@@ -121,7 +121,7 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
     for (int j = 0; j < NB_BLK; ++j) {
         const int row = 8 * j + (lane >> 3);
         int col = 8 * ((lane & 7) ^ swz_nb(row));
-        if (GEN) col = n0 + col >= N ? N - 8 : n0 + col;
+        if (GEN) col = n0 + col >= N ? ((N - 8) & ~7) : n0 + col;
         b_off_g[j] = (uint32_t)(row * ldb + col) * 2u;
     }
     const char *a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * lda);
@@ -354,7 +354,7 @@ bool h16_narrow_eligible(const Problem &p) { return narrow_whole(p, 32); }
 bool h16_narrow64_eligible(const Problem &p) { return narrow_whole(p, 64); }
 
 // The guarded instantiation: any M, N >= 8 (a clamped column chunk starts at
-// N-8), any K >= 1, any leading dimensions with 32-bit per-lane offsets.
+// N-8 rounded down to a multiple of 8), any K >= 1, any leading dimensions with 32-bit per-lane offsets.
 bool h16_narrow_general_eligible(const Problem &p)
 {
     return p.M >= 1 && p.N >= 8 && p.K >= 1 && p.lda < (1 << 24) && p.ldb < (1 << 24) &&
