@@ -167,7 +167,8 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             (forced != H16_FAST_128 || h16_fast128_eligible(p)) &&
             (forced != H16_GEN_128 || h16_general_eligible(p)) &&
             (forced != H16_FAST_128x256 || h16_fast128x256_eligible(p)) &&
-            (forced != H16_GEN_128x256 || h16_general_eligible(p)))
+            (forced != H16_GEN_128x256 || h16_general_eligible(p)) &&
+            (forced != H16_FEWROWS || h16_fewrows_eligible(p)))
             return to_status(h16_launch(is_bf16, forced, p));
     }
     // The large-tile kernel with 256 x 256 tiles, when their grid fills more than
@@ -207,11 +208,16 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             bottom.M = tail;
             bottom.A = static_cast<const uint16_t *>(p.A) + (int64_t)top.M * p.lda;
             bottom.C = static_cast<uint16_t *>(p.C) + (int64_t)top.M * p.ldc;
-            if (h16_narrow_general_eligible(bottom)) {
+            // One row: B streamed by every CU (1 x 4095 x 4100: 13.5 us against
+            // 17.6 on the narrow kernel's 64 workgroups); more: the narrow kernel.
+            const int tail_cfg = h16_fewrows_preferred(bottom)         ? H16_FEWROWS
+                                 : h16_narrow_general_eligible(bottom) ? H16_NARROW_GEN
+                                                                       : -1;
+            if (tail_cfg >= 0) {
                 st = to_status(h16_launch(
                     is_bf16, h16_fast_eligible(top) ? H16_FAST_256x256 : H16_GEN_256x256, top));
                 if (st != GEMM_OK) return st;
-                return to_status(h16_launch(is_bf16, H16_NARROW_GEN, bottom));
+                return to_status(h16_launch(is_bf16, tail_cfg, bottom));
             }
         }
         return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
@@ -224,6 +230,14 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
     // 512 x 2048 x 2048 9.1 against 13.3) or where 128 x 128 tiles would be fewer
     // than 64 (3000 x 200 x 3000: 22.9 against 34.4); its guarded form otherwise
     // ties or loses (2048 x 512 x 1000: 11.1 against 9.9).
+    // At most 32 rows (one row strip of the narrow kernel) with a long K: the
+    // narrow kernel, or for one row the few-row kernel where it is faster; the
+    // 64 x 64 tiles below would walk all of K in each workgroup
+    // (1 x 8192 x 8192: 27.2 us against 80.1; 1 x 16384 x 12288: 79 against 169).
+    if (p.M <= 32 && p.K >= 256) {
+        if (h16_fewrows_preferred(p)) return to_status(h16_launch(is_bf16, H16_FEWROWS, p));
+        if (h16_narrow_general_eligible(p)) return narrow();
+    }
     const int64_t small_tiles = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
     const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
     const bool narrow_whole = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64) > cus && p.M >= 64

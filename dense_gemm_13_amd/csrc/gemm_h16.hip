@@ -362,6 +362,7 @@ hipError_t h16_launch(bool is_bf16, int config, const Problem &p)
     if (config == H16_NARROW64) return h16_narrow64_launch(is_bf16, p);
     if (config == H16_NARROW64_GEN) return h16_narrow64_general_launch(is_bf16, p);
     if (config == H16_ROWS) return rows_launch(is_bf16 ? OUT_BF16 : OUT_F16, p);
+    if (config == H16_FEWROWS) return h16_fewrows_launch(is_bf16, p);
     if (config == H16_FAST_128) return h16_fast128_launch(is_bf16, p);
     if (config == H16_GEN_128) return h16_general128_launch(is_bf16, p);
     if (config == H16_FAST_128x256) return h16_fast128x256_launch(is_bf16, p);

@@ -326,26 +326,41 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             if constexpr (ISSUE) issue(nas_dma, nbs_dma, next_kt);
         }
         mfmas(cur);
-        if constexpr (!LAST) {
-            cur = nxt;
+        constexpr int MF = FFM * FFN;                    // MFMAs per sub-step
+        if constexpr (!LAST) cur = nxt;
+        if constexpr (!LAST && ISSUE && MF >= DS && MF >= NBLK) {
+            // One fragment read after each of the first DS MFMAs and the NBLK
+            // loads spread evenly over all of them: issued in a burst, the loads
+            // of the four waves overfill the texture unit's address queue and the
+            // waves stall on them (SQ_VMEM_TA_CMD_FIFO_FULL 4.7M -> 1.0M,
+            // 4096^3 104.5 -> 103.0 us, 4097 x 4095 x 4100 139.0 -> 135.4 us).
 #pragma unroll
-            for (int x = 0; x < DS / 2; ++x) {
+            for (int x = 0; x < MF; ++x) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (x < DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if ((x * NBLK) % MF < NBLK) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
-        }
-        if constexpr (ISSUE && FFM * FFN >= DS / 2 + NBLK) {
+        } else {
+            if constexpr (!LAST) {
 #pragma unroll
-            for (int x = 0; x < NBLK; ++x) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                for (int x = 0; x < DS / 2; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2 - NBLK, 0);
-        } else if constexpr (ISSUE) {
-            // (64 x 64 sub-tiles: too few MFMAs to pair each load with one.)
-            static_assert(FFM * FFN > DS / 2, "MFMAs to interleave with");
-            __builtin_amdgcn_sched_group_barrier(0x020, NBLK, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, FFM * FFN - DS / 2, 0);
+            if constexpr (ISSUE && MF >= DS / 2 + NBLK) {
+#pragma unroll
+                for (int x = 0; x < NBLK; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MF - DS / 2 - NBLK, 0);
+            } else if constexpr (ISSUE) {
+                // (64 x 64 sub-tiles: too few MFMAs to pair each load with one.)
+                static_assert(MF > DS / 2, "MFMAs to interleave with");
+                __builtin_amdgcn_sched_group_barrier(0x020, NBLK, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MF - DS / 2, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };

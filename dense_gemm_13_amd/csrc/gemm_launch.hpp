@@ -47,7 +47,8 @@ enum H16Config {
     H16_GEN_128 = 12,     // same kernel, guarded
     H16_FAST_128x256 = 13, // whole 128x256 tiles of the large-tile kernel, one workgroup per CU
     H16_GEN_128x256 = 14, // same kernel, guarded
-    H16_NUM_CONFIGS = 15
+    H16_FEWROWS = 15,     // at most 4 rows: B streamed through per-wave LDS rings, 16 columns per workgroup
+    H16_NUM_CONFIGS = 16
 };
 
 int h16_pick_config(int M, int N, int K);
@@ -69,6 +70,10 @@ hipError_t h16_narrow_general_launch(bool is_bf16, const Problem &p);
 bool h16_narrow64_eligible(const Problem &p);
 hipError_t h16_narrow64_launch(bool is_bf16, const Problem &p);
 hipError_t h16_narrow64_general_launch(bool is_bf16, const Problem &p);
+// At most 4 rows of A (N >= 16, the rows of A fit in 32 KiB of LDS).
+bool h16_fewrows_eligible(const Problem &p);
+bool h16_fewrows_preferred(const Problem &p);
+hipError_t h16_fewrows_launch(bool is_bf16, const Problem &p);
 // The measured optimisation ladder (fp16 or bf16): rungs 0-2 on the vector
 // ALUs, rungs 3-5 the 128 x 128 MFMA kernel with its ring / swizzle switched,
 // and the MFMA-only ceiling of the large-tile kernel.

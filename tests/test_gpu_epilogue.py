@@ -104,6 +104,8 @@ H16_CASES = [
     (12, (300, 264, 200), (203, 267, 269)),  # the same, guarded
     (13, (256, 512, 256), None),             # 128 x 256 tiles of the large-tile kernel
     (14, (300, 520, 200), (203, 523, 525)),  # the same, guarded
+    (15, (3, 200, 300), (301, 203, 205)),    # the few-row kernel (B through LDS rings)
+    (15, (1, 4095, 4100), (4100, 4095, 4095)),   # the same on the ragged workload's tail row
 ]
 
 

@@ -34,6 +34,7 @@ FAST128 = 11      # whole 128x128 tiles of the large-tile kernel, two workgroups
 GEN128 = 12       # the same kernel, guarded
 FAST128x256 = 13  # whole 128x256 tiles of the large-tile kernel, one workgroup per CU
 GEN128x256 = 14   # the same kernel, guarded
+FEWROWS = 15      # at most 4 rows: B streamed through per-wave LDS rings, 16 columns per workgroup
 
 
 @pytest.fixture(autouse=True)
@@ -501,6 +502,72 @@ def test_rows_permutation_exact(dtype):
     os.environ[var] = val
     say(f"[probe] rows {dtype} A*P")
     ops, perm = _perm_case(dtype, M, K, 18)
+    _, got = run_gemm(dtype, ops, M, K, K)
+    want = np.empty((M, K))
+    want[:, perm] = oracle.decode(ops["A"], dtype)
+    bad = np.argwhere(oracle.decode(got, OUT_DTYPE[dtype]) != want)
+    assert bad.size == 0, f"first mismatch at {bad[0]}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 16, 1), None),                      # one workgroup, K below one block: registers only
+    ((1, 4095, 4100), (4100, 4095, 4095)),   # the tail row of 4097 x 4095 x 4100
+    ((1, 4096, 4096), None),                 # whole blocks only, every wave 8 blocks
+    ((2, 100, 333), (337, 101, 103)),        # window of the last workgroup moved left, offsets
+    ((3, 4095, 517), None),                  # waves with no block, partial block
+    ((4, 130, 2048), (2051, 131, 133)),      # four rows, unaligned leading dimensions
+    ((1, 16500, 300), (301, 16501, 16503)),  # 1032 workgroups, several rounds
+    ((4, 17, 3072), (3075, 19, 21)),         # the largest K four rows fit, window straddling
+    ((1, 40, 12288), None),                  # the largest K one row fits: three turns of the ring
+    ((2, 64, 4640), (4643, 67, 69)),         # two turns, partial block
+])
+def test_fewrows_path(dtype, shape, lds):
+    """The few-row kernel (half-precision config 15): B streamed through per-wave
+    LDS rings; the partial last block through registers; the last workgroup's
+    window moved to end at N."""
+    os.environ["LIBGEMM_H16_CONFIG"] = str(FEWROWS)
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[fewrows] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 52)
+    C, got = run_gemm(dtype, ops, M, N, K, **kw)
+    if lds is not None:
+        pad = C.as_strided((M, lds[2] - N), (lds[2], 1), C.storage_offset() + N)
+        padv = oracle.decode(pad.cpu().contiguous().view(torch.int16).numpy().view(np.uint16),
+                             OUT_DTYPE[dtype])
+        assert np.isnan(padv).all(), "C written between N and ldc"
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "fewrows")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape,lds", [
+    ((1, 8192, 8192), None),                 # one row, long K: the narrow kernel
+    ((1, 4096, 4096), None),                 # one row within one turn: the few-row kernel
+    ((1, 4095, 4100), (4100, 4095, 4095)),   # the same with 2-byte-aligned rows
+    ((3, 5000, 2000), (2003, 5001, 5003)),   # three rows: the narrow kernel, guarded
+    ((32, 4100, 1000), None),                # one full row strip of the narrow kernel
+])
+def test_few_rows_dispatch(dtype, shape, lds):
+    """Products of at most 32 rows through the automatic dispatch (no override)."""
+    M, N, K = shape
+    kw = {} if lds is None else dict(lda=lds[0], ldb=lds[1], ldc=lds[2], offset=1)
+    say(f"[few rows, auto] {dtype} {M}x{N}x{K} {kw}")
+    ops = gi.operands(dtype, M, N, K, 53)
+    _, got = run_gemm(dtype, ops, M, N, K, **kw)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "few rows")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M,K", [(4, 520), (1, 4100)])
+def test_fewrows_permutation_exact(dtype, M, K):
+    """A*P on the few-row kernel must equal a column permutation of A bit for bit
+    (a row of B moved to another lane, slot or wave shows as a moved entry)."""
+    os.environ["LIBGEMM_H16_CONFIG"] = str(FEWROWS)
+    say(f"[probe] fewrows {dtype} {M}x{K} A*P")
+    ops, perm = _perm_case(dtype, M, K, 19)
     _, got = run_gemm(dtype, ops, M, K, K)
     want = np.empty((M, K))
     want[:, perm] = oracle.decode(ops["A"], dtype)
