@@ -522,23 +522,29 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             uint16_t *buf = st[row / ROWS_PER_ARR] + (row % ROWS_PER_ARR) * FWTN;
             [[maybe_unused]] const int gm = m0 + wm0 + row;
             [[maybe_unused]] const uint16_t *crow = C + (int64_t)gm * ldc;
-            // EPI, whole tiles: the prior C of the row's entries first (all
-            // loads in flight at once), then the arithmetic.  The guarded
-            // variant, short of registers, takes each group of 4 entries on its
-            // own.
-            [[maybe_unused]] float prior[EPI && !GEN && PRIOR ? FFN : 1][4][4];
+            // EPI, whole tiles: the prior C of half the row's entries first
+            // (all their loads in flight at once), then their arithmetic, then
+            // the other half (the whole row at once spilled registers in the
+            // fp16 instantiation).  The guarded variant, shorter of registers,
+            // takes each group of 4 entries on its own.
+            constexpr int JH = FFN > 1 ? FFN / 2 : 1;    // column tiles per half
+#pragma unroll
+            for (int h0 = 0; h0 < FFN; h0 += JH) {
+            [[maybe_unused]] float prior[EPI && !GEN && PRIOR ? JH : 1][4][4];
             if constexpr (EPI && !GEN && PRIOR) {
 #pragma unroll
-                for (int j = 0; j < FFN; ++j)
+                for (int jj = 0; jj < JH; ++jj)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         epilogue_prior_whole<IS_BF16 ? OUT_BF16 : OUT_F16, 4>(
-                            crow, n0 + wn0 + 32 * j + 8 * q + 4 * half, prior_vec, prior[j][q]);
+                            crow, n0 + wn0 + 32 * (h0 + jj) + 8 * q + 4 * half, prior_vec,
+                            prior[jj][q]);
             }
 #pragma unroll
-            for (int j = 0; j < FFN; ++j)
+            for (int jj = 0; jj < JH; ++jj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    const int j = h0 + jj;
                     float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                   acc[i][j][4 * q + 3]};
                     if constexpr (EPI && GEN) {
@@ -549,7 +555,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
                         for (int t = 0; t < 4; ++t) {
                             if constexpr (PRIOR)
-                                v[t] = epilogue_value(epi, v[t], ebias[j][q][t], prior[j][q][t]);
+                                v[t] = epilogue_value(epi, v[t], ebias[j][q][t], prior[jj][q][t]);
                             else
                                 v[t] = epilogue_value(epi, v[t], ebias[j][q][t]);
                             if constexpr (RELU) v[t] = epilogue_relu(v[t]);
@@ -558,6 +564,7 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                     *reinterpret_cast<u32x2 *>(buf + lds::h16_epi_write<CPRC>(row, 4 * j + q, half)) =
                         u32x2{pack2<IS_BF16>(v[0], v[1]), pack2<IS_BF16>(v[2], v[3])};
                 }
+            }
         }
     };
     if constexpr (EPI && !GEN) {

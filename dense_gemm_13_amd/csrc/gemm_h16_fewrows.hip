@@ -138,14 +138,14 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int k = tid + FR_WAVES * 64 * u;
-            av[m][u] = A[k < K ? (int64_t)m * lda + k : 0];
+            av[m][u] = k < K ? A[(int64_t)m * lda + k] : (uint16_t)0;   // (waves past K skip)
         }
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int k = tid + FR_WAVES * 64 * u;
-            if (k < kp) fr_a[m * kp + k] = k < K ? av[m][u] : (uint16_t)0;
+            if (k < kp) fr_a[m * kp + k] = av[m][u];
         }
     __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): A is in LDS
     asm volatile("s_barrier" ::: "memory");              // (no fence: B loads stay in flight)
