@@ -156,3 +156,21 @@ def test_rows_operand_B_past_2_31_entries_exact(dtype):
     _run(dtype, A, B, C, M, K)
     _check_rows(C, lambda r0, r1: A[r0:r1], sel, dtype, f"large-B rows {dtype}")
     del A, B, C
+
+
+def test_fewrows_operand_B_past_2_31_entries_exact():
+    """The few-row kernel with a B of more than 2^31 entries (K = 4096 rows of
+    540000 columns, one row of A, chosen by the automatic dispatch): its 64-bit
+    row offsets, 33750 workgroups and the window of the last one."""
+    M, K, N = 1, 4096, 540000
+    say(f"[large-B fewrows] bf16 M={M} N={N} K={K}: generating")
+    A = _device(gi.operands("bf16", M, 8, K, 506)["A"], "bf16")
+    sel = torch.from_numpy(np.random.default_rng(507).integers(0, K, N)).cuda()
+    B = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
+    B[sel, torch.arange(N, device="cuda")] = 1
+    assert B.numel() > 2 ** 31
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    say("[large-B fewrows] bf16: gpu")
+    _run("bf16", A, B, C, M, K)
+    _check_rows(C, lambda r0, r1: A[r0:r1], sel, "bf16", "large-B fewrows bf16")
+    del A, B, C
