@@ -122,9 +122,10 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
 
     // Loads: this wave's first ring slots, then the rows of the partial last
     // block of B (K % 32 rows, through registers; used by the wave whose turn
-    // that block is), then the rows of A (zero past K; FR_A_HALVES / 1024 per
-    // thread, some past kp unused).  Waiting for A waits for the slots too, which then are all
-    // ready: with K up to 32 * FR_WAVES * FR_SLOTS (4096) that is every block.
+    // that block is), then the rows of A (zero past K; up to FR_A_HALVES / 1024
+    // per thread).  Loads complete in issue order, so waiting for A waits for
+    // the first slots too; with K up to 32 * FR_WAVES * FR_SLOTS (4096) those
+    // are all of the blocks.
     fr_unroll<FR_SLOTS>([&](auto S) { issue(fr_slot<S>, S); });
     const bool tail_wave = wave == nb % FR_WAVES && nb * FR_ROWS < K;
     const int ktail = nb * FR_ROWS + r;                  // this lane's row of the partial block
