@@ -165,7 +165,6 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int A_STAGE = FBM * BK;                    // halves per stage
     constexpr int B_STAGE = BK * FBN;
     constexpr int CPR = BK / 8;                          // 16-byte chunks per A row
-    constexpr int ROWS_PER_KB = 1024 / (BK * 2);         // A rows per 1 KiB load
     constexpr int A_BLK = A_STAGE * 2 / 1024 / FNW;      // 1 KiB loads per wave per stage
     constexpr int B_BLK = B_STAGE * 2 / 1024 / FNW;
     constexpr int SUB = BK / 16;                         // MFMA K sub-steps per stage
@@ -185,8 +184,8 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // ---- per-lane sources of this wave's 1 KiB loads: a wave-uniform base
     // (this tile's first row of A / first column of B at K step kt) plus a
     // 32-bit byte offset per lane and load.
-    // A block b: lane -> row ROWS_PER_KB*b + lane/CPR, slot lane%CPR, which
-    // holds logical chunk slot ^ swz_a(row).
+    // A block b: lane -> row (1024 / (2 BK)) b + lane/CPR, slot lane%CPR,
+    // which holds logical chunk slot ^ swz_a(row) (lds::h16_a_dma).
     uint32_t a_off[A_BLK];
 #pragma unroll
     for (int j = 0; j < A_BLK; ++j) {
@@ -195,10 +194,10 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int lrow = GEN && m0 + row >= M ? M - 1 - m0 : row;
         a_off[j] = (uint32_t)(lrow * lda + 8 * chunk) * 2u;
     }
-    // B block b (BRPK rows of FBN halves: 2 rows of 512 bytes, or 4 of 256):
-    // lane -> row BRPK*b + lane/BCPR, slot lane%BCPR.  For GEN the column
-    // (including n0) is part of the per-lane offset.
-    constexpr int BCPR = FBN / 8, BRPK = 64 / BCPR;
+    // B block b (rows of FBN halves, BCPR = FBN / 8 chunks each: 2 rows of 512
+    // bytes, or 4 of 256): lane -> row (64 / BCPR) b + lane/BCPR, slot
+    // lane%BCPR (lds::h16_b_dma).  For GEN the column (including n0) is part of
+    // the per-lane offset.
     uint32_t b_off_g[B_BLK];
 #pragma unroll
     for (int j = 0; j < B_BLK; ++j) {
