@@ -222,14 +222,6 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
         }
         return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
     }
-    // Small grids: with few tiles and a long K, splitting K over the narrow
-    // kernel's waves beats walking all of K in one workgroup per tile.  Measured
-    // on MI355X (bf16): 256^3 4.1 us narrow against 5.0 on 64 x 64 tiles;
-    // 1 x 4096 x 1000 6.1 against 11.2.  Up to 256 tiles of 64 x 64 it also beats
-    // 128 x 128 tiles where its whole-tile form applies (1024^3 6.2 against 8.4,
-    // 512 x 2048 x 2048 9.1 against 13.3) or where 128 x 128 tiles would be fewer
-    // than 64 (3000 x 200 x 3000: 22.9 against 34.4); its guarded form otherwise
-    // ties or loses (2048 x 512 x 1000: 11.1 against 9.9).
     // At most 32 rows (one row strip of the narrow kernel) with a long K: the
     // narrow kernel, or for one row the few-row kernel where it is faster; the
     // 64 x 64 tiles below would walk all of K in each workgroup
@@ -238,6 +230,14 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
         if (h16_fewrows_preferred(p)) return to_status(h16_launch(is_bf16, H16_FEWROWS, p));
         if (h16_narrow_general_eligible(p)) return narrow();
     }
+    // Small grids: with few tiles and a long K, splitting K over the narrow
+    // kernel's waves beats walking all of K in one workgroup per tile.  Measured
+    // on MI355X (bf16): 256^3 4.1 us narrow against 5.0 on 64 x 64 tiles;
+    // 1 x 4096 x 1000 6.1 against 11.2.  Up to 256 tiles of 64 x 64 it also beats
+    // 128 x 128 tiles where its whole-tile form applies (1024^3 6.2 against 8.4,
+    // 512 x 2048 x 2048 9.1 against 13.3) or where 128 x 128 tiles would be fewer
+    // than 64 (3000 x 200 x 3000: 22.9 against 34.4); its guarded form otherwise
+    // ties or loses (2048 x 512 x 1000: 11.1 against 9.9).
     const int64_t small_tiles = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
     const int64_t tiles128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
     const bool narrow_whole = (int64_t)((p.M + 31) / 32) * ((p.N + 63) / 64) > cus && p.M >= 64
