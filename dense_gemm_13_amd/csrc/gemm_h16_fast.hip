@@ -61,9 +61,10 @@ __device__ __forceinline__ void dma16(const void *src, uint16_t *lds_block)
 // spends no vector instructions on 64-bit load addresses (4096^3: 103.9 ->
 // 102.4 us).  `reach` bounds the bytes a tile may touch from the base (an
 // offset past it reads zeros).  The 4th descriptor word 0x00020000 is the raw
-// 32-bit data format of gfx9.  The guarded instantiation keeps dma16: its rows
-// need not be 16-byte aligned, and buffer loads at such offsets were measured
-// to return wrong data.
+// 32-bit data format of gfx9.  The guarded instantiations use them for each
+// operand whose rows start on 4-byte boundaries and dma16 otherwise: buffer
+// LDS-direct loads at offsets that are not 4-byte aligned were measured to
+// return wrong data.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(const void *base, int reach)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, reach, 0x00020000);
@@ -151,7 +152,8 @@ __device__ __forceinline__ uint16_t *b_ring_array(int idx)
 // rounded (each lane reads the bias and, for beta != 0, the prior C of the
 // entries it holds; it never stores them itself, but the store of an entry
 // depends through LDS on the value this read produced).
-template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI, int TBM, int TBN>
+template <bool IS_BF16, int BK, int STAGES, int WM, int WN, bool GEN, bool EPI, int TBM, int TBN,
+          int BUF>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
     TBM * TBN == 128 * 128 ? 2 : WM * WN / 4, TBM * TBN == 128 * 128 ? 2 : WM * WN / 4)))
 h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -219,10 +221,24 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const char *ab = a_base + kb * a_step;
         const char *bb = b_base + kb * b_step;
         if constexpr (GEN) {
+            // Each operand through a buffer descriptor when its rows start on
+            // 4-byte boundaries (BUF bit 0: A, bit 1: B), else global loads.
+            if constexpr (BUF & 1) {
+                const __amdgpu_buffer_rsrc_t ra = h_rsrc(ab, a_reach);
 #pragma unroll
-            for (int j = 0; j < A_BLK; ++j) dma16(ab + a_off[j], as + (wave * A_BLK + j) * 512);
+                for (int j = 0; j < A_BLK; ++j) bdma16(ra, a_off[j], as + (wave * A_BLK + j) * 512);
+            } else {
 #pragma unroll
-            for (int j = 0; j < B_BLK; ++j) dma16(bb + b_off_g[j], bs + (wave * B_BLK + j) * 512);
+                for (int j = 0; j < A_BLK; ++j) dma16(ab + a_off[j], as + (wave * A_BLK + j) * 512);
+            }
+            if constexpr (BUF & 2) {
+                const __amdgpu_buffer_rsrc_t rb = h_rsrc(bb, b_reach);
+#pragma unroll
+                for (int j = 0; j < B_BLK; ++j) bdma16(rb, b_off_g[j], bs + (wave * B_BLK + j) * 512);
+            } else {
+#pragma unroll
+                for (int j = 0; j < B_BLK; ++j) dma16(bb + b_off_g[j], bs + (wave * B_BLK + j) * 512);
+            }
         } else {
             const __amdgpu_buffer_rsrc_t ra = h_rsrc(ab, a_reach), rb = h_rsrc(bb, b_reach);
 #pragma unroll
@@ -661,7 +677,7 @@ bool h16_general_eligible(const Problem &p)
            (int64_t)FAST_BK * p.ldb + p.N < (int64_t)1 << 30;
 }
 
-template <bool GEN, bool EPI, int TBM, int TBN>
+template <bool GEN, bool EPI, int TBM, int TBN, int BUF>
 static hipError_t fast_launch(bool is_bf16, const Problem &p)
 {
     const int tiles_m = (p.M + TBM - 1) / TBM, tiles_n = (p.N + TBN - 1) / TBN;
@@ -675,25 +691,48 @@ static hipError_t fast_launch(bool is_bf16, const Problem &p)
     const Epilogue epi = p.epi ? *p.epi : Epilogue{1.f, 0.f, nullptr, 0};
     if (is_bf16)
         hipLaunchKernelGGL(
-            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TBM, TBN>), grid,
+            (h16_fast_kernel<true, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TBM, TBN, BUF>), grid,
             block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
             group_m, epi);
     else
         hipLaunchKernelGGL(
-            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TBM, TBN>), grid,
+            (h16_fast_kernel<false, FAST_BK, FAST_STAGES, FAST_WM, FAST_WN, GEN, EPI, TBM, TBN, BUF>), grid,
             block, 0, p.stream, A, B, C, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n,
             group_m, epi);
     return hipGetLastError();
+}
+
+// Guarded instantiations load an operand through a buffer descriptor when its
+// rows start on 4-byte boundaries (base pointer 4-byte aligned, even leading
+// dimension); buffer LDS-direct loads at offsets that are not 4-byte aligned
+// returned wrong data.  Measured on one box: 4096 x 4000 x 4096 109.1 -> 106.6
+// us, 4000^3 107.2 -> 104.5 us with both operands; 4097 x 4095 x 4100 (A rows
+// 4-byte aligned, B rows only 2-byte aligned) 132.9 -> 131.2 us.
+template <bool GEN, bool EPI, int TBM, int TBN>
+static hipError_t fast_buf_dispatch(bool is_bf16, const Problem &p)
+{
+    if constexpr (!GEN) {
+        return fast_launch<false, EPI, TBM, TBN, 3>(is_bf16, p);
+    } else {
+        const bool a4 = ((uintptr_t)p.A & 3) == 0 && p.lda % 2 == 0;
+        const bool b4 = ((uintptr_t)p.B & 3) == 0 && p.ldb % 2 == 0;
+        switch ((a4 ? 1 : 0) | (b4 ? 2 : 0)) {
+        case 3: return fast_launch<true, EPI, TBM, TBN, 3>(is_bf16, p);
+        case 2: return fast_launch<true, EPI, TBM, TBN, 2>(is_bf16, p);
+        case 1: return fast_launch<true, EPI, TBM, TBN, 1>(is_bf16, p);
+        default: return fast_launch<true, EPI, TBM, TBN, 0>(is_bf16, p);
+        }
+    }
 }
 
 template <int TBM, int TBN>
 static hipError_t fast_dispatch(bool is_bf16, bool gen, const Problem &p)
 {
     if (gen)
-        return p.epi ? fast_launch<true, true, TBM, TBN>(is_bf16, p)
-                     : fast_launch<true, false, TBM, TBN>(is_bf16, p);
-    return p.epi ? fast_launch<false, true, TBM, TBN>(is_bf16, p)
-                 : fast_launch<false, false, TBM, TBN>(is_bf16, p);
+        return p.epi ? fast_buf_dispatch<true, true, TBM, TBN>(is_bf16, p)
+                     : fast_buf_dispatch<true, false, TBM, TBN>(is_bf16, p);
+    return p.epi ? fast_buf_dispatch<false, true, TBM, TBN>(is_bf16, p)
+                 : fast_buf_dispatch<false, false, TBM, TBN>(is_bf16, p);
 }
 
 hipError_t h16_fast_launch(bool is_bf16, const Problem &p)

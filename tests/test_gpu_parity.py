@@ -603,6 +603,36 @@ def test_forced_config_ragged(dtype, config, aligned):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("config", [GENERAL, GEN128, GEN128x256])
+@pytest.mark.parametrize("a_pad,a_off,b_pad,b_off", [
+    (0, 0, 0, 0),   # both operands' rows 4-byte aligned: both through buffer descriptors
+    (0, 0, 1, 0),   # B's leading dimension odd: A buffer, B global
+    (1, 0, 0, 0),   # A's leading dimension odd: A global, B buffer
+    (0, 1, 0, 0),   # A's base 2-byte aligned, even leading dimension: A global
+    (0, 0, 0, 1),   # B's base 2-byte aligned: B global
+    (1, 1, 1, 1),   # neither
+])
+def test_guarded_operand_alignment(dtype, config, a_pad, a_off, b_pad, b_off):
+    """The guarded large-tile kernels load each operand through a buffer
+    descriptor when its rows start on 4-byte boundaries and through global loads
+    otherwise; every combination against the oracle, with a K tail."""
+    os.environ["LIBGEMM_H16_CONFIG"] = str(config)
+    M, N, K = 300, 520, 202
+    lda, ldb = K + a_pad, N + b_pad
+    say(f"[guarded align] {dtype} config={config} lda={lda}+{a_off} ldb={ldb}+{b_off}")
+    import dense_gemm_13_amd as dg
+    ops = gi.operands(dtype, M, N, K, 54)
+    A = to_device(ops["A"][:M, :K], dtype, lda, a_off)
+    B = to_device(ops["B"][:K, :N], dtype, ldb, b_off)
+    C = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+    getattr(dg, "gemm_" + dtype)(A, B, C)
+    torch.cuda.synchronize()
+    got = C.cpu().view(torch.int16).numpy().view(np.uint16)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "guarded align")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [(256, 256, 128), (512, 768, 384), (1024, 512, 2048),
                                    (768, 256, 1152)])
 def test_fast_path_whole_tiles(dtype, shape):
