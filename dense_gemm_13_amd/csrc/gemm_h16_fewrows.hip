@@ -221,7 +221,27 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] += red[w * 256 + m * FR_COLS + 8 * cc + e];
         uint16_t *rowp = C + (int64_t)m * ldc;
-        if constexpr (EPI) epilogue_row<IS_BF16 ? OUT_BF16 : OUT_F16, 8>(epi, s, rowp, n, 8);
+        constexpr int OUT = IS_BF16 ? OUT_BF16 : OUT_F16;
+        if constexpr (EPI) {
+            if (n >= c0) {
+                epilogue_row<OUT, 8>(epi, s, rowp, n, 8);
+            } else {
+                // The moved window's chunk that starts left of c0: only the
+                // columns this workgroup stores read their bias and prior C
+                // (the others belong to the previous workgroup, which may be
+                // writing them).
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (n + e < c0) continue;
+                    const float bias = epi.bias ? epi.bias[n + e] : 0.f;
+                    float x = epi.beta != 0.f
+                                  ? epilogue_value(epi, s[e], bias, load_out<OUT>(rowp, n + e))
+                                  : epilogue_value(epi, s[e], bias);
+                    if (epi.relu) x = epilogue_relu(x);
+                    s[e] = x;
+                }
+            }
+        }
         uint16_t *dst = rowp + n;
         if (n >= c0 && ((uintptr_t)dst & 15) == 0) {
             *reinterpret_cast<u32x4 *>(dst) = u32x4{pack2<IS_BF16>(s[0], s[1]), pack2<IS_BF16>(s[2], s[3]),
