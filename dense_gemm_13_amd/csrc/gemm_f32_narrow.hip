@@ -133,8 +133,10 @@ f32_narrow_kernel(const float *__restrict__ A, const float *__restrict__ B, floa
     // Each row strip starts its walk over K at a different block (a rotation of
     // the block order, so every block is still summed once): with all strips in
     // step, the loads in flight would sit at one K offset of rows lda apart,
-    // which for power-of-two row strides crowds a few HBM channels.
-    const int krot = kdma > 0 ? (FNW * tm) % kdma : 0;
+    // which for power-of-two row strides crowds a few HBM channels.  Workgroups
+    // go to the XCDs in turn, so with one column of tiles strip tm runs on XCD
+    // tm % 8: the XCDs start 2 FNW blocks apart, the strips of one XCD FNW apart.
+    const int krot = kdma > 0 ? (int)(((int64_t)FNW * (tm / 8 + 2 * (tm % 8))) % kdma) : 0;
     auto issue = [&](float *as, float *bs, int t) {
         int kb = wave + FNW * (t < nsteps ? t : nsteps - 1) + krot;
         if (kb >= kdma) kb -= kdma;

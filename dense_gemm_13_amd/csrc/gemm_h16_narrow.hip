@@ -134,8 +134,13 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
     // the block order, so every block is still summed once): with all strips in
     // step, the loads in flight would sit at one K offset of rows lda apart,
     // which for power-of-two row strides crowds a few HBM channels
-    // (8192 x 64 x 4096: 21.1 us in step, 14.1 us rotated).
-    const int krot = kdma > 0 ? (NNW * tm) % kdma : 0;
+    // (8192 x 64 x 4096: 21.1 us in step, 14.1 us rotated).  Workgroups go to
+    // the XCDs in turn, so with one column of tiles strip tm runs on XCD tm % 8;
+    // the start block mixes both parts of tm: the eight XCDs start 2 NNW blocks
+    // apart and the strips within one XCD NNW apart, which
+    // keeps the XCDs' L2 misses apart too (16384 x 64 x 8192 from cold caches:
+    // 71.5 us with start NNW * tm, 53.7 us with this one).
+    const int krot = kdma > 0 ? (int)(((int64_t)NNW * (tm / 8 + 2 * (tm % 8))) % kdma) : 0;
     auto issue = [&](uint16_t *as, uint16_t *bs, int t) {
         int kb = wave + NNW * (t < nsteps ? t : nsteps - 1) + krot;
         if (kb >= kdma) kb -= kdma;
