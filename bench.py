@@ -653,6 +653,40 @@ def loop_fit(rounds: int = 2, settle: int = 300, launches: int = 200) -> dict:
     return out
 
 
+def vs_hipblaslt(w, rounds: int = 3, settle: int = 300, launches: int = 200) -> dict:
+    """The same product through torch.matmul (hipBLASLt on ROCm; TF32 and
+    reduced-precision reductions off), timed in alternation with the library's
+    call on the workload's own operands: `settle` launches, then the mean of
+    `launches` back-to-back ones, median over `rounds`.  Context only: it does
+    not enter `value`."""
+    import numpy as np
+    import torch
+    torch.backends.cuda.matmul.allow_tf32 = False
+    torch.backends.cuda.matmul.allow_bf16_reduced_precision_reduction = False
+    torch.backends.cuda.matmul.allow_fp16_reduced_precision_reduction = False
+    st = w.stream
+    C2 = torch.empty_like(w.C)
+    calls = {"libgemm": w.call, "hipblaslt": lambda: torch.matmul(w.A, w.B, out=C2)}
+    times = {k: [] for k in calls}
+    for _ in range(rounds):
+        for k, f in calls.items():
+            for _ in range(settle):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(launches):
+                f()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times[k].append(e0.elapsed_time(e1) * 1e3 / launches)
+    out = {k: round(float(np.median(v)), 2) for k, v in times.items()}
+    out["hipblaslt_time_over_libgemm"] = round(out["hipblaslt"] / out["libgemm"], 4)
+    out["method"] = (f"{settle} launches to settle, then the mean of {launches} back to back (us), "
+                     f"alternated, median of {rounds} rounds")
+    del C2
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -726,6 +760,9 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=SETTLE_SECONDS * 1e3,
                     help="back-to-back launches before each workload's warm-up, in ms of "
                          "GPU time (0: none; counter runs use 0)")
+    ap.add_argument("--vs-hipblaslt", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on each plain fp16/bf16/fp32 "
+                         "workload, in alternation with the library (context, not the metric)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy (torch.neg) of this many MiB, "
                          "5 times: the known-size kernel that calibrates HBM byte counters")
@@ -763,6 +800,10 @@ def main():
         steps = args.steps if w is headline else max(10, args.steps // 2)
         r = w.run(steps, args.warmup, args.cold_steps)
         print(f"[bench] {w.name}: {w.summary(r)}", file=sys.stderr, flush=True)
+        if args.vs_hipblaslt and type(w) is Workload and w.dtype != "fp8":
+            r["vs_hipblaslt"] = vs_hipblaslt(w)
+            print(f"[bench] {w.name}: libgemm {r['vs_hipblaslt']['libgemm']} us, hipBLASLt "
+                  f"{r['vs_hipblaslt']['hipblaslt']} us", file=sys.stderr, flush=True)
         results.append(r)
         if w is not headline:
             del w.A, w.B, w.C
