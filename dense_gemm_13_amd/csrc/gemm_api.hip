@@ -208,8 +208,9 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
             bottom.M = tail;
             bottom.A = static_cast<const uint16_t *>(p.A) + (int64_t)top.M * p.lda;
             bottom.C = static_cast<uint16_t *>(p.C) + (int64_t)top.M * p.ldc;
-            // One row: B streamed by every CU (1 x 4095 x 4100: 13.5 us against
-            // 17.6 on the narrow kernel's 64 workgroups); more: the narrow kernel.
+            // Up to four rows: the few-row kernel where it was measured faster
+            // (1 x 4095 x 4100: 12.0 us against 17.6 on the narrow kernel's 64
+            // workgroups); otherwise the narrow kernel.
             const int tail_cfg = h16_fewrows_preferred(bottom)         ? H16_FEWROWS
                                  : h16_narrow_general_eligible(bottom) ? H16_NARROW_GEN
                                                                        : -1;
@@ -223,7 +224,7 @@ int h16_entry(bool is_bf16, const void *A, const void *B, void *C, int64_t M, in
         return to_status(h16_launch(is_bf16, H16_GEN_256x256, p));
     }
     // At most 32 rows (one row strip of the narrow kernel) with a long K: the
-    // narrow kernel, or for one row the few-row kernel where it is faster; the
+    // narrow kernel, or for up to four rows the few-row kernel where it is faster; the
     // 64 x 64 tiles below would walk all of K in each workgroup
     // (1 x 8192 x 8192: 27.2 us against 80.1; 1 x 16384 x 12288: 79 against 169).
     if (p.M <= 32 && p.K >= 256) {

@@ -3,16 +3,19 @@
 // B rows of any alignment.
 //
 // Such a product streams B once: 1 x 4095 x 4100 reads 33.6 MB of B for 33.6
-// MFLOP, so the bound is memory, and the whole chip has to stream.  Here a
-// workgroup owns 16 columns of C, 32 bytes of every B row, so N = 4095
-// already gives 256 workgroups (one per CU).  Consecutive workgroups of one
-// XCD take consecutive column groups, so the 128-byte lines of B that four
-// groups share are fetched once into that XCD's L2.  The 8 waves of a
-// workgroup take the 32-row blocks of B in turns (wave w: blocks w, w + 16,
-// ...), each through a private ring of 8 one-KiB LDS slots filled by
-// LDS-direct 16-byte loads (lane l: row l/2 of the block, 8 columns at
-// 8*(l%2)), so every lane keeps 8 loads in flight and a CU holds 128 KiB of B
-// in flight.  LDS-direct loads keep their rate at 2-byte-aligned addresses,
+// MFLOP, so the bound is memory.  Here a workgroup owns 32 columns of C, 64
+// bytes of every B row, so N = 4095 gives 128 workgroups.  Consecutive
+// workgroups of one XCD take consecutive column groups, so the 128-byte lines
+// of B that two groups share are fetched once into that XCD's L2.  (16-column
+// groups, twice the workgroups but four of them to a line, were slower: the
+// loads in flight per CU are limited in cache lines, not bytes, and each line
+// then brought 32 useful bytes.  1 x 4095 x 4100: 13.3 against 12.0 us;
+// 1 x 8192 x 4096: 23.1 against 16.0 us.  64-column groups, whole lines but a
+// quarter of the workgroups: 14.7 and 16.2 us.)  The 16 waves of a workgroup
+// take the 16-row blocks of B in turns (wave w: blocks w, w + 16, ...), each
+// through a private ring of 8 one-KiB LDS slots filled by LDS-direct 16-byte
+// loads (lane l: row l/4 of the block, 8 columns at 8*(l%4)), so every lane
+// keeps 8 loads in flight and a CU holds 128 KiB of B in flight.  LDS-direct loads keep their rate at 2-byte-aligned addresses,
 // where 16-byte loads into registers do not (B rows of 4095 elements).  The
 // rows of A are copied into LDS once, zero-padded to whole blocks, so a block
 // needs no load of A.  Each lane reads back exactly the 16 bytes it loaded and
@@ -20,9 +23,9 @@
 // lanes of a wave with shuffles and across the waves through LDS, then the
 // epilogue is applied, the result rounded and stored.
 //
-// Edges: the ring carries whole 32-row blocks only; the K % 32 rows after them
+// Edges: the ring carries whole 16-row blocks only; the K % 16 rows after them
 // come through registers, with zeros past K in both operands.  The last
-// workgroup's 16-column window is moved left to end at N (N >= 16), so no load
+// workgroup's 32-column window is moved left to end at N (N >= 32), so no load
 // leaves B's rows, and it stores only the columns past the previous window.
 //
 // The rows of A are the vectors of a matrix-vector product; the split of the K
@@ -40,10 +43,11 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_f_t;
 
-constexpr int FR_COLS = 16;                              // columns of C per workgroup
+constexpr int FR_COLS = 32;                              // columns of C per workgroup
+constexpr int FR_LPR = FR_COLS / 8;                      // lanes per B row (16 bytes each)
 constexpr int FR_WAVES = 16;                             // waves per workgroup
 constexpr int FR_SLOTS = 8;                              // ring slots per wave
-constexpr int FR_ROWS = 32;                              // B rows per block (one 1 KiB load)
+constexpr int FR_ROWS = 64 / FR_LPR;                     // B rows per block (one 1 KiB load)
 constexpr int FR_A_HALVES = 12288;                       // LDS for the rows of A (24 KiB)
 
 // One LDS array per ring slot (each wave its own KiB in it): distinct objects,
@@ -88,7 +92,7 @@ __device__ __forceinline__ float fr_half(uint16_t bits)
 }
 
 // MR: rows of A and C (1 to 4).  EPI: the fused epilogue on the sums before
-// rounding.  Requires N >= 16 and MR * (K rounded up to 32) <= FR_A_HALVES.
+// rounding.  Requires N >= 32 and MR * (K rounded up to 16) <= FR_A_HALVES.
 template <bool IS_BF16, int MR, bool EPI>
 __global__ void __launch_bounds__(FR_WAVES * 64)
 h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -108,7 +112,7 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
     const int nbw = wave < nb ? (nb - wave + FR_WAVES - 1) / FR_WAVES : 0;   // this wave's
 
     // Lane -> row r of each block, 8 columns from wstart + 8c.
-    const int r = lane >> 1, c = lane & 1;
+    const int r = lane / FR_LPR, c = lane % FR_LPR;
     const uint16_t *bsrc = B + wstart + 8 * c;
     // First K row of this wave's t-th block.
     auto blk_k = [&](int t) { return (wave + FR_WAVES * t) * FR_ROWS; };
@@ -121,10 +125,10 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
     };
 
     // Loads: this wave's first ring slots, then the rows of the partial last
-    // block of B (K % 32 rows, through registers; used by the wave whose turn
+    // block of B (K % 16 rows, through registers; used by the wave whose turn
     // that block is), then the rows of A (zero past K; up to FR_A_HALVES / 1024
     // per thread).  Loads complete in issue order, so waiting for A waits for
-    // the first slots too; with K up to 32 * FR_WAVES * FR_SLOTS (4096) those
+    // the first slots too; with K up to 16 * FR_WAVES * FR_SLOTS (2048) those
     // are all of the blocks.
     fr_unroll<FR_SLOTS>([&](auto S) { issue(fr_slot<S>, S); });
     const bool tail_wave = wave == nb % FR_WAVES && nb * FR_ROWS < K;
@@ -190,9 +194,9 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
     }
     fr_wait<0>();
 
-    // Lanes with the same c hold the same columns: add across the 32 rows.
+    // Lanes with the same c hold the same columns: add across the 16 rows.
 #pragma unroll
-    for (int off = 2; off < 64; off *= 2)
+    for (int off = FR_LPR; off < 64; off *= 2)
 #pragma unroll
         for (int m = 0; m < MR; ++m)
 #pragma unroll
@@ -209,8 +213,8 @@ h16_fewrows_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ 
             for (int e = 0; e < 8; ++e) red[wave * 256 + m * FR_COLS + 8 * c + e] = acc[m][e];
     }
     __syncthreads();
-    if (tid < 2 * MR) {
-        const int m = tid >> 1, cc = tid & 1;
+    if (tid < FR_LPR * MR) {
+        const int m = tid / FR_LPR, cc = tid % FR_LPR;
         const int n = wstart + 8 * cc;                   // first of 8 columns, all < N
         float s[8];
 #pragma unroll
@@ -294,14 +298,32 @@ bool h16_fewrows_eligible(const Problem &p)
     return p.M * kp <= FR_A_HALVES;
 }
 
-// Where it was measured ahead of the narrow K-split kernel: one row, at least
-// 128 workgroups, K within one turn of the rings (1 x 4095 x 4100 with B rows
-// 2-byte aligned: 13.5 against 17.6 us; 1 x 4096^2: 11.6 against 12.7 us; with
-// 2 or 4 rows, or K past one turn, the narrow kernel is faster).
+// Where it was measured ahead of the narrow K-split kernel (guarded form), over
+// M = 1..4, N = 256..16384, K = 256..12288, B rows 16-byte aligned or not:
+//  * one row with K >= 2048, when B's rows are not 16-byte aligned (the narrow
+//    kernel's loads slow down there: 1 x 4096 x 4100 with ldb = 4097 12.0
+//    against 17.4 us), when N <= 2048 (64 or fewer workgroups either way:
+//    1 x 1024 x 12288 13.3 against 21.4 us) or while N * K <= 17 M
+//    (1 x 4096 x 4100 11.2 against 12.9 us; 1 x 8192 x 4100 16.9 against 15.6);
+//  * two rows with K >= 2048 and unaligned B rows up to N = 8192, or K >= 4096
+//    with unaligned rows or N <= 2048;
+//  * N not a multiple of 64, up to N = 8192: from K = 512 for one or two rows
+//    and from K = 2048 for up to four (1 x 4095 x 512 8.1 against 11.4 us,
+//    4 x 4095 x 2048 13.5 against 18.0).
+// Elsewhere, and always from N = 16384 with short K, the narrow kernel wins
+// (4 x 16384 x 512: 5.5 against 20.0 us).
 bool h16_fewrows_preferred(const Problem &p)
 {
-    return h16_fewrows_eligible(p) && p.M == 1 && p.N >= 128 * FR_COLS &&
-           p.K / FR_ROWS <= FR_WAVES * FR_SLOTS;
+    if (!h16_fewrows_eligible(p)) return false;
+    const bool unaligned = p.ldb % 8 != 0 || (reinterpret_cast<uintptr_t>(p.B) & 15) != 0;
+    const int64_t nk = (int64_t)p.N * p.K;
+    if (p.M == 1 && p.K >= 2048 && (unaligned || p.N <= 2048 || nk <= 17000000)) return true;
+    if (p.M <= 2 && p.K >= 2048 && unaligned && p.N <= 8192) return true;
+    if (p.M <= 2 && p.K >= 4096 && (unaligned || p.N <= 2048)) return true;
+    if (p.N % 64 != 0 && p.N <= 8192 &&
+        ((p.M <= 2 && p.K >= 512) || p.K >= 2048))
+        return true;
+    return false;
 }
 
 hipError_t h16_fewrows_launch(bool is_bf16, const Problem &p)

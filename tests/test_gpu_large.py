@@ -158,11 +158,14 @@ def test_rows_operand_B_past_2_31_entries_exact(dtype):
     del A, B, C
 
 
-def test_fewrows_operand_B_past_2_31_entries_exact():
-    """The few-row kernel with a B of more than 2^31 entries (K = 4096 rows of
-    540000 columns, one row of A, chosen by the automatic dispatch): its 64-bit
-    row offsets, 33750 workgroups and the window of the last one."""
-    M, K, N = 1, 4096, 540000
+@pytest.mark.parametrize("N", [540000, 540001])
+def test_one_row_operand_B_past_2_31_entries_exact(N):
+    """One row of A times a B of more than 2^31 entries (K = 4096 rows), through
+    the automatic dispatch: with N = 540000 (16-byte-aligned rows) the narrow
+    K-split kernel, its 64-bit block offsets and 8438 column tiles; with
+    N = 540001 (rows 2-byte aligned) the few-row kernel, its 64-bit row offsets,
+    16876 workgroups and the window of the last one moved left."""
+    M, K = 1, 4096
     say(f"[large-B fewrows] bf16 M={M} N={N} K={K}: generating")
     A = _device(gi.operands("bf16", M, 8, K, 506)["A"], "bf16")
     sel = torch.from_numpy(np.random.default_rng(507).integers(0, K, N)).cuda()

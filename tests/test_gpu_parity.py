@@ -34,7 +34,7 @@ FAST128 = 11      # whole 128x128 tiles of the large-tile kernel, two workgroups
 GEN128 = 12       # the same kernel, guarded
 FAST128x256 = 13  # whole 128x256 tiles of the large-tile kernel, one workgroup per CU
 GEN128x256 = 14   # the same kernel, guarded
-FEWROWS = 15      # at most 4 rows: B streamed through per-wave LDS rings, 16 columns per workgroup
+FEWROWS = 15      # at most 4 rows: B streamed through per-wave LDS rings, 32 columns per workgroup
 
 
 @pytest.fixture(autouse=True)
@@ -511,16 +511,16 @@ def test_rows_permutation_exact(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape,lds", [
-    ((1, 16, 1), None),                      # one workgroup, K below one block: registers only
+    ((1, 32, 1), None),                      # one workgroup, K below one block: registers only
     ((1, 4095, 4100), (4100, 4095, 4095)),   # the tail row of 4097 x 4095 x 4100
-    ((1, 4096, 4096), None),                 # whole blocks only, every wave 8 blocks
+    ((1, 4096, 4096), None),                 # whole blocks only, every wave 16 blocks (two turns)
     ((2, 100, 333), (337, 101, 103)),        # window of the last workgroup moved left, offsets
-    ((3, 4095, 517), None),                  # waves with no block, partial block
+    ((3, 4095, 200), None),                  # waves with no block; the partial block to one of them
     ((4, 130, 2048), (2051, 131, 133)),      # four rows, unaligned leading dimensions
-    ((1, 16500, 300), (301, 16501, 16503)),  # 1032 workgroups, several rounds
-    ((4, 17, 3072), (3075, 19, 21)),         # the largest K four rows fit, window straddling
-    ((1, 40, 12288), None),                  # the largest K one row fits: three turns of the ring
-    ((2, 64, 4640), (4643, 67, 69)),         # two turns, partial block
+    ((1, 16500, 300), (301, 16501, 16503)),  # 516 workgroups, several rounds
+    ((4, 33, 3072), (3075, 35, 37)),         # the largest K four rows fit, window straddling
+    ((1, 40, 12288), None),                  # the largest K one row fits: six turns of the ring
+    ((2, 64, 4650), (4653, 67, 69)),         # two turns and more, partial block
 ])
 def test_fewrows_path(dtype, shape, lds):
     """The few-row kernel (half-precision config 15): B streamed through per-wave
@@ -543,10 +543,13 @@ def test_fewrows_path(dtype, shape, lds):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape,lds", [
-    ((1, 8192, 8192), None),                 # one row, long K: the narrow kernel
-    ((1, 4096, 4096), None),                 # one row within one turn: the few-row kernel
+    ((1, 8192, 8192), None),                 # one row, long K and wide: the narrow kernel
+    ((1, 4096, 4096), None),                 # one row, N * K <= 17 M: the few-row kernel
     ((1, 4095, 4100), (4100, 4095, 4095)),   # the same with 2-byte-aligned rows
-    ((3, 5000, 2000), (2003, 5001, 5003)),   # three rows: the narrow kernel, guarded
+    ((3, 5000, 2000), (2003, 5001, 5003)),   # three rows, K < 2048: the narrow kernel, guarded
+    ((4, 4095, 2048), (2048, 4095, 4095)),   # four rows, N not a multiple of 64: few-row
+    ((2, 1000, 600), None),                  # two rows, N not a multiple of 64: few-row
+    ((2, 16384, 1024), None),                # two rows, wide, short K: the narrow kernel
     ((32, 4100, 1000), None),                # one full row strip of the narrow kernel
 ])
 def test_few_rows_dispatch(dtype, shape, lds):
