@@ -47,7 +47,7 @@ enum H16Config {
     H16_GEN_128 = 12,     // same kernel, guarded
     H16_FAST_128x256 = 13, // whole 128x256 tiles of the large-tile kernel, one workgroup per CU
     H16_GEN_128x256 = 14, // same kernel, guarded
-    H16_FEWROWS = 15,     // at most 4 rows: B streamed through per-wave LDS rings, 16 columns per workgroup
+    H16_FEWROWS = 15,     // at most 4 rows: B streamed through per-wave LDS rings, 32 columns per workgroup
     H16_NUM_CONFIGS = 16
 };
 
