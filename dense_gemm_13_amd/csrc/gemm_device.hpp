@@ -272,6 +272,55 @@ __device__ __forceinline__ void epilogue_row(const Epilogue &e, float *v, const 
     epilogue_apply<W>(e, v, b, c, cnt);
 }
 
+// -------------------------------------------------------------- masked loads
+
+// v shifted down by `bytes` (0..16): byte i of the result is byte i + bytes of
+// v, zero past the end.  Selects, no branches: a caller's loads can all be in
+// flight before the first value is used.
+__device__ __forceinline__ u32x4 shift_down_bytes(u32x4 v, int bytes)
+{
+    const uint64_t lo = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+    const uint64_t hi = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
+    const int s = 8 * bytes, a = s & 63;
+    const uint64_t hi_a = hi >> a;
+    const uint64_t lo_small = (lo >> a) | ((hi << 1) << (63 - a));   // s < 64
+    const uint64_t nlo = s >= 128 ? 0 : s >= 64 ? hi_a : lo_small;
+    const uint64_t nhi = s >= 64 ? 0 : hi_a;
+    return u32x4{(uint32_t)nlo, (uint32_t)(nlo >> 32), (uint32_t)nhi, (uint32_t)(nhi >> 32)};
+}
+
+// The 16 bytes of elements [k, k + 16/ESZ) of row `row` of a row-major matrix
+// (leading dimension ld elements, rows x cols valid), with zeros for a row
+// past `rows` and for columns past `cols`, in two halves: masked16_load issues
+// one 16-byte load at an address inside the matrix, masked16_value applies the
+// zeros to what it returned.  A chunk that straddles `cols` is loaded as the
+// row's last 16 bytes and shifted down; a chunk wholly outside reads the
+// matrix's first element and is zeroed.  A caller issues all its loads before
+// taking the first value, so they are in flight together.  Requires
+// cols * ESZ >= 16.  The address may be only ESZ-aligned (the hardware runs in
+// unaligned-access mode).
+struct Masked16 {
+    u32x4 raw;
+    int drop;                                          // bytes to shift out
+};
+template <int ESZ>
+__device__ __forceinline__ Masked16 masked16_load(const void *base, int64_t ld, int row, int rows,
+                                                  int k, int cols)
+{
+    constexpr int EPV = 16 / ESZ;
+    const bool inside = row < rows && k < cols;
+    int kk = k, drop = 0;
+    if (k + EPV > cols) kk = cols - EPV, drop = (k - kk) * ESZ;
+    if (!inside) kk = 0, drop = 16;
+    const char *src = static_cast<const char *>(base) +
+                      ((int64_t)(inside ? row : 0) * ld + kk) * ESZ;
+    return Masked16{*reinterpret_cast<const u32x4 *>(src), drop};
+}
+__device__ __forceinline__ u32x4 masked16_value(const Masked16 &m)
+{
+    return shift_down_bytes(m.raw, m.drop);
+}
+
 // -------------------------------------------------------------- MFMA wrappers
 
 // D(32x32, fp32) += X(32x16) * Y(16x32) with X taken from `x` (row = lane%32,

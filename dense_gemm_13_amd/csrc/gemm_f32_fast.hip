@@ -282,37 +282,65 @@ f32_fast_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         // filled, in the swizzled layout the LDS-direct loads produce.
         const int k0 = SBK * (ktiles - 1);
         float *as = s_stage<0>, *bs = s_stage<SSTAGES>;
-        for (int q = tid; q < SBM * SBK / 4; q += SNW * 64) {
-            const int r = q >> 2, c = q & 3;
-            const int gm = m0 + r, gk = k0 + 4 * c;
-            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (gm < M) {
-                const float *src = A + (int64_t)gm * lda + gk;
-                if (gk + 4 <= K) {
-                    v = *reinterpret_cast<const f32x4 *>(src);
-                } else {
+        constexpr int NT = SNW * 64, NQA = SBM * SBK / 4 / NT, NQB = SBK * SBN / 4 / NT;
+        static_assert(NQA * NT * 4 == SBM * SBK && NQB * NT * 4 == SBK * SBN, "whole chunks");
+        if (K >= 4) {
+            // One 16-byte load inside the matrix per chunk, all in flight before
+            // the first wait; zeros past M, N and K applied in registers.
+            Masked16 va[NQA], vb[NQB];
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = tid + NT * i, r = q >> 2, c = q & 3;
+                va[i] = masked16_load<4>(A, lda, m0 + r, M, k0 + 4 * c, K);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = tid + NT * i, r = q >> 5, c = q & 31;
+                vb[i] = masked16_load<4>(B, ldb, k0 + r, K, n0 + 4 * c, N);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = tid + NT * i, r = q >> 2, c = q & 3;
+                *reinterpret_cast<f32x4 *>(as + lds::f32_a_frag(r, c)) =
+                    __builtin_bit_cast(f32x4, masked16_value(va[i]));
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = tid + NT * i, r = q >> 5, c = q & 31;
+                *reinterpret_cast<f32x4 *>(bs + lds::f32_b_elem(r, 4 * c)) =
+                    __builtin_bit_cast(f32x4, masked16_value(vb[i]));
+            }
+        } else {
+            // K < 4: element by element.
+            for (int q = tid; q < SBM * SBK / 4; q += NT) {
+                const int r = q >> 2, c = q & 3;
+                const int gm = m0 + r, gk = k0 + 4 * c;
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (gm < M) {
+                    const float *src = A + (int64_t)gm * lda + gk;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (gk + e < K) v[e] = src[e];
                 }
+                *reinterpret_cast<f32x4 *>(as + lds::f32_a_frag(r, c)) = v;
             }
-            *reinterpret_cast<f32x4 *>(as + lds::f32_a_frag(r, c)) = v;
-        }
-        for (int q = tid; q < SBK * SBN / 4; q += SNW * 64) {
-            const int r = q >> 5, c = q & 31;
-            const int gk = k0 + r, gn = n0 + 4 * c;
-            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (gk < K) {
-                const float *src = B + (int64_t)gk * ldb + gn;
-                if (gn + 4 <= N) {
-                    v = *reinterpret_cast<const f32x4 *>(src);
-                } else {
+            for (int q = tid; q < SBK * SBN / 4; q += NT) {
+                const int r = q >> 5, c = q & 31;
+                const int gk = k0 + r, gn = n0 + 4 * c;
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (gk < K) {
+                    const float *src = B + (int64_t)gk * ldb + gn;
+                    if (gn + 4 <= N) {
+                        v = *reinterpret_cast<const f32x4 *>(src);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (gn + e < N) v[e] = src[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (gn + e < N) v[e] = src[e];
+                    }
                 }
+                *reinterpret_cast<f32x4 *>(bs + lds::f32_b_elem(r, 4 * c)) = v;
             }
-            *reinterpret_cast<f32x4 *>(bs + lds::f32_b_elem(r, 4 * c)) = v;
         }
     }
     // (GEN: steps past the last one re-load the last full block, K > SBK.)

@@ -219,39 +219,66 @@ f32_narrow_kernel(const float *__restrict__ A, const float *__restrict__ B, floa
         const int k0 = FBK * kdma;
         float *as = fa_stage<STG - 1, TBM>() + wave * FA_WAVE;
         float *bs = fb_stage<STG - 1, STG>() + wave * FB_WAVE;
+        constexpr int NQA = TBM * FBK / 4 / 64, NQB = FBK * FBN / 4 / 64;   // chunks per lane
+        if (K >= 4) {
+            // One 16-byte load inside the matrix per chunk, all in flight before
+            // the first wait; zeros past M, N and K applied in registers.
+            Masked16 va[NQA], vb[NQB];
 #pragma unroll
-        for (int q = lane; q < TBM * FBK / 4; q += 64) {
-            const int r = q >> 3, c = q & 7;
-            const int gm = m0 + r, gk = k0 + 4 * c;
-            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (gm < M) {
-                const float *src = A + (int64_t)gm * lda + gk;
-                if (gk + 4 <= K) {
-                    v = *reinterpret_cast<const f32x4 *>(src);
-                } else {
+            for (int i = 0; i < NQA; ++i) {
+                const int q = lane + 64 * i, r = q >> 3, c = q & 7;
+                va[i] = masked16_load<4>(A, lda, m0 + r, M, k0 + 4 * c, K);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = lane + 64 * i, r = q >> 4, c = q & 15;
+                vb[i] = masked16_load<4>(B, ldb, k0 + r, K, n0 + 4 * c, N);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = lane + 64 * i, r = q >> 3, c = q & 7;
+                *reinterpret_cast<f32x4 *>(as + r * FBK + ((c ^ swz8(r)) << 2)) =
+                    __builtin_bit_cast(f32x4, masked16_value(va[i]));
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = lane + 64 * i, r = q >> 4, c = q & 15;
+                *reinterpret_cast<f32x4 *>(bs + r * FBN + ((c ^ swz_fb(r)) << 2)) =
+                    __builtin_bit_cast(f32x4, masked16_value(vb[i]));
+            }
+        } else {
+            // K < 4: element by element.
+#pragma unroll
+            for (int q = lane; q < TBM * FBK / 4; q += 64) {
+                const int r = q >> 3, c = q & 7;
+                const int gm = m0 + r, gk = k0 + 4 * c;
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (gm < M) {
+                    const float *src = A + (int64_t)gm * lda + gk;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (gk + e < K) v[e] = src[e];
                 }
+                *reinterpret_cast<f32x4 *>(as + r * FBK + ((c ^ swz8(r)) << 2)) = v;
             }
-            *reinterpret_cast<f32x4 *>(as + r * FBK + ((c ^ swz8(r)) << 2)) = v;
-        }
 #pragma unroll
-        for (int q = lane; q < FBK * FBN / 4; q += 64) {
-            const int r = q >> 4, c = q & 15;
-            const int gk = k0 + r, gn = n0 + 4 * c;
-            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (gk < K) {
-                const float *src = B + (int64_t)gk * ldb + gn;
-                if (gn + 4 <= N) {
-                    v = *reinterpret_cast<const f32x4 *>(src);
-                } else {
+            for (int q = lane; q < FBK * FBN / 4; q += 64) {
+                const int r = q >> 4, c = q & 15;
+                const int gk = k0 + r, gn = n0 + 4 * c;
+                f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (gk < K) {
+                    const float *src = B + (int64_t)gk * ldb + gn;
+                    if (gn + 4 <= N) {
+                        v = *reinterpret_cast<const f32x4 *>(src);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (gn + e < N) v[e] = src[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (gn + e < N) v[e] = src[e];
+                    }
                 }
+                *reinterpret_cast<f32x4 *>(bs + r * FBN + ((c ^ swz_fb(r)) << 2)) = v;
             }
-            *reinterpret_cast<f32x4 *>(bs + r * FBN + ((c ^ swz_fb(r)) << 2)) = v;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): the LDS writes landed
         compute(fa_stage<STG - 1, TBM>(), fb_stage<STG - 1, STG>());

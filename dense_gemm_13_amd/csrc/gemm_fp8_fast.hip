@@ -400,39 +400,64 @@ fp8_fast_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
     if constexpr (GEN) {
         const int k0 = QBK * (ktiles - 1);
         uint8_t *as = q_stage<QSTAGES, QSTAGE>, *bs = q_stage<0, QSTAGE>;
-        for (int q = tid; q < QBM * QBK / 16; q += QNW * 64) {
-            const int r = q >> 2, c = q & 3;
-            const int gm = m0 + r, gk = k0 + 16 * c;
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (gm < M) {
-                const uint8_t *src = A + (int64_t)gm * lda + gk;
-                if (gk + 16 <= K) {
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                } else {
-                    uint32_t w[4] = {0, 0, 0, 0};
+        constexpr int NT = QNW * 64, NQA = QBM * QBK / 16 / NT, NQB = QBK * QBN / 16 / NT;
+        static_assert(NQA * NT * 16 == QBM * QBK && NQB * NT * 16 == QBK * QBN, "whole chunks");
+        if (K >= 16) {
+            // One 16-byte load inside the matrix per chunk, all in flight before
+            // the first wait; zeros past M, N and K applied in registers.
+            Masked16 va[NQA], vb[NQB];
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = tid + NT * i, r = q >> 2, c = q & 3;
+                va[i] = masked16_load<1>(A, lda, m0 + r, M, k0 + 16 * c, K);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = tid + NT * i, r = q / Sh::BCPR, c = q % Sh::BCPR;
+                vb[i] = masked16_load<1>(B, ldb, k0 + r, K, n0 + 16 * c, N);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = tid + NT * i, r = q >> 2, c = q & 3;
+                *reinterpret_cast<u32x4 *>(as + lds::fp8_a_frag(r, c)) = masked16_value(va[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = tid + NT * i, r = q / Sh::BCPR, c = q % Sh::BCPR;
+                *reinterpret_cast<u32x4 *>(bs + r * QBN + lds::fp8_b_col<QBN>(r, 16 * c)) =
+                    masked16_value(vb[i]);
+            }
+        } else {
+            // K < 16: element by element.
+            for (int q = tid; q < QBM * QBK / 16; q += NT) {
+                const int r = q >> 2, c = q & 3;
+                const int gm = m0 + r, gk = k0 + 16 * c;
+                uint32_t w[4] = {0, 0, 0, 0};
+                if (gm < M) {
+                    const uint8_t *src = A + (int64_t)gm * lda + gk;
                     for (int e = 0; e < 16; ++e)
                         if (gk + e < K) w[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
-                    v = u32x4{w[0], w[1], w[2], w[3]};
                 }
+                *reinterpret_cast<u32x4 *>(as + lds::fp8_a_frag(r, c)) = u32x4{w[0], w[1], w[2], w[3]};
             }
-            *reinterpret_cast<u32x4 *>(as + lds::fp8_a_frag(r, c)) = v;
-        }
-        for (int q = tid; q < QBK * QBN / 16; q += QNW * 64) {
-            const int r = q / Sh::BCPR, c = q % Sh::BCPR;
-            const int gk = k0 + r, gn = n0 + 16 * c;
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (gk < K) {
-                const uint8_t *src = B + (int64_t)gk * ldb + gn;
-                if (gn + 16 <= N) {
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                } else {
-                    uint32_t w[4] = {0, 0, 0, 0};
-                    for (int e = 0; e < 16; ++e)
-                        if (gn + e < N) w[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
-                    v = u32x4{w[0], w[1], w[2], w[3]};
+            for (int q = tid; q < QBK * QBN / 16; q += NT) {
+                const int r = q / Sh::BCPR, c = q % Sh::BCPR;
+                const int gk = k0 + r, gn = n0 + 16 * c;
+                u32x4 v = u32x4{0, 0, 0, 0};
+                if (gk < K) {
+                    const uint8_t *src = B + (int64_t)gk * ldb + gn;
+                    if (gn + 16 <= N) {
+                        v = *reinterpret_cast<const u32x4 *>(src);
+                    } else {
+                        uint32_t w[4] = {0, 0, 0, 0};
+                        for (int e = 0; e < 16; ++e)
+                            if (gn + e < N) w[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+                        v = u32x4{w[0], w[1], w[2], w[3]};
+                    }
                 }
+                *reinterpret_cast<u32x4 *>(bs + r * QBN + lds::fp8_b_col<QBN>(r, 16 * c)) = v;
             }
-            *reinterpret_cast<u32x4 *>(bs + r * QBN + lds::fp8_b_col<QBN>(r, 16 * c)) = v;
         }
         q_scale<0>[64 * wave + lane] = sc_src[(int64_t)(ktiles - 1) * sc_step];
         q_unroll<QSTAGES - 1>([&](auto S) {

@@ -249,39 +249,64 @@ fp8_narrow_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B,
         const int k0 = GBK * kdma;
         uint8_t *as = ga_stage<GSTG - 1, TBM>() + wave * GA_WAVE;
         uint8_t *bs = gb_stage<GSTG - 1>() + wave * GB_WAVE;
+        constexpr int NQA = TBM * 4 / 64, NQB = GBK * 4 / 64;     // chunks per lane
+        if (K >= 16) {
+            // One 16-byte load inside the matrix per chunk, all in flight before
+            // the first wait; zeros past M, N and K applied in registers.
+            Masked16 va[NQA], vb[NQB];
 #pragma unroll
-        for (int q = lane; q < TBM * 4; q += 64) {
-            const int r = q >> 2, c = q & 3;
-            const int gm = m0 + r, gk = k0 + 16 * c;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (gm < M) {
-                const uint8_t *src = A + (int64_t)gm * lda + gk;
-                if (gk + 16 <= K) {
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                } else {
+            for (int i = 0; i < NQA; ++i) {
+                const int q = lane + 64 * i, r = q >> 2, c = q & 3;
+                va[i] = masked16_load<1>(A, lda, m0 + r, M, k0 + 16 * c, K);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = lane + 64 * i, r = q >> 2, c = q & 3;
+                vb[i] = masked16_load<1>(B, ldb, k0 + r, K, n0 + 16 * c, N);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = lane + 64 * i, r = q >> 2, c = q & 3;
+                *reinterpret_cast<u32x4 *>(as + r * GBK + ((c ^ gswz_a(r)) << 4)) = masked16_value(va[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = lane + 64 * i, r = q >> 2, c = q & 3;
+                *reinterpret_cast<u32x4 *>(bs + r * GBN + ((c ^ gswz_b(r)) << 4)) = masked16_value(vb[i]);
+            }
+        } else {
+            // K < 16: element by element.
+#pragma unroll
+            for (int q = lane; q < TBM * 4; q += 64) {
+                const int r = q >> 2, c = q & 3;
+                const int gm = m0 + r, gk = k0 + 16 * c;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (gm < M) {
+                    const uint8_t *src = A + (int64_t)gm * lda + gk;
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
                         if (gk + e < K) v[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
                 }
+                *reinterpret_cast<u32x4 *>(as + r * GBK + ((c ^ gswz_a(r)) << 4)) = v;
             }
-            *reinterpret_cast<u32x4 *>(as + r * GBK + ((c ^ gswz_a(r)) << 4)) = v;
-        }
 #pragma unroll
-        for (int q = lane; q < GBK * 4; q += 64) {
-            const int r = q >> 2, c = q & 3;
-            const int gk = k0 + r, gn = n0 + 16 * c;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (gk < K) {
-                const uint8_t *src = B + (int64_t)gk * ldb + gn;
-                if (gn + 16 <= N) {
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                } else {
+            for (int q = lane; q < GBK * 4; q += 64) {
+                const int r = q >> 2, c = q & 3;
+                const int gk = k0 + r, gn = n0 + 16 * c;
+                u32x4 v = u32x4{0u, 0u, 0u, 0u};
+                if (gk < K) {
+                    const uint8_t *src = B + (int64_t)gk * ldb + gn;
+                    if (gn + 16 <= N) {
+                        v = *reinterpret_cast<const u32x4 *>(src);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (gn + e < N) v[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+                        for (int e = 0; e < 16; ++e)
+                            if (gn + e < N) v[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
+                    }
                 }
+                *reinterpret_cast<u32x4 *>(bs + r * GBN + ((c ^ gswz_b(r)) << 4)) = v;
             }
-            *reinterpret_cast<u32x4 *>(bs + r * GBN + ((c ^ gswz_b(r)) << 4)) = v;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): the LDS writes landed
         compute(ga_stage<GSTG - 1, TBM>(), gb_stage<GSTG - 1>(), kdma);

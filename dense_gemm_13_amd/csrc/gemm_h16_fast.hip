@@ -397,42 +397,68 @@ h16_fast_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int k0 = BK * (ktiles - 1);
         uint16_t *as = lds_stage<0, A_STAGE>, *bs = lds_stage<STAGES, B_STAGE>;
         constexpr int NT = FNW * 64;
+        constexpr int NQA = A_STAGE / 8 / NT, NQB = B_STAGE / 8 / NT;   // chunks per thread
+        static_assert(NQA * NT * 8 == A_STAGE && NQB * NT * 8 == B_STAGE, "whole chunks");
+        if (K >= 8) {
+            // Every chunk one 16-byte load inside the matrix, all issued before
+            // the first wait; the zeros past M, N and K applied in registers.
+            Masked16 va[NQA], vb[NQB];
 #pragma unroll
-        for (int q = tid; q < A_STAGE / 8; q += NT) {
-            const int r = q / CPR, c = q % CPR;
-            const int gm = m0 + r, gk = k0 + 8 * c;
-            uint32_t w[4] = {0, 0, 0, 0};
-            if (gm < M) {
-                const uint16_t *src = A + (int64_t)gm * lda + gk;
-                if (gk + 8 <= K) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
-                    w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
-                } else {
+            for (int i = 0; i < NQA; ++i) {
+                const int q = tid + NT * i, r = q / CPR, c = q % CPR;
+                va[i] = masked16_load<2>(A, lda, m0 + r, M, k0 + 8 * c, K);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = tid + NT * i, r = q / (FBN / 8), c = q % (FBN / 8);
+                vb[i] = masked16_load<2>(B, ldb, k0 + r, K, n0 + 8 * c, N);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = tid + NT * i, r = q / CPR, c = q % CPR;
+                *reinterpret_cast<u32x4 *>(as + lds::h16_a_frag<BK>(r, c)) = masked16_value(va[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = tid + NT * i, r = q / (FBN / 8), c = q % (FBN / 8);
+                *reinterpret_cast<u32x4 *>(bs + r * FBN + lds::h16_b_col(r, 8 * c)) =
+                    masked16_value(vb[i]);
+            }
+        } else {
+            // K < 8: element by element.
+#pragma unroll
+            for (int q = tid; q < A_STAGE / 8; q += NT) {
+                const int r = q / CPR, c = q % CPR;
+                const int gm = m0 + r, gk = k0 + 8 * c;
+                uint32_t w[4] = {0, 0, 0, 0};
+                if (gm < M) {
+                    const uint16_t *src = A + (int64_t)gm * lda + gk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         if (gk + e < K) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
                 }
+                *reinterpret_cast<u32x4 *>(as + lds::h16_a_frag<BK>(r, c)) = u32x4{w[0], w[1], w[2], w[3]};
             }
-            *reinterpret_cast<u32x4 *>(as + lds::h16_a_frag<BK>(r, c)) = u32x4{w[0], w[1], w[2], w[3]};
-        }
 #pragma unroll
-        for (int q = tid; q < B_STAGE / 8; q += NT) {
-            const int r = q / (FBN / 8), c = q % (FBN / 8);
-            const int gk = k0 + r, gn = n0 + 8 * c;
-            uint32_t w[4] = {0, 0, 0, 0};
-            if (gk < K) {
-                const uint16_t *src = B + (int64_t)gk * ldb + gn;
-                if (gn + 8 <= N) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
-                    w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
-                } else {
+            for (int q = tid; q < B_STAGE / 8; q += NT) {
+                const int r = q / (FBN / 8), c = q % (FBN / 8);
+                const int gk = k0 + r, gn = n0 + 8 * c;
+                uint32_t w[4] = {0, 0, 0, 0};
+                if (gk < K) {
+                    const uint16_t *src = B + (int64_t)gk * ldb + gn;
+                    if (gn + 8 <= N) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                        w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                        for (int e = 0; e < 8; ++e)
+                            if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                    }
                 }
+                *reinterpret_cast<u32x4 *>(bs + r * FBN + lds::h16_b_col(r, 8 * c)) =
+                    u32x4{w[0], w[1], w[2], w[3]};
             }
-            *reinterpret_cast<u32x4 *>(bs + r * FBN + lds::h16_b_col(r, 8 * c)) =
-                u32x4{w[0], w[1], w[2], w[3]};
         }
     }
     // (GEN: steps past the last one re-load the last full block, K > BK.)

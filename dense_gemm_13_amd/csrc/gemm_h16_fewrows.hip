@@ -301,17 +301,15 @@ bool h16_fewrows_eligible(const Problem &p)
 // Where it was measured ahead of the narrow K-split kernel (guarded form), over
 // M = 1..4, N = 256..16384, K = 256..12288, B rows 16-byte aligned or not:
 //  * one row with K >= 2048, when B's rows are not 16-byte aligned (the narrow
-//    kernel's loads slow down there: 1 x 4096 x 4100 with ldb = 4097 12.0
-//    against 17.4 us), when N <= 2048 (64 or fewer workgroups either way:
-//    1 x 1024 x 12288 13.3 against 21.4 us) or while N * K <= 17 M
-//    (1 x 4096 x 4100 11.2 against 12.9 us; 1 x 8192 x 4100 16.9 against 15.6);
+//    kernel's LDS-direct loads slow down there: 1 x 4096 x 4100 with ldb =
+//    4097 12.1 against 17.2 us), when N <= 2048 (64 or fewer workgroups either
+//    way: 1 x 1024 x 12288 13.4 against 21.3 us) or while N * K <= 17 M
+//    (1 x 4096 x 4100 10.9 against 12.1 us; 1 x 8192 x 4100 16.8 against 15.3);
 //  * two rows with K >= 2048 and unaligned B rows up to N = 8192, or K >= 4096
-//    with unaligned rows or N <= 2048;
-//  * N not a multiple of 64, up to N = 8192: from K = 512 for one or two rows
-//    and from K = 2048 for up to four (1 x 4095 x 512 8.1 against 11.4 us,
-//    4 x 4095 x 2048 13.5 against 18.0).
-// Elsewhere, and always from N = 16384 with short K, the narrow kernel wins
-// (4 x 16384 x 512: 5.5 against 20.0 us).
+//    with unaligned rows or N <= 2048.
+// Elsewhere, and always with short K or from N = 16384 with aligned rows, the
+// narrow kernel wins (4 x 16384 x 512: 5.6 against 20.0 us; 1 x 4095 x 1024:
+// 7.2 against 8.3).
 bool h16_fewrows_preferred(const Problem &p)
 {
     if (!h16_fewrows_eligible(p)) return false;
@@ -320,9 +318,6 @@ bool h16_fewrows_preferred(const Problem &p)
     if (p.M == 1 && p.K >= 2048 && (unaligned || p.N <= 2048 || nk <= 17000000)) return true;
     if (p.M <= 2 && p.K >= 2048 && unaligned && p.N <= 8192) return true;
     if (p.M <= 2 && p.K >= 4096 && (unaligned || p.N <= 2048)) return true;
-    if (p.N % 64 != 0 && p.N <= 8192 &&
-        ((p.M <= 2 && p.K >= 512) || p.K >= 2048))
-        return true;
     return false;
 }
 

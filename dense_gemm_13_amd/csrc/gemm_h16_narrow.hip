@@ -219,41 +219,65 @@ h16_narrow_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
         const int k0 = NBK * kdma;
         uint16_t *as = a_stage<STG - 1, TBM>() + wave * NA_WAVE;
         uint16_t *bs = b_stage<STG - 1, STG>() + wave * NB_WAVE;
+        constexpr int NQA = NBM * NBK / 8 / 64, NQB = NBK * NBN / 8 / 64;   // chunks per lane
+        if (K >= 8) {
+            // One 16-byte load inside the matrix per chunk, all in flight before
+            // the first wait; zeros past M, N and K applied in registers.
+            Masked16 va[NQA], vb[NQB];
 #pragma unroll
-        for (int q = lane; q < NBM * NBK / 8; q += 64) {
-            const int r = q >> 3, c = q & 7;
-            const int gm = m0 + r, gk = k0 + 8 * c;
-            uint32_t w[4] = {0, 0, 0, 0};
-            if (gm < M) {
-                const uint16_t *src = A + (int64_t)gm * lda + gk;
-                if (gk + 8 <= K) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
-                    w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
-                } else {
+            for (int i = 0; i < NQA; ++i) {
+                const int q = lane + 64 * i, r = q >> 3, c = q & 7;
+                va[i] = masked16_load<2>(A, lda, m0 + r, M, k0 + 8 * c, K);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = lane + 64 * i, r = q >> 3, c = q & 7;
+                vb[i] = masked16_load<2>(B, ldb, k0 + r, K, n0 + 8 * c, N);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NQA; ++i) {
+                const int q = lane + 64 * i, r = q >> 3, c = q & 7;
+                *reinterpret_cast<u32x4 *>(as + r * NBK + ((c ^ swz8(r)) << 3)) = masked16_value(va[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < NQB; ++i) {
+                const int q = lane + 64 * i, r = q >> 3, c = q & 7;
+                *reinterpret_cast<u32x4 *>(bs + r * NBN + ((c ^ swz_nb(r)) << 3)) = masked16_value(vb[i]);
+            }
+        } else {
+            // K < 8: element by element.
+#pragma unroll
+            for (int q = lane; q < NBM * NBK / 8; q += 64) {
+                const int r = q >> 3, c = q & 7;
+                const int gm = m0 + r, gk = k0 + 8 * c;
+                uint32_t w[4] = {0, 0, 0, 0};
+                if (gm < M) {
+                    const uint16_t *src = A + (int64_t)gm * lda + gk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         if (gk + e < K) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
                 }
+                *reinterpret_cast<u32x4 *>(as + r * NBK + ((c ^ swz8(r)) << 3)) = u32x4{w[0], w[1], w[2], w[3]};
             }
-            *reinterpret_cast<u32x4 *>(as + r * NBK + ((c ^ swz8(r)) << 3)) = u32x4{w[0], w[1], w[2], w[3]};
-        }
 #pragma unroll
-        for (int q = lane; q < NBK * NBN / 8; q += 64) {
-            const int r = q >> 3, c = q & 7;
-            const int gk = k0 + r, gn = n0 + 8 * c;
-            uint32_t w[4] = {0, 0, 0, 0};
-            if (gk < K) {
-                const uint16_t *src = B + (int64_t)gk * ldb + gn;
-                if (gn + 8 <= N) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
-                    w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
-                } else {
+            for (int q = lane; q < NBK * NBN / 8; q += 64) {
+                const int r = q >> 3, c = q & 7;
+                const int gk = k0 + r, gn = n0 + 8 * c;
+                uint32_t w[4] = {0, 0, 0, 0};
+                if (gk < K) {
+                    const uint16_t *src = B + (int64_t)gk * ldb + gn;
+                    if (gn + 8 <= N) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                        w[0] = v[0], w[1] = v[1], w[2] = v[2], w[3] = v[3];
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                        for (int e = 0; e < 8; ++e)
+                            if (gn + e < N) w[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                    }
                 }
+                *reinterpret_cast<u32x4 *>(bs + r * NBN + ((c ^ swz_nb(r)) << 3)) = u32x4{w[0], w[1], w[2], w[3]};
             }
-            *reinterpret_cast<u32x4 *>(bs + r * NBN + ((c ^ swz_nb(r)) << 3)) = u32x4{w[0], w[1], w[2], w[3]};
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): the LDS writes landed
         compute(a_stage<STG - 1, TBM>(), b_stage<STG - 1, STG>());

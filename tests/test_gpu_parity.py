@@ -547,8 +547,8 @@ def test_fewrows_path(dtype, shape, lds):
     ((1, 4096, 4096), None),                 # one row, N * K <= 17 M: the few-row kernel
     ((1, 4095, 4100), (4100, 4095, 4095)),   # the same with 2-byte-aligned rows
     ((3, 5000, 2000), (2003, 5001, 5003)),   # three rows, K < 2048: the narrow kernel, guarded
-    ((4, 4095, 2048), (2048, 4095, 4095)),   # four rows, N not a multiple of 64: few-row
-    ((2, 1000, 600), None),                  # two rows, N not a multiple of 64: few-row
+    ((4, 4095, 2048), (2048, 4095, 4095)),   # four rows: the narrow kernel, guarded
+    ((2, 1000, 2048), (2048, 1001, 1003)),   # two rows, unaligned B rows, K >= 2048: few-row
     ((2, 16384, 1024), None),                # two rows, wide, short K: the narrow kernel
     ((32, 4100, 1000), None),                # one full row strip of the narrow kernel
 ])
@@ -632,6 +632,35 @@ def test_guarded_operand_alignment(dtype, config, a_pad, a_off, b_pad, b_off):
     torch.cuda.synchronize()
     got = C.cpu().view(torch.int16).numpy().view(np.uint16)
     ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "guarded align")
+    assert ok, msg
+
+
+@pytest.mark.parametrize("dtype,var,force,K", [
+    ("bf16", "LIBGEMM_H16_CONFIG", "5", 100),    # guarded 256 x 256 tiles
+    ("f16", "LIBGEMM_H16_CONFIG", "12", 100),    # guarded 128 x 128 tiles
+    ("bf16", "LIBGEMM_H16_CONFIG", "14", 100),   # guarded 128 x 256 tiles
+    ("bf16", "LIBGEMM_H16_CONFIG", "7", 100),    # narrow kernel, guarded
+    ("f16", "LIBGEMM_H16_CONFIG", "9", 100),     # narrow 64-row kernel, guarded
+    ("bf16", "LIBGEMM_H16_CONFIG", "7", 7),      # K below one 16-byte chunk: element loads
+    ("f32", "LIBGEMM_F32_SMALL", "2", 101),      # fp32 guarded large tiles
+    ("f32", "LIBGEMM_F32_SMALL", "5", 101),      # fp32 K-split, guarded
+    ("f32", "LIBGEMM_F32_SMALL", "7", 3),        # fp32 K-split 64-row, K below one chunk
+    ("fp8", "LIBGEMM_FP8_SMALL", "2", 130),      # fp8 guarded large tiles
+    ("fp8", "LIBGEMM_FP8_SMALL", "4", 130),      # fp8 K-split, guarded
+    ("fp8", "LIBGEMM_FP8_SMALL", "6", 9),        # fp8 K-split 64-row, K below one chunk
+])
+def test_guarded_last_block_at_buffer_end(dtype, var, force, K):
+    """The last K block of the guarded kernels goes through registers: one 16-byte
+    load per chunk from inside the matrix, a chunk that straddles K or N taken
+    from the row's last 16 bytes and shifted.  Leading dimensions equal to the
+    row lengths and offset base pointers put those chunks at the very end of A's
+    and B's buffers (A's last row straddles K, B's last row straddles N)."""
+    os.environ[var] = force
+    M, N = 290, 300
+    say(f"[last block] {dtype} {var}={force} {M}x{N}x{K}")
+    ops = gi.operands(dtype, M, N, K, 56)
+    _, got = run_gemm(dtype, ops, M, N, K, lda=K, ldb=N, ldc=N, offset=1)
+    ok, msg, _ = compare(dtype, got, reference(dtype, ops, M, N, K), "last block")
     assert ok, msg
 
 
