@@ -75,16 +75,32 @@ f32_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
         for (int j = 0; j < FN; ++j) total[i][j] = f32x16{};
 
     f32x4 areg[A_ITERS], breg[B_ITERS];
+    // Chunks are 16-byte loads whatever the rows' alignment (the hardware runs in
+    // unaligned-access mode).  !ALIGNED: a chunk at an edge is one 16-byte load
+    // from inside the matrix (masked16_load) whose zeros past M, N and K are
+    // applied when it is stored to LDS, after the step's MFMAs, so load_tile
+    // waits for nothing.  (ALIGNED keeps element loads at the edges, which
+    // measured faster there: fewer registers.)
+    int loaded_k0 = 0;                                   // K step in the registers
+    // Bytes a chunk's masked load shifts out (0 for a chunk wholly inside).
+    const auto drop_of = [](int row, int rows, int k, int cols) {
+        if (ALIGNED || cols < 4) return 0;               // (element loads instead)
+        if (row >= rows || k >= cols) return 16;
+        return k + 4 > cols ? 4 * (k + 4 - cols) : 0;
+    };
 
     auto load_tile = [&](int k0) {
+        loaded_k0 = k0;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             const int q = tid + it * NT;
             const int row = q >> 3, c = q & 7;
             const int gm = m0 + row, gk = k0 + 4 * c;
             const float *src = A + (int64_t)gm * lda + gk;
-            if (ALIGNED && gm < M && gk + 4 <= K)
+            if (gm < M && gk + 4 <= K)
                 areg[it] = *reinterpret_cast<const f32x4 *>(src);
+            else if (!ALIGNED && K >= 4)
+                areg[it] = __builtin_bit_cast(f32x4, masked16_load<4>(A, lda, gm, M, gk, K).raw);
             else
                 areg[it] = load4_guarded(src, gm < M, K - gk);
         }
@@ -94,14 +110,34 @@ f32_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B, float 
             const int row = q / (BN / 4), c = q % (BN / 4);
             const int gk = k0 + row, gn = n0 + 4 * c;
             const float *src = B + (int64_t)gk * ldb + gn;
-            if (ALIGNED && gk < K && gn + 4 <= N)
+            if (gk < K && gn + 4 <= N)
                 breg[it] = *reinterpret_cast<const f32x4 *>(src);
+            else if (!ALIGNED && N >= 4)
+                breg[it] = __builtin_bit_cast(f32x4, masked16_load<4>(B, ldb, gk, K, gn, N).raw);
             else
                 breg[it] = load4_guarded(src, gk < K, N - gn);
         }
     };
 
     auto store_tile = [&](int buf) {
+        const int k0 = loaded_k0;
+        if (!ALIGNED && (m0 + BM > M || n0 + BN > N || k0 + BK > K)) {
+#pragma unroll
+            for (int it = 0; it < A_ITERS; ++it) {
+                const int q = tid + it * NT;
+                areg[it] = __builtin_bit_cast(
+                    f32x4, shift_down_bytes(__builtin_bit_cast(u32x4, areg[it]),
+                                            drop_of(m0 + (q >> 3), M, k0 + 4 * (q & 7), K)));
+            }
+#pragma unroll
+            for (int it = 0; it < B_ITERS; ++it) {
+                const int q = tid + it * NT;
+                const int row = q / (BN / 4), c = q % (BN / 4);
+                breg[it] = __builtin_bit_cast(
+                    f32x4, shift_down_bytes(__builtin_bit_cast(u32x4, breg[it]),
+                                            drop_of(k0 + row, K, n0 + 4 * c, N)));
+            }
+        }
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             const int q = tid + it * NT;

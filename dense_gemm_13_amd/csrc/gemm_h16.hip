@@ -98,19 +98,36 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     u32x4 areg[A_ITERS];
     u32x4 breg[B_ITERS][BR];
+    // Chunks at the edges: one 16-byte load from inside the matrix (masked16_load)
+    // whose zeros past M, N and K are applied when the chunk is stored to LDS,
+    // after the step's MFMAs, so no load is waited for inside load_tile.  The
+    // shift of each chunk is worked out again from its indices then.  (Not in
+    // the 8-wave 256 x 256 tiles, whose registers are full: element loads there.)
+    constexpr bool MASKED = BM * BN <= 128 * 128;
+    int loaded_k0 = 0;                                   // K step in the registers
+    // Bytes a chunk's masked load shifts out (0 for a chunk wholly inside).
+    const auto drop_of = [](int row, int rows, int k, int cols) {
+        if (!MASKED || cols < 8) return 0;               // (element loads instead)
+        if (row >= rows || k >= cols) return 16;
+        return k + 8 > cols ? 2 * (k + 8 - cols) : 0;
+    };
 
     // ---- global -> registers for the K step starting at k0
     auto load_tile = [&](int k0) {
+        loaded_k0 = k0;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             const int q = tid + it * NT;
             const int row = q >> 3, c = q & 7;
             const int gm = m0 + row, gk = k0 + c * 8;
             const uint16_t *src = A + (int64_t)gm * lda + gk;
-            if (gm < M && gk + 8 <= K)
+            if (gm < M && gk + 8 <= K) {
                 areg[it] = *reinterpret_cast<const u32x4 *>(src);
-            else
+            } else if (MASKED && K >= 8) {
+                areg[it] = masked16_load<2>(A, lda, gm, M, gk, K).raw;
+            } else {
                 areg[it] = load8_guarded(src, gm < M, K - gk);
+            }
         }
 #pragma unroll
         for (int it = 0; it < B_ITERS; ++it) {
@@ -121,16 +138,35 @@ h16_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             for (int r = 0; r < BR; ++r) {
                 const int gk = k0 + kb * BR + r;
                 const uint16_t *src = B + (int64_t)gk * ldb + gn;
-                if (gk < K && gn + 8 <= N)
+                if (gk < K && gn + 8 <= N) {
                     breg[it][r] = *reinterpret_cast<const u32x4 *>(src);
-                else
+                } else if (MASKED && N >= 8) {
+                    breg[it][r] = masked16_load<2>(B, ldb, gk, K, gn, N).raw;
+                } else {
                     breg[it][r] = load8_guarded(src, gk < K, N - gn);
+                }
             }
         }
     };
 
     // ---- registers -> LDS stage `buf` (A as is, B transposed)
     auto store_tile = [&](int buf) {
+        const int k0 = loaded_k0;
+        if (MASKED && (m0 + BM > M || n0 + BN > N || k0 + BK > K)) {
+#pragma unroll
+            for (int it = 0; it < A_ITERS; ++it) {
+                const int q = tid + it * NT;
+                areg[it] = shift_down_bytes(areg[it], drop_of(m0 + (q >> 3), M, k0 + (q & 7) * 8, K));
+            }
+#pragma unroll
+            for (int it = 0; it < B_ITERS; ++it) {
+                const int p = tid + it * NT;
+                const int gn = n0 + (p % (BN / 8)) * 8, kb = p / (BN / 8);
+#pragma unroll
+                for (int r = 0; r < BR; ++r)
+                    breg[it][r] = shift_down_bytes(breg[it][r], drop_of(k0 + kb * BR + r, K, gn, N));
+            }
+        }
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             const int q = tid + it * NT;
