@@ -124,3 +124,32 @@ def test_conv_in_graph(noalloc):
         call = lambda: dg.gemm_conv2d_nhwc(X, Wt, padding=1, bias=bias, activation="relu", Y=Y,
                                            workspace=ws)
         _replays_match(call, [Y])
+
+
+def test_calls_on_concurrent_streams():
+    """GEMMs of different kernel families issued on two streams at once (the
+    GEMM kernels keep no state between calls): each output equals the same
+    call run alone, bit for bit."""
+    say("[streams] six products on two streams")
+    shapes = [("bf16", 4097, 4095, 4100), ("f16", 1000, 1000, 1000), ("bf16", 8192, 64, 4096),
+              ("f32", 300, 1500, 4096), ("bf16", 2, 1000, 2048), ("f16", 2048, 2048, 2048)]
+    ops = []
+    for i, (dt, M, N, K) in enumerate(shapes):
+        A, B = _rand((M, K), DT[dt], 20 + i), _rand((K, N), DT[dt], 40 + i)
+        ops.append((getattr(dg, f"gemm_{dt}"), A, B, torch.empty((M, N), dtype=DT[dt], device="cuda")))
+    refs = []
+    for fn, A, B, C in ops:
+        fn(A, B, C)
+        torch.cuda.synchronize()
+        refs.append(C.clone())
+        C.view(torch.uint8).fill_(0xA5)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for i, (fn, A, B, C) in enumerate(ops):
+            fn(A, B, C, stream=streams[i % 2])
+        torch.cuda.synchronize()
+        for i, (_, _, _, C) in enumerate(ops):
+            assert torch.equal(C.view(torch.uint8), refs[i].view(torch.uint8)), f"call {i}, round {rep}"
+            C.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
